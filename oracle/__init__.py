@@ -1,0 +1,306 @@
+"""CPU oracle for the VC-Attention hot path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  It shares no code with the HIP library
+in ``bit_fp8_attention_amd`` and never imports it.
+
+Two parts:
+
+* ``exact``: fp64 attention by its plain definition
+  (VC-Attention paper, §3.1: S = QK^T/sqrt(d), P = softmax(S), O = PV) plus the
+  closed forms of §3.3 and Appendix D used as pins.
+* ``vc_oracle.c`` (wrapped here): a step-by-step emulation of the quantised
+  pipeline -- E4M3 codec, per-block / per-head quantisers, the V-Smooth
+  grouping (k-means, argsort, block means, residual codes) and the ExpCast
+  attention recurrence, one query row at a time.
+
+Tensors cross this wrapper as numpy arrays; bf16 values travel as their
+uint16 bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "vc_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libvc_oracle.so")
+_lib = None
+
+SEQUENTIAL = 1
+EXACT_EXP = 2
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc (IEEE fp32, no contraction)."""
+    if force or not os.path.exists(_LIB_PATH):
+        cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+               "-o", _LIB_PATH + ".tmp", _SRC, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        i32, i64, f32, u64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_uint64
+        L.vco_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.vco_e4m3_decode.restype = ctypes.c_double
+        L.vco_e4m3_encode.argtypes = [f32]
+        L.vco_e4m3_encode.restype = ctypes.c_uint8
+        L.vco_e4m3_encode_array.argtypes = [P, i64, P]
+        L.vco_f32_to_bf16.argtypes = [f32]
+        L.vco_f32_to_bf16.restype = ctypes.c_uint16
+        L.vco_expcast_codes.argtypes = [P, P, P, i64, i32, P]
+        L.vco_expcast_code_u.argtypes = [ctypes.c_double, ctypes.c_double]
+        L.vco_expcast_code_u.restype = ctypes.c_int
+        L.vco_quantize_blocks.argtypes = [P, i64, i32, i32, P, P]
+        L.vco_quantize_v_head.argtypes = [P, i64, i32, i32, P]
+        L.vco_quantize_v_head.restype = f32
+        L.vco_splitmix64_stream.argtypes = [u64, i32, P]
+        L.vco_forgy_indices.argtypes = [u64, i32, i32, i32, i32, i32, P]
+        L.vco_kmeans.argtypes = [P, i64, i32, i32, i32, i32, u64, i32, i32, i32, i32, P, P]
+        L.vco_argsort_labels.argtypes = [P, i32, i32, P]
+        L.vco_smooth_apply.argtypes = [P, i64, P, i64, i32, i32, P, P, P, P, P, P, P]
+        L.vco_tile_order.argtypes = [i32, i32, i32, i32, P]
+        L.vco_attn_emulate_rows.argtypes = [P, P, P, P, P, P, P, i32, i32, f32, i32, i32, P, i32, P, P, P]
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+# --------------------------------------------------------------------------- #
+# scalars and small codecs
+# --------------------------------------------------------------------------- #
+
+def bf16_bits_to_f32(x: np.ndarray) -> np.ndarray:
+    return (x.astype(np.uint32) << 16).view(np.float32)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    L = lib()
+    flat = np.ascontiguousarray(x, dtype=np.float32).ravel()
+    return np.array([L.vco_f32_to_bf16(float(v)) for v in flat], dtype=np.uint16).reshape(np.shape(x))
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    L = lib()
+    table = np.array([L.vco_e4m3_decode(c) for c in range(256)], dtype=np.float64)
+    return table[np.asarray(codes, dtype=np.uint8)]
+
+
+def e4m3_encode(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint8)
+    lib().vco_e4m3_encode_array(_p(x), x.size, _p(out))
+    return out
+
+
+def expcast_codes(x: np.ndarray, a: np.ndarray, b: np.ndarray, row_len: int) -> np.ndarray:
+    """codes[i] = clip_[0,120](RNE(fmaf(a[row], x[i], b[row]))), row = i // row_len."""
+    x = np.ascontiguousarray(x, dtype=np.float32).ravel()
+    a = np.ascontiguousarray(a, dtype=np.float32).ravel()
+    b = np.ascontiguousarray(b, dtype=np.float32).ravel()
+    assert x.size == a.size * row_len == b.size * row_len
+    out = np.empty(x.size, dtype=np.uint8)
+    lib().vco_expcast_codes(_p(x), _p(a), _p(b), x.size, row_len, _p(out))
+    return out
+
+
+def expcast_code_u(u: float, beta: float = -0.35) -> int:
+    return int(lib().vco_expcast_code_u(float(u), float(beta)))
+
+
+# --------------------------------------------------------------------------- #
+# quantisers ([B,S,H,D] bf16 bits in, per-head outputs)
+# --------------------------------------------------------------------------- #
+
+def _head(x: np.ndarray, b: int, h: int) -> np.ndarray:
+    return np.ascontiguousarray(x[b, :, h, :])
+
+
+def quantize_qk(x: np.ndarray):
+    """Per-128-token-block E4M3.  x: uint16 [B,S,H,D].
+    Returns codes uint8 [B,H,S_pad,D], scales fp32 [B,H,nblk]."""
+    B, S, H, D = x.shape
+    nblk = (S + 127) // 128
+    codes = np.zeros((B, H, nblk * 128, D), np.uint8)
+    scales = np.zeros((B, H, nblk), np.float32)
+    L = lib()
+    for b in range(B):
+        for h in range(H):
+            xh = _head(x, b, h)
+            c = np.zeros((nblk * 128, D), np.uint8)
+            s = np.zeros(nblk, np.float32)
+            L.vco_quantize_blocks(_p(xh), D, S, D, _p(c), _p(s))
+            codes[b, h], scales[b, h] = c, s
+    return codes, scales
+
+
+def quantize_v(x: np.ndarray):
+    """Per-head E4M3, key-contiguous.  Returns codes uint8 [B,H,D,S_pad],
+    scales fp32 [B,H,D] (the head's scale repeated over channels)."""
+    B, S, H, D = x.shape
+    S_pad = (S + 127) // 128 * 128
+    codes = np.zeros((B, H, D, S_pad), np.uint8)
+    scales = np.zeros((B, H, D), np.float32)
+    L = lib()
+    for b in range(B):
+        for h in range(H):
+            xh = _head(x, b, h)
+            c = np.zeros((D, S_pad), np.uint8)
+            s = L.vco_quantize_v_head(_p(xh), D, S, D, _p(c))
+            codes[b, h], scales[b, h, :] = c, s
+    return codes, scales
+
+
+# --------------------------------------------------------------------------- #
+# V-Smooth grouping
+# --------------------------------------------------------------------------- #
+
+def splitmix64_stream(seed: int, n: int) -> list:
+    out = np.zeros(n, np.uint64)
+    lib().vco_splitmix64_stream(seed, n, _p(out))
+    return [int(x) for x in out]
+
+
+def forgy_indices(seed: int, b: int, h: int, H: int, S: int, k: int) -> np.ndarray:
+    out = np.zeros(k, np.int32)
+    lib().vco_forgy_indices(seed, b, h, H, S, k, _p(out))
+    return out
+
+
+def kmeans_head(v_head: np.ndarray, k: int, iters: int, seed: int, b: int, h: int, H: int,
+                init: np.ndarray | None = None):
+    """v_head: uint16 [S,D].  Returns (labels int32 [S], centroids fp32 [k,D])."""
+    v_head = np.ascontiguousarray(v_head)
+    S, D = v_head.shape
+    cent = np.zeros((k, D), np.float32) if init is None else np.ascontiguousarray(init, np.float32).copy()
+    labels = np.zeros(S, np.int32)
+    lib().vco_kmeans(_p(v_head), D, S, D, k, iters, seed, b, h, H, 0 if init is None else 1, _p(cent),
+                     _p(labels))
+    return labels, cent
+
+
+def argsort_labels(labels: np.ndarray, k: int) -> np.ndarray:
+    labels = np.ascontiguousarray(labels, np.int32)
+    perm = np.zeros(labels.size, np.int32)
+    lib().vco_argsort_labels(_p(labels), labels.size, k, _p(perm))
+    return perm
+
+
+def smooth_apply_head(k_head: np.ndarray, v_head: np.ndarray, perm: np.ndarray):
+    k_head, v_head = np.ascontiguousarray(k_head), np.ascontiguousarray(v_head)
+    perm = np.ascontiguousarray(perm, np.int32)
+    S, D = v_head.shape
+    nblk = (S + 127) // 128
+    out = dict(
+        mu_bf16=np.zeros((nblk, D), np.uint16),
+        mu_scaled=np.zeros((nblk, D), np.float32),
+        r_codes=np.zeros((D, nblk * 128), np.uint8),
+        r_scale=np.zeros(D, np.float32),
+        k_codes=np.zeros((nblk * 128, D), np.uint8),
+        k_scale=np.zeros(nblk, np.float32),
+    )
+    lib().vco_smooth_apply(_p(k_head), D, _p(v_head), D, S, D, _p(perm), _p(out["mu_bf16"]),
+                           _p(out["mu_scaled"]), _p(out["r_codes"]), _p(out["r_scale"]),
+                           _p(out["k_codes"]), _p(out["k_scale"]))
+    return out
+
+
+def smooth_group(k: np.ndarray, v: np.ndarray, nclust: int, iters: int, seed: int, heads=None):
+    """The whole grouping step for the listed (b, h) heads (default: all).
+    k, v: uint16 [B,S,H,D].  Returns {(b,h): dict(labels, centroids, perm, ...)}."""
+    B, S, H, D = v.shape
+    heads = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    res = {}
+    for (b, h) in heads:
+        labels, cent = kmeans_head(_head(v, b, h), nclust, iters, seed, b, h, H)
+        perm = argsort_labels(labels, nclust)
+        d = smooth_apply_head(_head(k, b, h), _head(v, b, h), perm)
+        d.update(labels=labels, centroids=cent, perm=perm)
+        res[(b, h)] = d
+    return res
+
+
+# --------------------------------------------------------------------------- #
+# attention emulation
+# --------------------------------------------------------------------------- #
+
+def tile_order(qt: int, nblk: int, window: int = 2, sequential: bool = False) -> np.ndarray:
+    out = np.zeros(nblk, np.int32)
+    lib().vco_tile_order(qt, nblk, window, 1 if sequential else 0, _p(out))
+    return out
+
+
+def attn_emulate_rows(q_codes, q_scale, k_codes, k_scale, v_codes_t, v_scale, mu_scaled, S, sm_scale,
+                      rows, window=2, flags=0):
+    """One head.  q_codes/k_codes [S_pad,D], v_codes_t [D,S_pad], scales as
+    produced by the quantisers, mu_scaled [nblk,D] or None.
+    Returns (out_f32 [n,D], out_bf16 bits [n,D], stats [n,2])."""
+    q_codes = np.ascontiguousarray(q_codes, np.uint8)
+    k_codes = np.ascontiguousarray(k_codes, np.uint8)
+    v_codes_t = np.ascontiguousarray(v_codes_t, np.uint8)
+    q_scale = np.ascontiguousarray(q_scale, np.float32)
+    k_scale = np.ascontiguousarray(k_scale, np.float32)
+    v_scale = np.ascontiguousarray(v_scale, np.float32)
+    D = q_codes.shape[1]
+    rows = np.ascontiguousarray(rows, np.int32)
+    n = rows.size
+    of = np.zeros((n, D), np.float32)
+    ob = np.zeros((n, D), np.uint16)
+    st = np.zeros((n, 2), np.float64)
+    mu_p = None
+    if mu_scaled is not None:
+        mu_scaled = np.ascontiguousarray(mu_scaled, np.float32)
+        mu_p = _p(mu_scaled)
+    lib().vco_attn_emulate_rows(_p(q_codes), _p(q_scale), _p(k_codes), _p(k_scale), _p(v_codes_t),
+                                _p(v_scale), mu_p, S, D, float(sm_scale), window, flags, _p(rows), n,
+                                _p(of), _p(ob), _p(st))
+    return of, ob, st
+
+
+def pipeline_head(q, k, v, b, h, *, vsmooth, nclust=64, iters=4, seed=0, sm_scale=None, rows=None,
+                  window=2, flags=0):
+    """Full oracle pipeline for one head from bf16 inputs [B,S,H,D]:
+    quantise, (group,) emulate the listed query rows.  Returns a dict."""
+    B, S, H, D = q.shape
+    sm_scale = 1.0 / np.sqrt(D) if sm_scale is None else sm_scale
+    rows = np.arange(S) if rows is None else np.asarray(rows)
+    qh = _head(q, b, h)
+    nblk = (S + 127) // 128
+    qc = np.zeros((nblk * 128, D), np.uint8)
+    qs = np.zeros(nblk, np.float32)
+    lib().vco_quantize_blocks(_p(qh), D, S, D, _p(qc), _p(qs))
+    out = dict(q_codes=qc, q_scale=qs)
+    if vsmooth:
+        labels, cent = kmeans_head(_head(v, b, h), nclust, iters, seed, b, h, H)
+        perm = argsort_labels(labels, nclust)
+        g = smooth_apply_head(_head(k, b, h), _head(v, b, h), perm)
+        out.update(g, labels=labels, centroids=cent, perm=perm)
+        kc, ks, vc, vs, mu = g["k_codes"], g["k_scale"], g["r_codes"], g["r_scale"], g["mu_scaled"]
+    else:
+        kh = _head(k, b, h)
+        kc = np.zeros((nblk * 128, D), np.uint8)
+        ks = np.zeros(nblk, np.float32)
+        lib().vco_quantize_blocks(_p(kh), D, S, D, _p(kc), _p(ks))
+        vc = np.zeros((D, nblk * 128), np.uint8)
+        s = lib().vco_quantize_v_head(_p(_head(v, b, h)), D, S, D, _p(vc))
+        vs = np.full(D, s, np.float32)
+        mu = None
+        out.update(k_codes=kc, k_scale=ks, v_codes=vc, v_scale=vs)
+    of, ob, st = attn_emulate_rows(qc, qs, kc, ks, vc, vs, mu, S, sm_scale, rows, window, flags)
+    out.update(out_f32=of, out_bf16=ob, stats=st, rows=rows)
+    return out

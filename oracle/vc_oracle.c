@@ -1,0 +1,488 @@
+/*
+ * vc_oracle.c -- plain, slow CPU oracle for the VC-Attention hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline leg do.  It shares no code, header, table or constant generator
+ * with the HIP library.
+ *
+ * Sources (web pages, cited by title and place):
+ *   [VC]   "VC-Attention: Value Smoothing and Softmax Casting for Low-bit
+ *          Attention" (arXiv 2609.15810).
+ *   [OVC]  "Open-VC Attention: an open-source, error-tunable variant of
+ *          VC-Attention" (machgen.ai blog).
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no -ffast-math:
+ * every fp32 operation here is an IEEE-754 operation in round-to-nearest-
+ * even, denormals kept).  Floating point steps the GPU performs in fp32 are
+ * written out one by one in fp32 (fmaf where the method folds a multiply-add,
+ * plain * and / otherwise); sums the matrix cores accumulate are done here
+ * in fp64.
+ *
+ * Readings where the pages leave a step open are stated at each function and
+ * collected in the design doc.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define EXPORT __attribute__((visibility("default")))
+
+/* ------------------------------------------------------------------------ */
+/* bf16 <-> fp32                                                            */
+/* ------------------------------------------------------------------------ */
+
+static float bf16_to_f32(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+/* Round-to-nearest-even of an fp32 value to bf16 (finite inputs). */
+static uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffff) ? 0x40 : 0));
+  uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7fffu + lsb;
+  return (uint16_t)(u >> 16);
+}
+
+EXPORT uint16_t vco_f32_to_bf16(float f) { return f32_to_bf16_rne(f); }
+
+/* ------------------------------------------------------------------------ */
+/* E4M3 (OCP E4M3FN: bias 7, no infinities, 0x7F/0xFF are NaN, max 448).    */
+/* [VC] §3.3: a byte with exponent field e and mantissa field m encodes      */
+/* 2^(e-7)(1+m/8); e = 0 holds the subnormals m * 2^-9.                     */
+/* ------------------------------------------------------------------------ */
+
+EXPORT double vco_e4m3_decode(uint8_t c) {
+  int e = (c >> 3) & 15, m = c & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp(1.0 + m / 8.0, e - 7);
+  return (c & 0x80) ? -v : v;
+}
+
+static double g_e4m3_pos[127]; /* decoded values of codes 0..126 */
+static double g_e4m3_all[256]; /* decoded values of all 256 bytes */
+static int g_e4m3_init = 0;
+
+static void e4m3_table_init(void) {
+  if (g_e4m3_init) return;
+  for (int c = 0; c < 256; ++c) g_e4m3_all[c] = vco_e4m3_decode((uint8_t)c);
+  for (int c = 0; c < 127; ++c) g_e4m3_pos[c] = g_e4m3_all[c];
+  g_e4m3_init = 1;
+}
+
+#define DEC(c) (g_e4m3_all[(uint8_t)(c)])
+
+/*
+ * Encode: the finite E4M3 code nearest to x, ties to the code with an even
+ * mantissa (= even code), magnitudes beyond 448 saturating to 448 (the
+ * nearest finite code).  The sign bit is x's sign bit.  Written as a search
+ * over all 127 non-negative codes so that it is correct by inspection.
+ * Reading: the pages fix the format and round-to-nearest-even but not the
+ * handling of overflow; saturation is used (inputs here never exceed 448 by
+ * more than an fp32 rounding).
+ */
+EXPORT uint8_t vco_e4m3_encode(float x) {
+  e4m3_table_init();
+  double a = fabs((double)x);
+  int best = 0;
+  double bd = fabs(a - g_e4m3_pos[0]);
+  for (int c = 1; c < 127; ++c) {
+    double d = fabs(a - g_e4m3_pos[c]);
+    if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1)) {
+      bd = d;
+      best = c;
+    }
+  }
+  return (uint8_t)(best | (signbit(x) ? 0x80 : 0));
+}
+
+EXPORT void vco_e4m3_encode_array(const float* x, int64_t n, uint8_t* codes) {
+  for (int64_t i = 0; i < n; ++i) codes[i] = vco_e4m3_encode(x[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* ExpCast-FP8 code, [VC] §3.3 Eq. 7 and Fig. 2:                            */
+/*   c = clip_[0,120]( Round( a*x + b ) ),  Round = round-half-even,         */
+/* with a*x+b formed by one fp32 fused multiply-add.                         */
+/* ------------------------------------------------------------------------ */
+
+static int expcast_code_f32(float a, float x, float b) {
+  float y = fmaf(a, x, b);
+  float r = nearbyintf(y); /* default rounding mode: nearest-even */
+  if (!(r > 0.0f)) return 0; /* also maps -inf to code 0 */
+  if (r > 120.0f) return 120;
+  return (int)r;
+}
+
+EXPORT void vco_expcast_codes(const float* x, const float* a, const float* b, int64_t n,
+                              int32_t row_len, uint8_t* codes) {
+  for (int64_t i = 0; i < n; ++i) {
+    int64_t row = i / row_len;
+    codes[i] = (uint8_t)expcast_code_f32(a[row], x[i], b[row]);
+  }
+}
+
+/* Real-number closed form of Eq. 7 evaluated in fp64 for a log2-domain u. */
+EXPORT int vco_expcast_code_u(double u, double beta) {
+  double y = 8.0 * (u + 8.0) + 56.0 + beta;
+  double r = nearbyint(y);
+  if (!(r > 0.0)) return 0;
+  if (r > 120.0) return 120;
+  return (int)r;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Quantizers, [OVC] "Scheduling around ExpCast": Q and K take one scale per */
+/* 128-token block, V one scale per head; X_q = s_X * Xhat ([VC] §3.1).      */
+/* Reading: s = amax/448 and the codes are E4M3(x * (448/amax)) with both    */
+/* quotients rounded to fp32; a block of zeros takes s = 1.                  */
+/* ------------------------------------------------------------------------ */
+
+static void scale_pair(float amax, float* s, float* inv) {
+  if (amax > 0.0f) {
+    *s = amax / 448.0f;
+    *inv = 448.0f / amax;
+  } else {
+    *s = 1.0f;
+    *inv = 1.0f;
+  }
+}
+
+/*
+ * One head.  x: bf16 rows, row r at x + r*ld (D contiguous).
+ * Out: codes [nblk*128][D] (rows >= S are zero), scale [nblk].
+ */
+EXPORT void vco_quantize_blocks(const uint16_t* x, int64_t ld, int32_t S, int32_t D, uint8_t* codes,
+                                float* scale) {
+  int32_t nblk = (S + 127) / 128;
+  for (int32_t j = 0; j < nblk; ++j) {
+    int32_t r0 = j * 128, r1 = r0 + 128 < S ? r0 + 128 : S;
+    float amax = 0.0f;
+    for (int32_t r = r0; r < r1; ++r)
+      for (int32_t d = 0; d < D; ++d) amax = fmaxf(amax, fabsf(bf16_to_f32(x[r * ld + d])));
+    float s, inv;
+    scale_pair(amax, &s, &inv);
+    scale[j] = s;
+    for (int32_t r = r0; r < j * 128 + 128; ++r)
+      for (int32_t d = 0; d < D; ++d)
+        codes[(int64_t)r * D + d] = (r < S) ? vco_e4m3_encode(bf16_to_f32(x[r * ld + d]) * inv) : 0;
+  }
+}
+
+/*
+ * Per-head V (plain path).  Out: codes in key-contiguous order
+ * codes_t[d][S_pad] (pad keys zero), one scale.
+ */
+EXPORT float vco_quantize_v_head(const uint16_t* x, int64_t ld, int32_t S, int32_t D,
+                                 uint8_t* codes_t) {
+  int32_t S_pad = (S + 127) / 128 * 128;
+  float amax = 0.0f;
+  for (int32_t r = 0; r < S; ++r)
+    for (int32_t d = 0; d < D; ++d) amax = fmaxf(amax, fabsf(bf16_to_f32(x[r * ld + d])));
+  float s, inv;
+  scale_pair(amax, &s, &inv);
+  for (int32_t d = 0; d < D; ++d)
+    for (int32_t r = 0; r < S_pad; ++r)
+      codes_t[(int64_t)d * S_pad + r] = (r < S) ? vco_e4m3_encode(bf16_to_f32(x[r * ld + d]) * inv) : 0;
+  return s;
+}
+
+/* ------------------------------------------------------------------------ */
+/* V-Smooth grouping, [VC] §3.2 "Value-guided permutation" and "Unbalanced   */
+/* clusters cost little": per (b,h) an online k-means over the value tokens  */
+/* gives labels z; pi = argsort(z); K' = K[pi], V' = V[pi].                  */
+/* Readings (the pages give no initialisation, precision or tie rule):       */
+/*  - Lloyd iterations, Forgy initialisation: k distinct token indices from  */
+/*    a partial Fisher-Yates shuffle driven by SplitMix64;                   */
+/*  - squared distance up to the token's own norm, |c|^2 - 2 v.c, each dot    */
+/*    product one fp32 fused-multiply-add chain over channels 0..D-1, ties   */
+/*    to the lowest cluster index;                                           */
+/*  - cluster sums in 64-bit fixed point with 24 fraction bits, so the sum   */
+/*    does not depend on the order tokens are added; an empty cluster keeps  */
+/*    its centroid;                                                          */
+/*  - labels are those of the last assignment, centroids those after the    */
+/*    last update;                                                           */
+/*  - argsort is stable (ties keep token order).                             */
+/* ------------------------------------------------------------------------ */
+
+/* SplitMix64 (Steele, Lea and Flood, 2014), from its published definition. */
+static uint64_t splitmix64_next(uint64_t* st) {
+  uint64_t z = (*st += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+/* The first n outputs of a SplitMix64 stream started at state `seed`. */
+EXPORT void vco_splitmix64_stream(uint64_t seed, int32_t n, uint64_t* out) {
+  uint64_t st = seed;
+  for (int32_t i = 0; i < n; ++i) out[i] = splitmix64_next(&st);
+}
+
+/* The k initial token indices for head (b, h) of a batch with H heads. */
+EXPORT void vco_forgy_indices(uint64_t seed, int32_t b, int32_t h, int32_t H, int32_t S, int32_t k,
+                              int32_t* idx) {
+  int32_t* a = (int32_t*)malloc(sizeof(int32_t) * (size_t)S);
+  for (int32_t i = 0; i < S; ++i) a[i] = i;
+  uint64_t st = seed + 0x9E3779B97F4A7C15ull * (uint64_t)(1 + (int64_t)b * H + h);
+  for (int32_t i = 0; i < k; ++i) {
+    uint64_t r = splitmix64_next(&st);
+    uint32_t j = (uint32_t)i + (uint32_t)(((r >> 32) * (uint64_t)(uint32_t)(S - i)) >> 32);
+    int32_t t = a[i];
+    a[i] = a[j];
+    a[j] = t;
+  }
+  for (int32_t i = 0; i < k; ++i) idx[i] = a[i];
+  free(a);
+}
+
+static int64_t fx24(float v) { return llrint((double)v * 16777216.0); }
+
+static float fx24_mean(int64_t sum, int64_t n) {
+  return (float)(((double)sum * (1.0 / 16777216.0)) / (double)n);
+}
+
+/* Squared-norm chain of one centroid. */
+static float cnorm(const float* c, int32_t D) {
+  float n = 0.0f;
+  for (int32_t d = 0; d < D; ++d) n = fmaf(c[d], c[d], n);
+  return n;
+}
+
+/*
+ * One head.  v: bf16 rows at v + r*ld.  cent [k][D] fp32: initial centroids
+ * on entry when warm != 0, else overwritten from the Forgy indices; final
+ * centroids on exit.  labels [S].
+ */
+EXPORT void vco_kmeans(const uint16_t* v, int64_t ld, int32_t S, int32_t D, int32_t k, int32_t iters,
+                       uint64_t seed, int32_t b, int32_t h, int32_t H, int32_t warm, float* cent,
+                       int32_t* labels) {
+  if (!warm) {
+    int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+    vco_forgy_indices(seed, b, h, H, S, k, idx);
+    for (int32_t c = 0; c < k; ++c)
+      for (int32_t d = 0; d < D; ++d) cent[c * D + d] = bf16_to_f32(v[(int64_t)idx[c] * ld + d]);
+    free(idx);
+  }
+  float* nrm = (float*)malloc(sizeof(float) * (size_t)k);
+  int64_t* sum = (int64_t*)malloc(sizeof(int64_t) * (size_t)k * D);
+  int64_t* cnt = (int64_t*)malloc(sizeof(int64_t) * (size_t)k);
+  for (int32_t it = 0; it < iters; ++it) {
+    for (int32_t c = 0; c < k; ++c) nrm[c] = cnorm(cent + (int64_t)c * D, D);
+    /* assignment: tokens are independent */
+#pragma omp parallel for schedule(static)
+    for (int32_t t = 0; t < S; ++t) {
+      float vt[256];
+      for (int32_t d = 0; d < D; ++d) vt[d] = bf16_to_f32(v[(int64_t)t * ld + d]);
+      int32_t best = 0;
+      float bd = 0.0f;
+      for (int32_t c = 0; c < k; ++c) {
+        const float* cc = cent + (int64_t)c * D;
+        float dot = 0.0f;
+        for (int32_t d = 0; d < D; ++d) dot = fmaf(vt[d], cc[d], dot);
+        float dist = fmaf(-2.0f, dot, nrm[c]);
+        if (c == 0 || dist < bd) {
+          bd = dist;
+          best = c;
+        }
+      }
+      labels[t] = best;
+    }
+    /* update: member means */
+    memset(sum, 0, sizeof(int64_t) * (size_t)k * D);
+    memset(cnt, 0, sizeof(int64_t) * (size_t)k);
+    for (int32_t t = 0; t < S; ++t) {
+      int32_t c = labels[t];
+      cnt[c] += 1;
+      for (int32_t d = 0; d < D; ++d) sum[(int64_t)c * D + d] += fx24(bf16_to_f32(v[(int64_t)t * ld + d]));
+    }
+    for (int32_t c = 0; c < k; ++c)
+      if (cnt[c] > 0)
+        for (int32_t d = 0; d < D; ++d) cent[(int64_t)c * D + d] = fx24_mean(sum[(int64_t)c * D + d], cnt[c]);
+  }
+  free(nrm);
+  free(sum);
+  free(cnt);
+}
+
+/* pi = stable argsort of the labels (counting sort). */
+EXPORT void vco_argsort_labels(const int32_t* labels, int32_t S, int32_t k, int32_t* perm) {
+  int64_t* off = (int64_t*)calloc((size_t)k + 1, sizeof(int64_t));
+  for (int32_t t = 0; t < S; ++t) off[labels[t] + 1] += 1;
+  for (int32_t c = 0; c < k; ++c) off[c + 1] += off[c];
+  for (int32_t t = 0; t < S; ++t) perm[off[labels[t]]++] = t;
+  free(off);
+}
+
+/*
+ * Block demeaning and residual quantisation, [VC] §3.2 Eq. 4 and Appendix B:
+ * mu_j is the mean of block j of V' (B_v = 128 rows), stored as a 16-bit
+ * vector; R_j = V'_j - 1 mu_j^T goes through the per-channel E4M3 value
+ * quantiser; the means are stored divided by the per-channel value scale.
+ * Readings: mu is bf16 (round-to-nearest-even of the fp32 mean); the tail
+ * block averages over its valid rows; the scaled mean is kept in fp32;
+ * K' is quantised per 128-row block in permuted order like K.
+ *
+ * Out (one head): mu_bf16 [nblk][D], mu_scaled [nblk][D], r_codes_t [D][S_pad]
+ * (key-contiguous, pad zero), r_scale [D], k_codes [S_pad][D], k_scale [nblk].
+ */
+EXPORT void vco_smooth_apply(const uint16_t* k, int64_t ldk, const uint16_t* v, int64_t ldv, int32_t S,
+                             int32_t D, const int32_t* perm, uint16_t* mu_bf16, float* mu_scaled,
+                             uint8_t* r_codes_t, float* r_scale, uint8_t* k_codes, float* k_scale) {
+  int32_t nblk = (S + 127) / 128, S_pad = nblk * 128;
+  float* R = (float*)malloc(sizeof(float) * (size_t)S * D);
+  float* amax = (float*)calloc((size_t)D, sizeof(float));
+  for (int32_t j = 0; j < nblk; ++j) {
+    int32_t r0 = j * 128, r1 = r0 + 128 < S ? r0 + 128 : S;
+    for (int32_t d = 0; d < D; ++d) {
+      int64_t s = 0;
+      for (int32_t r = r0; r < r1; ++r) s += fx24(bf16_to_f32(v[(int64_t)perm[r] * ldv + d]));
+      uint16_t mu = f32_to_bf16_rne(fx24_mean(s, r1 - r0));
+      mu_bf16[(int64_t)j * D + d] = mu;
+      float muf = bf16_to_f32(mu);
+      for (int32_t r = r0; r < r1; ++r) {
+        float x = bf16_to_f32(v[(int64_t)perm[r] * ldv + d]) - muf;
+        R[(int64_t)r * D + d] = x;
+        amax[d] = fmaxf(amax[d], fabsf(x));
+      }
+    }
+  }
+  for (int32_t d = 0; d < D; ++d) {
+    float s, inv;
+    scale_pair(amax[d], &s, &inv);
+    r_scale[d] = s;
+    for (int32_t r = 0; r < S_pad; ++r)
+      r_codes_t[(int64_t)d * S_pad + r] = (r < S) ? vco_e4m3_encode(R[(int64_t)r * D + d] * inv) : 0;
+    for (int32_t j = 0; j < nblk; ++j)
+      mu_scaled[(int64_t)j * D + d] = bf16_to_f32(mu_bf16[(int64_t)j * D + d]) * inv;
+  }
+  /* K' = K[pi], quantised per block */
+  uint16_t* kp = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)S * D);
+  for (int32_t r = 0; r < S; ++r)
+    for (int32_t d = 0; d < D; ++d) kp[(int64_t)r * D + d] = k[(int64_t)perm[r] * ldk + d];
+  vco_quantize_blocks(kp, D, S, D, k_codes, k_scale);
+  free(kp);
+  free(R);
+  free(amax);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Attention emulation, one query row at a time.                            */
+/*  - online softmax recurrence: [VC] §3.1 Eq. 1;                            */
+/*  - running maximum on the true score, every increase applied, and the    */
+/*    scale folding into one fused multiply-add per score: [OVC]            */
+/*    "Scheduling around ExpCast";                                          */
+/*  - ExpCast code: [VC] §3.3 Eq. 7 (beta = -0.35, so the additive constant  */
+/*    is 120 + beta = 119.65);                                              */
+/*  - row sum over the same decoded codes: [OVC] "A consistent denominator"; */
+/*  - mean restoration A <- aA + P R_q + r mu^T: [VC] §3.2 Eq. 6;           */
+/*  - mid-window key order: [OVC] "Mid-window key traversal".               */
+/* ------------------------------------------------------------------------ */
+
+/* Visit order of the key blocks for query tile qt. */
+EXPORT void vco_tile_order(int32_t qt, int32_t nblk, int32_t window, int32_t sequential, int32_t* order) {
+  if (sequential) {
+    for (int32_t i = 0; i < nblk; ++i) order[i] = i;
+    return;
+  }
+  int32_t start = qt + window < nblk - 1 ? qt + window : nblk - 1;
+  int32_t n = 0;
+  for (int32_t t = start; t >= 0; --t) order[n++] = t;
+  for (int32_t t = start + 1; t < nblk; ++t) order[n++] = t;
+}
+
+#define VCO_SEQUENTIAL 1
+#define VCO_EXACT_EXP 2
+
+/*
+ * q_codes [S_pad][D] with q_scale [nblk] (query rows in token order),
+ * k_codes [S_pad][D] with k_scale [nblk], v_codes_t [D][S_pad] with
+ * v_scale [D], mu_scaled [nblk][D] or NULL for the plain path.
+ * rows: n query indices.  Out: out_f32 [n][D] (pre-rounding output, fp32)
+ * and out_bf16 [n][D]; stats (may be NULL) [n][2] = {rescales, final max M}.
+ */
+EXPORT void vco_attn_emulate_rows(const uint8_t* q_codes, const float* q_scale, const uint8_t* k_codes,
+                                  const float* k_scale, const uint8_t* v_codes_t, const float* v_scale,
+                                  const float* mu_scaled, int32_t S, int32_t D, float sm_scale,
+                                  int32_t window, int32_t flags, const int32_t* rows, int32_t n,
+                                  float* out_f32, uint16_t* out_bf16, double* stats) {
+  int32_t nblk = (S + 127) / 128, S_pad = nblk * 128;
+  const float log2e = 1.44269504088896340736f;
+  double dq[256];
+  e4m3_table_init();
+#pragma omp parallel for schedule(dynamic, 1) private(dq)
+  for (int32_t ri = 0; ri < n; ++ri) {
+    int32_t i = rows[ri];
+    int32_t qt = i / 128;
+    int32_t* order = (int32_t*)malloc(sizeof(int32_t) * (size_t)nblk);
+    vco_tile_order(qt, nblk, window, flags & VCO_SEQUENTIAL, order);
+    double* A = (double*)calloc((size_t)D, sizeof(double));
+    float acc[128];
+    double l = 0.0;
+    float M = -INFINITY;
+    int32_t rescales = 0;
+    float c2 = (sm_scale * log2e) * q_scale[qt];
+    for (int32_t d = 0; d < D; ++d) dq[d] = DEC(q_codes[(int64_t)i * D + d]);
+    for (int32_t oi = 0; oi < nblk; ++oi) {
+      int32_t t = order[oi];
+      int32_t k0 = t * 128, k1 = k0 + 128 < S ? k0 + 128 : S;
+      float mxacc = -INFINITY;
+      for (int32_t kk = k0; kk < k1; ++kk) {
+        double s = 0.0; /* exact: FP8 x FP8 products summed over D <= 256 fit in fp64 */
+        for (int32_t d = 0; d < D; ++d) s += dq[d] * DEC(k_codes[(int64_t)kk * D + d]);
+        acc[kk - k0] = (float)s;
+        mxacc = fmaxf(mxacc, acc[kk - k0]);
+      }
+      float g = c2 * k_scale[t];
+      float mx = g * mxacc;
+      float Mn = fmaxf(M, mx);
+      if (Mn > M) {
+        double alpha = (M == -INFINITY) ? 0.0 : exp2((double)M - (double)Mn);
+        for (int32_t d = 0; d < D; ++d) A[d] *= alpha;
+        l *= alpha;
+        if (M != -INFINITY) rescales += 1;
+        M = Mn;
+      }
+      float a = 8.0f * g;
+      float b = 119.65f - 8.0f * M;
+      double r = 0.0;
+      for (int32_t kk = k0; kk < k1; ++kk) {
+        double w;
+        if (flags & VCO_EXACT_EXP) {
+          /* diagnostic: fp32 exponential then an E4M3 cast ([VC] Prop. 3.1 text) */
+          float u = g * acc[kk - k0] - M;
+          w = DEC(vco_e4m3_encode(exp2f(u + 8.0f)));
+        } else {
+          w = DEC(expcast_code_f32(a, acc[kk - k0], b));
+        }
+        if (w == 0.0) continue;
+        r += w;
+        for (int32_t d = 0; d < D; ++d) A[d] += w * DEC(v_codes_t[(int64_t)d * S_pad + kk]);
+      }
+      if (mu_scaled)
+        for (int32_t d = 0; d < D; ++d) A[d] += r * (double)mu_scaled[(int64_t)t * D + d];
+      l += r;
+    }
+    for (int32_t d = 0; d < D; ++d) {
+      float o = (float)((A[d] / l) * (double)v_scale[d]);
+      out_f32[(int64_t)ri * D + d] = o;
+      out_bf16[(int64_t)ri * D + d] = f32_to_bf16_rne(o);
+    }
+    if (stats) {
+      stats[2 * ri] = rescales;
+      stats[2 * ri + 1] = M;
+    }
+    free(A);
+    free(order);
+  }
+}
