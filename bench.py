@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Benchmark of the VC-Attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic
+Wan2.2-720p-shaped input (B=1, H=40, S=75600 = 21x45x80, D=128), inputs
+resident in HBM:  vc_quantize(Q) -> vc_smooth_group(K, V: 64-cluster k-means,
+4 iterations, argsort, K/V permute, block means, E4M3 residuals) ->
+vc_attn_fwd (FP8 matrix cores, ExpCast codes, mean restoration, mid-window
+key order).
+
+Reported `value` is the metric the workload is quoted on: vc_attn_fwd
+TFLOP/s (4*S^2*D*H algorithmic flops over the attention kernel's duration,
+HIP events on the stream it runs on), with `roofline` against the published
+dense FP8 matrix-core peak; `ms_per_step` is the whole path.  The CPU oracle
+is timed on a bounded sample of the same workload (`cpu_baseline`), and the
+in-house BF16 baseline on the same kernel skeleton gives the speedup.
+
+Usage: python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--workload wan]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP8_PEAK_TFLOPS = 5000.0   # MI355X published dense FP8 matrix-core peak
+BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense BF16 matrix-core peak
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fp8_wan_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "bit_fp8_attention_amd", "csrc", "vc_attn_fp8.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_from_profile():
+    """HBM bytes per launch of the attention kernel from the committed
+    rocprofv3 counter summary, or None when the kernel has changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != _sha(ATTN_SRC):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, target_s=12.0):
+    """The oracle as it stands on head 0 of the same inputs: quantise and
+    group the head (untimed, like the GPU's preparation), then emulate a
+    growing number of full-length query rows until about target_s seconds."""
+    import numpy as np
+
+    import oracle
+    import vcsynth
+    qb = vcsynth.bf16_bits(q[:, :, :1])
+    kb = vcsynth.bf16_bits(k[:, :, :1])
+    vb = vcsynth.bf16_bits(v[:, :, :1])
+    t0 = time.perf_counter()
+    prep = oracle.pipeline_head(qb, kb, vb, 0, 0, vsmooth=w.vsmooth, nclust=w.clusters or 64, iters=w.iters or 4,
+                                seed=w.seed, sm_scale=w.sm_scale, rows=np.array([0]))
+    t_prep = time.perf_counter() - t0
+    mu = prep.get("mu_scaled")
+    kc = prep["k_codes"]
+    ks = prep["k_scale"]
+    vc_ = prep["r_codes"] if w.vsmooth else prep["v_codes"]
+    vs = prep["r_scale"] if w.vsmooth else prep["v_scale"]
+    rng = np.random.default_rng(0)
+    n, elapsed = 8, 0.0
+    while True:
+        rows = np.sort(rng.choice(w.S, n, replace=False))
+        t0 = time.perf_counter()
+        oracle.attn_emulate_rows(prep["q_codes"], prep["q_scale"], kc, ks, vc_, vs, mu, w.S, w.sm_scale, rows)
+        elapsed = time.perf_counter() - t0
+        if elapsed >= target_s / 4 or n >= w.S:
+            break
+        n = min(w.S, int(n * max(2.0, target_s / 4 / max(elapsed, 1e-3))))
+    flops = 4.0 * n * w.S * w.D
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"{n} query rows of head 0 (full {w.S}-key range, {'V-Smooth' if w.vsmooth else 'plain'} "
+                   f"emulation) in {elapsed:.2f} s; the head's oracle quantise+grouping took {t_prep:.1f} s "
+                   f"untimed; extrapolated full call {elapsed * w.S * w.H / n:.0f} s"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="wan")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bf16", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_fp8_attention_amd as vc
+    import vcsynth
+
+    w = vcsynth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.perf_counter()
+    q, k, v = vcsynth.make_qkv(w.name, device=dev)
+    torch.cuda.synchronize()
+    log(f"inputs {w.name} B={w.B} H={w.H} S={w.S} D={w.D} generated in {time.perf_counter() - t0:.1f} s")
+
+    vs_on = w.vsmooth
+    clusters, iters = (w.clusters, w.iters) if vs_on else (0, 0)
+    qz = vc.vc_quantize(q) if vs_on else vc.vc_quantize(q, k, v)
+    if vs_on:
+        ws = torch.empty(vc.vc_smooth_group_workspace_size(w.B, w.H, w.S, w.D, clusters), dtype=torch.uint8,
+                         device=dev)
+        g = vc.vc_smooth_group(k, v, clusters, iters, w.seed, workspace=ws)
+    o = torch.empty_like(q)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+        e = [E() for _ in range(4)] if ev is not None else None
+        if e: e[0].record()
+        if vs_on:
+            vc.vc_quantize(q, out=qz)
+            if e: e[1].record()
+            vc.vc_smooth_group(k, v, clusters, iters, w.seed, workspace=ws, out=g)
+            if e: e[2].record()
+            vc.vc_attn_fwd(qz["q8"], qz["q_scale"], g["k8"], g["k_scale"], g["r8"], g["r_scale"], g["mu_scaled"],
+                           S=w.S, out=o, sm_scale=w.sm_scale)
+        else:
+            vc.vc_quantize(q, k, v, out=qz)
+            if e: e[1].record()
+            if e: e[2].record()
+            vc.vc_attn_fwd(qz["q8"], qz["q_scale"], qz["k8"], qz["k_scale"], qz["v8"], qz["v_scale"], None, S=w.S,
+                           out=o, sm_scale=w.sm_scale)
+        if e:
+            e[3].record()
+            ev.append(e)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"warmup step {i + 1}/{args.warmup} done")
+    evs = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"timed {args.steps} steps in {wall:.3f} s")
+    ms_q = [e[0].elapsed_time(e[1]) for e in evs]
+    ms_g = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_a = [e[2].elapsed_time(e[3]) for e in evs]
+    flops = w.flops()
+    attn_ms = sum(ms_a) / len(ms_a)
+    value = flops / (attn_ms * 1e-3) / 1e12
+    ms_per_step = wall * 1e3 / args.steps
+    assert torch.isfinite(o.float()).all().item(), "non-finite attention output"
+
+    traffic = traffic_from_profile() if (w.name == "wan" and vs_on) else None
+    roof = {"bound": "mfma", "achieved": round(value, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(value / FP8_PEAK_TFLOPS, 4), "traffic": traffic,
+            "kernel": "attn_fp8_kernel<128,%s>" % ("true" if vs_on else "false"),
+            "avg_launch_ms": round(attn_ms, 4), "flops_per_launch": flops}
+
+    bf16 = None
+    if not args.no_bf16:
+        try:
+            vt = vc.vc_pack_v_bf16(v)
+            ob = torch.empty_like(q)
+            for _ in range(2):
+                vc.vc_attn_fwd_bf16(q, k, vt, out=ob, sm_scale=w.sm_scale)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            n = max(3, args.steps)
+            e0.record()
+            for _ in range(n):
+                vc.vc_attn_fwd_bf16(q, k, vt, out=ob, sm_scale=w.sm_scale)
+            e1.record()
+            e1.synchronize()
+            bms = e0.elapsed_time(e1) / n
+            bt = flops / (bms * 1e-3) / 1e12
+            bf16 = {"ms": round(bms, 3), "tflops": round(bt, 1), "frac_of_bf16_peak": round(bt / BF16_PEAK_TFLOPS, 4),
+                    "speedup_fp8_over_bf16": round(bms / attn_ms, 3)}
+            del vt, ob
+        except vc.VcError as ex:
+            log(f"bf16 baseline unavailable: {ex}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(w, q.cpu(), k.cpu(), v.cpu())
+        log(f"cpu baseline: {cpu['sample']}")
+
+    res = {
+        "metric": "vc_attn_fwd TFLOP/s + % FP8 MFMA peak at H=40,S=75600,D=128",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={w.B} H={w.H} S={w.S} D={w.D}" +
+                   (f" grid={'x'.join(map(str, w.grid))}" if w.grid else ""),
+                   "vsmooth": vs_on, "clusters": clusters, "kmeans_iters": iters, "window": 2,
+                   "sm_scale": w.sm_scale},
+        "pct_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
+        "breakdown_ms": {"vc_quantize": round(sum(ms_q) / len(ms_q), 3),
+                         "vc_smooth_group": round(sum(ms_g) / len(ms_g), 3),
+                         "vc_attn_fwd": round(attn_ms, 3)},
+        "path_tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "roofline": roof,
+        "bf16_baseline": bf16,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,255 @@
+"""bit_fp8_attention_amd -- VC-Attention's FP8 attention hot path on MI355X.
+
+Thin ctypes binding over ``libvcattn.so`` (the C ABI in ``include/vc_attn.h``).
+Every step of the path runs in the library's HIP kernels; this module only
+marshals arguments: it takes torch tensors for device memory and the current
+HIP stream, allocates outputs when the caller does not pass them, and raises
+on a non-OK status.  There is no CPU fallback: if the library is missing or
+no GPU is present, calls fail loudly.
+
+Entry points (same names as the C ABI): vc_abi_version, vc_status_str,
+vc_quantize, vc_smooth_group_workspace_size, vc_smooth_group, vc_attn_fwd,
+vc_pack_v_bf16, vc_attn_fwd_bf16, vc_expcast_codes.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvcattn.so")
+_lib = None
+
+VC_OK = 0
+VC_ATTN_SEQUENTIAL = 1
+ABI_VERSION = 1
+
+
+class VcError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {vc_status_str(status)} (status {status})")
+        self.status = status
+
+
+class vc_shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("S", ctypes.c_int32), ("D", ctypes.c_int32)]
+
+
+class vc_bshd(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("sB", ctypes.c_int64), ("sS", ctypes.c_int64), ("sH", ctypes.c_int64)]
+
+
+class vc_bshd_out(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("sB", ctypes.c_int64), ("sS", ctypes.c_int64), ("sH", ctypes.c_int64)]
+
+
+class vc_group_params(ctypes.Structure):
+    _fields_ = [("clusters", ctypes.c_int32), ("iters", ctypes.c_int32), ("seed", ctypes.c_uint64),
+                ("flags", ctypes.c_uint32)]
+
+
+class vc_attn_params(ctypes.Structure):
+    _fields_ = [("sm_scale", ctypes.c_float), ("window", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+def lib():
+    """Load libvcattn.so (built by __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build the HIP library first "
+                               "(python -c 'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        L.vc_abi_version.restype = i32
+        L.vc_status_str.argtypes = [i32]
+        L.vc_status_str.restype = ctypes.c_char_p
+        L.vc_quantize.argtypes = [P] * 11
+        L.vc_quantize.restype = i32
+        L.vc_smooth_group_workspace_size.argtypes = [P, i32]
+        L.vc_smooth_group_workspace_size.restype = sz
+        L.vc_smooth_group.argtypes = [P] * 14 + [sz, P]
+        L.vc_smooth_group.restype = i32
+        L.vc_attn_fwd.argtypes = [P] * 11
+        L.vc_attn_fwd.restype = i32
+        L.vc_pack_v_bf16.argtypes = [P] * 4
+        L.vc_pack_v_bf16.restype = i32
+        L.vc_attn_fwd_bf16.argtypes = [P] * 7
+        L.vc_attn_fwd_bf16.restype = i32
+        L.vc_expcast_codes.argtypes = [P, P, P, i64, i32, P, P]
+        L.vc_expcast_codes.restype = i32
+        _lib = L
+    return _lib
+
+
+def vc_abi_version() -> int:
+    return int(lib().vc_abi_version())
+
+
+def vc_status_str(status: int) -> str:
+    return lib().vc_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != VC_OK:
+        raise VcError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _shape_of(x: torch.Tensor) -> vc_shape:
+    B, S, H, D = x.shape
+    return vc_shape(B, H, S, D)
+
+
+def _bshd(x: torch.Tensor | None) -> vc_bshd:
+    if x is None:
+        return vc_bshd(None, 0, 0, 0)
+    assert x.dtype == torch.bfloat16 and x.dim() == 4 and x.stride(3) == 1, "bf16 [B,S,H,D], D contiguous"
+    return vc_bshd(x.data_ptr(), x.stride(0), x.stride(1), x.stride(2))
+
+
+def _bshd_out(x: torch.Tensor) -> vc_bshd_out:
+    assert x.dtype == torch.bfloat16 and x.dim() == 4 and x.stride(3) == 1, "bf16 [B,S,H,D], D contiguous"
+    return vc_bshd_out(x.data_ptr(), x.stride(0), x.stride(1), x.stride(2))
+
+
+def nblk_of(S: int) -> int:
+    return (S + 127) // 128
+
+
+# --------------------------------------------------------------------------- #
+# vc_quantize
+# --------------------------------------------------------------------------- #
+
+def vc_quantize(q=None, k=None, v=None, *, out=None):
+    """FP8 operands.  q, k, v: bf16 [B,S,H,D] (any may be None).
+    Returns dict with q8, q_scale, k8, k_scale, v8, v_scale (see vc_attn.h)."""
+    ref = next(x for x in (q, k, v) if x is not None)
+    sh = _shape_of(ref)
+    B, H, S, D = sh.B, sh.H, sh.S, sh.D
+    nb = nblk_of(S)
+    dev = ref.device
+    o = dict(out or {})
+    if q is not None:
+        o.setdefault("q8", torch.empty((B, H, nb * 128, D), dtype=torch.uint8, device=dev))
+        o.setdefault("q_scale", torch.empty((B, H, nb), dtype=torch.float32, device=dev))
+    if k is not None:
+        o.setdefault("k8", torch.empty((B, H, nb * 128, D), dtype=torch.uint8, device=dev))
+        o.setdefault("k_scale", torch.empty((B, H, nb), dtype=torch.float32, device=dev))
+    if v is not None:
+        o.setdefault("v8", torch.empty((B, H, D, nb * 128), dtype=torch.uint8, device=dev))
+        o.setdefault("v_scale", torch.empty((B, H, D), dtype=torch.float32, device=dev))
+    qd, kd, vd = _bshd(q), _bshd(k), _bshd(v)
+    st = lib().vc_quantize(ctypes.byref(sh), ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd),
+                           _ptr(o.get("q8")), _ptr(o.get("q_scale")), _ptr(o.get("k8")), _ptr(o.get("k_scale")),
+                           _ptr(o.get("v8")), _ptr(o.get("v_scale")), _stream())
+    _check(st, "vc_quantize")
+    return o
+
+
+# --------------------------------------------------------------------------- #
+# vc_smooth_group
+# --------------------------------------------------------------------------- #
+
+def vc_smooth_group_workspace_size(B: int, H: int, S: int, D: int, clusters: int) -> int:
+    sh = vc_shape(B, H, S, D)
+    return int(lib().vc_smooth_group_workspace_size(ctypes.byref(sh), clusters))
+
+
+def vc_smooth_group(k, v, clusters: int, iters: int, seed: int, *, workspace=None, out=None):
+    """V-Smooth grouping.  k, v: bf16 [B,S,H,D].  Returns dict with centroids,
+    labels, perm, k8, k_scale, r8, r_scale, mu_bf16, mu_scaled."""
+    sh = _shape_of(v)
+    B, H, S, D = sh.B, sh.H, sh.S, sh.D
+    nb = nblk_of(S)
+    dev = v.device
+    o = dict(out or {})
+    o.setdefault("centroids", torch.empty((B, H, clusters, D), dtype=torch.float32, device=dev))
+    o.setdefault("labels", torch.empty((B, H, S), dtype=torch.int32, device=dev))
+    o.setdefault("perm", torch.empty((B, H, S), dtype=torch.int32, device=dev))
+    o.setdefault("k8", torch.empty((B, H, nb * 128, D), dtype=torch.uint8, device=dev))
+    o.setdefault("k_scale", torch.empty((B, H, nb), dtype=torch.float32, device=dev))
+    o.setdefault("r8", torch.empty((B, H, D, nb * 128), dtype=torch.uint8, device=dev))
+    o.setdefault("r_scale", torch.empty((B, H, D), dtype=torch.float32, device=dev))
+    o.setdefault("mu_bf16", torch.empty((B, H, nb, D), dtype=torch.int16, device=dev))
+    o.setdefault("mu_scaled", torch.empty((B, H, nb, D), dtype=torch.float32, device=dev))
+    wsb = vc_smooth_group_workspace_size(B, H, S, D, clusters)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    p = vc_group_params(clusters, iters, seed, 0)
+    kd, vd = _bshd(k), _bshd(v)
+    st = lib().vc_smooth_group(ctypes.byref(sh), ctypes.byref(kd), ctypes.byref(vd), ctypes.byref(p),
+                               _ptr(o["centroids"]), _ptr(o["labels"]), _ptr(o["perm"]), _ptr(o["k8"]),
+                               _ptr(o["k_scale"]), _ptr(o["r8"]), _ptr(o["r_scale"]), _ptr(o["mu_bf16"]),
+                               _ptr(o["mu_scaled"]), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _stream())
+    _check(st, "vc_smooth_group")
+    return o
+
+
+# --------------------------------------------------------------------------- #
+# vc_attn_fwd
+# --------------------------------------------------------------------------- #
+
+def vc_attn_fwd(q8, q_scale, k8, k_scale, v8, v_scale, mu_scaled=None, *, S: int, out=None, sm_scale: float = 0.0,
+                window: int = 2, sequential: bool = False):
+    """FP8 ExpCast attention.  Codes and scales as produced by vc_quantize /
+    vc_smooth_group; S is the token count.  Returns bf16 [B,S,H,D]."""
+    B, H, S_pad, D = q8.shape
+    assert S_pad == nblk_of(S) * 128
+    sh = vc_shape(B, H, S, D)
+    if out is None:
+        out = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=q8.device)
+    p = vc_attn_params(sm_scale, window, VC_ATTN_SEQUENTIAL if sequential else 0)
+    od = _bshd_out(out)
+    st = lib().vc_attn_fwd(ctypes.byref(sh), ctypes.byref(p), _ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale),
+                           _ptr(v8), _ptr(v_scale), _ptr(mu_scaled), ctypes.byref(od), _stream())
+    _check(st, "vc_attn_fwd")
+    return out
+
+
+def vc_pack_v_bf16(v, *, out=None):
+    sh = _shape_of(v)
+    nb = nblk_of(sh.S)
+    if out is None:
+        out = torch.empty((sh.B, sh.H, sh.D, nb * 128), dtype=torch.bfloat16, device=v.device)
+    vd = _bshd(v)
+    st = lib().vc_pack_v_bf16(ctypes.byref(sh), ctypes.byref(vd), _ptr(out), _stream())
+    _check(st, "vc_pack_v_bf16")
+    return out
+
+
+def vc_attn_fwd_bf16(q, k, vt, *, out=None, sm_scale: float = 0.0, window: int = 2, sequential: bool = False):
+    sh = _shape_of(q)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    p = vc_attn_params(sm_scale, window, VC_ATTN_SEQUENTIAL if sequential else 0)
+    qd, kd, od = _bshd(q), _bshd(k), _bshd_out(out)
+    st = lib().vc_attn_fwd_bf16(ctypes.byref(sh), ctypes.byref(p), ctypes.byref(qd), ctypes.byref(kd), _ptr(vt),
+                                ctypes.byref(od), _stream())
+    _check(st, "vc_attn_fwd_bf16")
+    return out
+
+
+def vc_expcast_codes(x, a, b, row_len: int, *, out=None):
+    """codes[i] = min(120, RNE_clamp0(fma(a[r], x[i], b[r]))), r = i // row_len."""
+    n = x.numel()
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device=x.device)
+    st = lib().vc_expcast_codes(_ptr(x), _ptr(a), _ptr(b), n, row_len, _ptr(out), _stream())
+    _check(st, "vc_expcast_codes")
+    return out
+
+
+def default_sm_scale(D: int) -> float:
+    return 1.0 / math.sqrt(D)

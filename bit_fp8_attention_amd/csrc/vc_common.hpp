@@ -1,0 +1,85 @@
+// vc_common.hpp -- device helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/vc_attn.h"
+
+#define VC_DEV __device__ __forceinline__
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef unsigned int u32;
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+namespace vc {
+
+constexpr int kBlk = 128;  // key/query block: the FP8 scale granularity and the tile height
+
+VC_DEV float bf16_lo(u32 w) { return __uint_as_float(w << 16); }
+VC_DEV float bf16_hi(u32 w) { return __uint_as_float(w & 0xffff0000u); }
+VC_DEV float bf16_to_f32(uint16_t h) { return __uint_as_float((u32)h << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
+VC_DEV uint16_t f32_to_bf16(float f) {
+  u32 u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Two fp32 -> two OCP E4M3 bytes (round-half-even) in the low 16 bits.
+VC_DEV u32 cvt2_fp8(float a, float b) { return (u32)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false); }
+
+// Four fp32 -> one dword of E4M3 bytes, byte i = x_i.
+VC_DEV u32 cvt4_fp8(float x0, float x1, float x2, float x3) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
+  return (u32)w;
+}
+
+// One ExpCast code into byte `sel` of `word`: round-half-even of fma(a, x, b),
+// clamped below at 0 by the integer conversion (v_cvt_pk_u8_f32).
+#define VC_EXPCAST_BYTE(word, a, x, b, sel) __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf((a), (x), (b)), (sel), (word))
+
+VC_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// FP8 16x16x128 matrix-core product with fp32 accumulate (unscaled form).
+VC_DEV v4f mfma_fp8(v8i a, v8i b, v4f c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+VC_DEV v4f mfma_bf16(v8bf a, v8bf b, v4f c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
+
+// Asynchronous 16-byte global -> LDS copy: lane i lands at lds_base + 16 i.
+VC_DEV void lds_dma16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, LDS_PTR(lds_base), 16, 0, 0);
+}
+
+// s_waitcnt with vmcnt = 0 and the other counters at their maxima.
+VC_DEV void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
+// Blocks of 8 XCDs: workgroup ids are dealt round-robin to the XCDs, so
+// remap them so that each XCD runs one contiguous range of logical tiles
+// (neighbouring query tiles of one head share K/V in that XCD's L2).
+VC_DEV int xcd_remap(int id, int n) {
+  const int X = 8;
+  int q = n / X, r = n % X;
+  int xcd = id % X, slot = id / X;
+  // XCD x owns logical ids [x*q + min(x, r), ...) of length q + (x < r)
+  int start = xcd * q + (xcd < r ? xcd : r);
+  return start + slot;
+}
+
+}  // namespace vc
+
+#define VC_CHECK_LAUNCH()                     \
+  do {                                        \
+    if (hipGetLastError() != hipSuccess) return VC_ERR_HIP; \
+  } while (0)

@@ -1,0 +1,44 @@
+// vc_launch.hpp -- internal launchers (validated arguments only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/vc_attn.h"
+
+namespace vc {
+
+struct Bshd {
+  const uint16_t* p;
+  int64_t sB, sS, sH;
+};
+
+struct BshdOut {
+  uint16_t* p;
+  int64_t sB, sS, sH;
+};
+
+// vc_quantize.hip
+hipError_t launch_qk_quant(const vc_shape& sh, Bshd x, uint8_t* codes, float* scale, hipStream_t st);
+hipError_t launch_v_quant(const vc_shape& sh, Bshd v, uint8_t* v8, float* v_scale, hipStream_t st);
+hipError_t launch_pack_v_bf16(const vc_shape& sh, Bshd v, uint16_t* vt, hipStream_t st);
+hipError_t launch_expcast_codes(const float* x, const float* a, const float* b, int64_t n, int32_t row_len,
+                                uint8_t* codes, hipStream_t st);
+
+// vc_group.hip
+size_t group_workspace_bytes(const vc_shape& sh, int clusters);
+hipError_t launch_smooth_group(const vc_shape& sh, Bshd k, Bshd v, const vc_group_params& p, float* centroids,
+                               int32_t* labels, int32_t* perm, uint8_t* k8, float* k_scale, uint8_t* r8,
+                               float* r_scale, uint16_t* mu_bf16, float* mu_scaled, void* ws, hipStream_t st);
+
+// vc_attn_fp8.hip
+hipError_t launch_attn_fp8(const vc_shape& sh, float sm_scale, int window, uint32_t flags, const uint8_t* q8,
+                           const float* q_scale, const uint8_t* k8, const float* k_scale, const uint8_t* v8,
+                           const float* v_scale, const float* mu_scaled, BshdOut o, hipStream_t st);
+
+// vc_attn_bf16.hip
+hipError_t launch_attn_bf16(const vc_shape& sh, float sm_scale, int window, uint32_t flags, Bshd q, Bshd k,
+                            const uint16_t* vt, BshdOut o, hipStream_t st);
+
+}  // namespace vc

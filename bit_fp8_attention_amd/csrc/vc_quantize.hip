@@ -1,0 +1,256 @@
+// vc_quantize.hip -- FP8 operand preparation (HBM-bound streaming kernels).
+//
+// [OVC] "Scheduling around ExpCast" / "Fused input preparation": Q and K are
+// quantised to E4M3 with one scale per 128-token block, V with one scale per
+// head, V written transposed with keys contiguous ("Packed V").  Three
+// stream-ordered passes as on the blog: Q/K per block; V per-head maximum;
+// V convert into the packed layout.  [VC] §3.1 gives X_q = s_X * Xhat.
+//
+// Each block kernel streams one 128-token x D tile: 256 threads, 16-byte
+// loads (each row is D contiguous bf16), amax through a wave then LDS
+// reduction, E4M3 conversion with the hardware round-half-even convert.
+#include "vc_common.hpp"
+#include "vc_launch.hpp"
+
+namespace vc {
+
+namespace {
+
+// amax over 8 bf16 packed in a uint4
+VC_DEV float amax8(uint4 w, float m) {
+  m = fmaxf(m, fabsf(bf16_lo(w.x)));
+  m = fmaxf(m, fabsf(bf16_hi(w.x)));
+  m = fmaxf(m, fabsf(bf16_lo(w.y)));
+  m = fmaxf(m, fabsf(bf16_hi(w.y)));
+  m = fmaxf(m, fabsf(bf16_lo(w.z)));
+  m = fmaxf(m, fabsf(bf16_hi(w.z)));
+  m = fmaxf(m, fabsf(bf16_lo(w.w)));
+  m = fmaxf(m, fabsf(bf16_hi(w.w)));
+  return m;
+}
+
+// 8 bf16 * inv -> 8 E4M3 bytes
+VC_DEV uint2 codes8(uint4 w, float inv) {
+  uint2 r;
+  r.x = cvt4_fp8(bf16_lo(w.x) * inv, bf16_hi(w.x) * inv, bf16_lo(w.y) * inv, bf16_hi(w.y) * inv);
+  r.y = cvt4_fp8(bf16_lo(w.z) * inv, bf16_hi(w.z) * inv, bf16_lo(w.w) * inv, bf16_hi(w.w) * inv);
+  return r;
+}
+
+VC_DEV float block_max256(float m, float* red) {
+  m = wave_max(m);
+  int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  return m;
+}
+
+VC_DEV void scale_pair(float amax, float& s, float& inv) {
+  if (amax > 0.0f) {
+    s = amax / 448.0f;
+    inv = 448.0f / amax;
+  } else {
+    s = 1.0f;
+    inv = 1.0f;
+  }
+}
+
+// Q or K: one workgroup per (block j, head h, batch b).
+template <int D>
+__global__ __launch_bounds__(256) void qk_block_quant(const uint16_t* __restrict__ x, int64_t sB, int64_t sS,
+                                                      int64_t sH, int S, int H, int nblk,
+                                                      uint8_t* __restrict__ codes, float* __restrict__ scale) {
+  constexpr int CPR = D / 8;             // 16-byte chunks per row
+  constexpr int NCH = kBlk * CPR / 256;  // chunks per thread
+  __shared__ float red[4];
+  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const uint16_t* xb = x + b * sB + h * sH;
+  uint4 v[NCH];
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    int c = t + 256 * i, row = c / CPR, ch = c % CPR, tok = j * kBlk + row;
+    v[i] = tok < S ? *(const uint4*)(xb + (int64_t)tok * sS + ch * 8) : make_uint4(0, 0, 0, 0);
+    m = amax8(v[i], m);
+  }
+  m = block_max256(m, red);
+  float s, inv;
+  scale_pair(m, s, inv);
+  const int64_t bh = (int64_t)b * H + h;
+  if (t == 0) scale[bh * nblk + j] = s;
+  uint8_t* cb = codes + (bh * nblk * kBlk + (int64_t)j * kBlk) * D;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    int c = t + 256 * i, row = c / CPR, ch = c % CPR;
+    *(uint2*)(cb + row * D + ch * 8) = codes8(v[i], inv);
+  }
+}
+
+// V pass 1: per-(b,h) amax as ordered uint bits, accumulated into
+// v_scale[bh*D] (zeroed beforehand).  256 tokens per workgroup.
+template <int D>
+__global__ __launch_bounds__(256) void v_amax(const uint16_t* __restrict__ x, int64_t sB, int64_t sS, int64_t sH,
+                                              int S, int H, float* __restrict__ v_scale) {
+  constexpr int CPR = D / 8;
+  constexpr int NCH = 256 * CPR / 256;
+  __shared__ float red[4];
+  const int h = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const uint16_t* xb = x + b * sB + h * sH;
+  float m = 0.0f;
+#pragma unroll 4
+  for (int i = 0; i < NCH; ++i) {
+    int c = t + 256 * i, row = c / CPR, ch = c % CPR, tok = blockIdx.x * 256 + row;
+    if (tok < S) m = amax8(*(const uint4*)(xb + (int64_t)tok * sS + ch * 8), m);
+  }
+  m = block_max256(m, red);
+  if (t == 0) atomicMax((unsigned int*)(v_scale + ((int64_t)b * H + h) * D), __float_as_uint(m));
+}
+
+__global__ void v_amax_zero(float* v_scale, int BH, int D) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < BH) v_scale[(int64_t)i * D] = 0.0f;
+}
+
+// V pass 2: convert one 128-token block and write it key-contiguous.
+template <int D>
+__global__ __launch_bounds__(256) void v_convert(const uint16_t* __restrict__ x, int64_t sB, int64_t sS, int64_t sH,
+                                                 int S, int H, int nblk, const float* __restrict__ v_scale,
+                                                 uint8_t* __restrict__ v8) {
+  constexpr int CPR = D / 8;
+  constexpr int NCH = kBlk * CPR / 256;
+  constexpr int LD = D + 4;  // LDS row pitch in bytes (spreads banks on the transposed read)
+  __shared__ uint8_t tile[kBlk * LD];
+  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const int64_t bh = (int64_t)b * H + h;
+  const uint16_t* xb = x + b * sB + h * sH;
+  float s, inv;
+  scale_pair(v_scale[bh * D], s, inv);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    int c = t + 256 * i, row = c / CPR, ch = c % CPR, tok = j * kBlk + row;
+    uint4 w = tok < S ? *(const uint4*)(xb + (int64_t)tok * sS + ch * 8) : make_uint4(0, 0, 0, 0);
+    uint2 cd = codes8(w, inv);
+    *(u32*)(tile + row * LD + ch * 8) = cd.x;
+    *(u32*)(tile + row * LD + ch * 8 + 4) = cd.y;
+  }
+  __syncthreads();
+  const int64_t S_pad = (int64_t)nblk * kBlk;
+  uint8_t* ob = v8 + bh * D * S_pad + (int64_t)j * kBlk;
+  constexpr int TASKS = D * (kBlk / 16);
+#pragma unroll
+  for (int i = 0; i < TASKS / 256; ++i) {
+    int task = t + 256 * i, d = task / (kBlk / 16), k0 = (task % (kBlk / 16)) * 16;
+    u32 w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      w[q] = (u32)tile[(k0 + 4 * q) * LD + d] | ((u32)tile[(k0 + 4 * q + 1) * LD + d] << 8) |
+             ((u32)tile[(k0 + 4 * q + 2) * LD + d] << 16) | ((u32)tile[(k0 + 4 * q + 3) * LD + d] << 24);
+    *(uint4*)(ob + d * S_pad + k0) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// V pass 3: amax bits -> scale, repeated over the D channels.
+__global__ void v_finalize(float* v_scale, int D) {
+  const int64_t bh = blockIdx.x;
+  float amax = v_scale[bh * D];
+  __syncthreads();
+  float s, inv;
+  scale_pair(amax, s, inv);
+  for (int d = threadIdx.x; d < D; d += blockDim.x) v_scale[bh * D + d] = s;
+}
+
+// bf16 V -> key-contiguous bf16 (baseline preparation).
+template <int D>
+__global__ __launch_bounds__(256) void v_pack_bf16(const uint16_t* __restrict__ x, int64_t sB, int64_t sS,
+                                                   int64_t sH, int S, int H, int nblk, uint16_t* __restrict__ vt) {
+  constexpr int CPR = D / 8;
+  constexpr int NCH = kBlk * CPR / 256;
+  constexpr int LD = D + 2;  // elements
+  __shared__ uint16_t tile[kBlk * LD];
+  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const int64_t bh = (int64_t)b * H + h;
+  const uint16_t* xb = x + b * sB + h * sH;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    int c = t + 256 * i, row = c / CPR, ch = c % CPR, tok = j * kBlk + row;
+    uint4 w = tok < S ? *(const uint4*)(xb + (int64_t)tok * sS + ch * 8) : make_uint4(0, 0, 0, 0);
+    u32* dst = (u32*)(tile + row * LD + ch * 8);
+    dst[0] = w.x;
+    dst[1] = w.y;
+    dst[2] = w.z;
+    dst[3] = w.w;
+  }
+  __syncthreads();
+  const int64_t S_pad = (int64_t)nblk * kBlk;
+  uint16_t* ob = vt + bh * D * S_pad + (int64_t)j * kBlk;
+  constexpr int TASKS = D * (kBlk / 8);
+#pragma unroll
+  for (int i = 0; i < TASKS / 256; ++i) {
+    int task = t + 256 * i, d = task / (kBlk / 8), k0 = (task % (kBlk / 8)) * 8;
+    u32 w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[q] = (u32)tile[(k0 + 2 * q) * LD + d] | ((u32)tile[(k0 + 2 * q + 1) * LD + d] << 16);
+    *(uint4*)(ob + d * S_pad + k0) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// The ExpCast code map alone (same byte routine as the attention kernel,
+// plus the explicit upper clip at 120).
+__global__ void expcast_codes_kernel(const float* __restrict__ x, const float* __restrict__ a,
+                                     const float* __restrict__ b, int64_t n, int32_t row_len,
+                                     uint8_t* __restrict__ codes) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  int64_t r = i / row_len;
+  u32 w = VC_EXPCAST_BYTE(0u, a[r], x[i], b[r], 0);
+  codes[i] = (uint8_t)min(w & 0xffu, 120u);
+}
+
+}  // namespace
+
+hipError_t launch_qk_quant(const vc_shape& sh, Bshd x, uint8_t* codes, float* scale, hipStream_t st) {
+  int nblk = (sh.S + kBlk - 1) / kBlk;
+  dim3 grid(nblk, sh.H, sh.B);
+  if (sh.D == 128)
+    qk_block_quant<128><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nblk, codes, scale);
+  else
+    qk_block_quant<64><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nblk, codes, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_v_quant(const vc_shape& sh, Bshd v, uint8_t* v8, float* v_scale, hipStream_t st) {
+  int nblk = (sh.S + kBlk - 1) / kBlk;
+  int BH = sh.B * sh.H;
+  v_amax_zero<<<(BH + 255) / 256, 256, 0, st>>>(v_scale, BH, sh.D);
+  dim3 g1((sh.S + 255) / 256, sh.H, sh.B), g2(nblk, sh.H, sh.B);
+  if (sh.D == 128) {
+    v_amax<128><<<g1, 256, 0, st>>>(v.p, v.sB, v.sS, v.sH, sh.S, sh.H, v_scale);
+    v_convert<128><<<g2, 256, 0, st>>>(v.p, v.sB, v.sS, v.sH, sh.S, sh.H, nblk, v_scale, v8);
+  } else {
+    v_amax<64><<<g1, 256, 0, st>>>(v.p, v.sB, v.sS, v.sH, sh.S, sh.H, v_scale);
+    v_convert<64><<<g2, 256, 0, st>>>(v.p, v.sB, v.sS, v.sH, sh.S, sh.H, nblk, v_scale, v8);
+  }
+  v_finalize<<<BH, 128, 0, st>>>(v_scale, sh.D);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_v_bf16(const vc_shape& sh, Bshd v, uint16_t* vt, hipStream_t st) {
+  int nblk = (sh.S + kBlk - 1) / kBlk;
+  dim3 grid(nblk, sh.H, sh.B);
+  if (sh.D == 128)
+    v_pack_bf16<128><<<grid, 256, 0, st>>>(v.p, v.sB, v.sS, v.sH, sh.S, sh.H, nblk, vt);
+  else
+    v_pack_bf16<64><<<grid, 256, 0, st>>>(v.p, v.sB, v.sS, v.sH, sh.S, sh.H, nblk, vt);
+  return hipGetLastError();
+}
+
+hipError_t launch_expcast_codes(const float* x, const float* a, const float* b, int64_t n, int32_t row_len,
+                                uint8_t* codes, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  expcast_codes_kernel<<<(unsigned)blocks, 256, 0, st>>>(x, a, b, n, row_len, codes);
+  return hipGetLastError();
+}
+
+}  // namespace vc

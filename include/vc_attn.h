@@ -1,0 +1,220 @@
+/*
+ * vc_attn.h -- C ABI of the VC-Attention hot path on AMD Instinct MI355X
+ * (gfx950): non-causal FP8 flash-attention forward with ExpCast-FP8 and
+ * V-Smooth.
+ *
+ * Sources, cited by page title and place:
+ *   [VC]  "VC-Attention: Value Smoothing and Softmax Casting for Low-bit
+ *         Attention" (arXiv 2609.15810).
+ *   [OVC] "Open-VC Attention: an open-source, error-tunable variant of
+ *         VC-Attention" (machgen.ai blog).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *    library never allocates, frees or synchronises; every call only
+ *    enqueues kernels on `stream` (a hipStream_t passed as void*; NULL is the
+ *    default stream) and returns.  Calls are graph-capturable.
+ *  - Shapes: B batches, H heads, S tokens, D head dim (D in {64, 128}).
+ *    nblk = ceil(S / 128) key/query blocks, S_pad = 128 * nblk.
+ *  - bf16 activations are described by vc_bshd: element (b, s, h, d) lives at
+ *    ptr + b*sB + s*sS + h*sH + d (strides in elements, d contiguous).  The
+ *    base and all three strides must be multiples of 8 elements (16 bytes).
+ *  - FP8 data is OCP E4M3 (E4M3FN: bias 7, max 448, no infinities), the
+ *    format gfx950's matrix cores consume.
+ *  - Validation of every argument happens before anything is enqueued; on
+ *    error nothing is written and a vc_status other than VC_OK is returned.
+ *    A failed launch returns VC_ERR_HIP (from hipGetLastError, no sync).
+ *    Device-side faults surface at the caller's next synchronisation.
+ *  - NaN or Inf inputs are not checked; they propagate.
+ *  - Entry points are thread-safe; concurrent calls must not share output
+ *    buffers or workspaces.
+ */
+#ifndef VC_ATTN_H
+#define VC_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VC_ABI_VERSION 1
+
+typedef enum vc_status {
+  VC_OK = 0,
+  VC_ERR_NULL = 1,        /* a required pointer is NULL */
+  VC_ERR_SHAPE = 2,       /* B, H, S or D out of range */
+  VC_ERR_ALIGN = 3,       /* pointer or stride not 16-byte aligned */
+  VC_ERR_UNSUPPORTED = 4, /* parameter outside the supported set */
+  VC_ERR_WORKSPACE = 5,   /* workspace too small */
+  VC_ERR_HIP = 6          /* a HIP launch failed */
+} vc_status;
+
+typedef struct vc_shape {
+  int32_t B, H, S, D;
+} vc_shape;
+
+/* bf16 tensor in [B, S, H, D] order with element strides (see above). */
+typedef struct vc_bshd {
+  const void* ptr;
+  int64_t sB, sS, sH;
+} vc_bshd;
+
+typedef struct vc_bshd_out {
+  void* ptr;
+  int64_t sB, sS, sH;
+} vc_bshd_out;
+
+/* ABI version of the loaded library (VC_ABI_VERSION it was built with). */
+int32_t vc_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* vc_status_str(int32_t status);
+
+/*
+ * vc_quantize -- FP8 operands for the attention kernel.
+ * [OVC] "Scheduling around ExpCast" and "Fused input preparation": Q and K
+ * take one E4M3 scale per 128-token block, V one scale per head; the packed
+ * V is stored transposed with the key dimension contiguous ("Packed V").
+ * [VC] §3.1: X_q = s_X * Xhat.
+ *
+ * For each (b, h) and 128-token block j of Q (and of K):
+ *   amax = max |x| over the block's valid rows; s = amax / 448 (fp32);
+ *   code = E4M3_rne(x * (448 / amax)) (fp32 product, round-half-even);
+ *   a block of zeros takes s = 1.  Rows >= S are written as code 0.
+ *   q8, k8:       uint8 [B][H][S_pad][D]
+ *   q_scale, k_scale: fp32 [B][H][nblk]
+ * For V: one amax per (b, h) over all S x D elements, same rule;
+ *   v8:      uint8 [B][H][D][S_pad]  (key-contiguous; keys >= S are 0)
+ *   v_scale: fp32 [B][H][D]          (the head's scale repeated over d)
+ * Any of q, k, v may have ptr == NULL to skip that operand (its outputs are
+ * then ignored and may be NULL).  q8/k8/v8 must be 16-byte aligned.
+ */
+int32_t vc_quantize(const vc_shape* shape, const vc_bshd* q, const vc_bshd* k, const vc_bshd* v,
+                    uint8_t* q8, float* q_scale, uint8_t* k8, float* k_scale, uint8_t* v8, float* v_scale,
+                    void* stream);
+
+/* ----------------------------------------------------------------------- */
+
+typedef struct vc_group_params {
+  int32_t clusters; /* k in [1, min(S, 8192 / D)] */
+  int32_t iters;    /* Lloyd iterations, [1, 64] */
+  uint64_t seed;    /* seeds the Forgy initialisation */
+  uint32_t flags;   /* must be 0 */
+} vc_group_params;
+
+/* Bytes of device workspace vc_smooth_group needs for this shape. */
+size_t vc_smooth_group_workspace_size(const vc_shape* shape, int32_t clusters);
+
+/*
+ * vc_smooth_group -- V-Smooth grouping, demeaning and residual quantisation.
+ * [VC] §3.2 "Value-guided permutation" (Eq. 3), "Block demeaning" (Eq. 4),
+ * "Unbalanced clusters cost little"; Appendix B (per-operand fused kernels,
+ * means stored divided by the per-channel value scale).
+ *
+ * Per (b, h):
+ *  1. k-means over the value tokens (Lloyd): centroids start at the values of
+ *     `clusters` distinct tokens drawn by a partial Fisher-Yates shuffle fed
+ *     by SplitMix64 with state seed + 0x9E3779B97F4A7C15 * (1 + b*H + h);
+ *     each assignment takes argmin_c (|c|^2 - 2 v.c) with every dot product
+ *     one fp32 fused-multiply-add chain over d = 0..D-1 (ties -> lowest c);
+ *     each update is the member mean, summed in 64-bit fixed point with 24
+ *     fraction bits (order independent); empty clusters keep their centroid.
+ *     labels = the last assignment, centroids = after the last update.
+ *  2. perm = stable argsort(labels)  (K' = K[perm], V' = V[perm]).
+ *  3. For each 128-row block j of V': mu_j = bf16(mean of its valid rows);
+ *     R = V' - 1 mu_j^T in fp32; per-channel s_R[d] = amax_d |R| / 448;
+ *     r8 = E4M3_rne(R * (448 / amax_d)); mu_scaled[j][d] = mu_j[d] * (448 /
+ *     amax_d) in fp32.  K' is quantised per 128-row block as in vc_quantize.
+ * Outputs (all device, caller-owned):
+ *   centroids fp32 [B][H][clusters][D]; labels, perm int32 [B][H][S];
+ *   k8 uint8 [B][H][S_pad][D], k_scale fp32 [B][H][nblk];
+ *   r8 uint8 [B][H][D][S_pad], r_scale fp32 [B][H][D];
+ *   mu_bf16 uint16 [B][H][nblk][D]; mu_scaled fp32 [B][H][nblk][D].
+ * workspace: >= vc_smooth_group_workspace_size(shape, clusters) bytes,
+ * 256-byte aligned; its contents on entry do not matter.
+ */
+int32_t vc_smooth_group(const vc_shape* shape, const vc_bshd* k, const vc_bshd* v, const vc_group_params* p,
+                        float* centroids, int32_t* labels, int32_t* perm, uint8_t* k8, float* k_scale,
+                        uint8_t* r8, float* r_scale, uint16_t* mu_bf16, float* mu_scaled, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* ----------------------------------------------------------------------- */
+
+#define VC_ATTN_SEQUENTIAL 1u /* visit key blocks 0..nblk-1 instead of mid-window */
+
+typedef struct vc_attn_params {
+  float sm_scale;  /* softmax scale; 0 selects 1/sqrt(D) */
+  int32_t window;  /* mid-window offset W >= 0 (default 2) */
+  uint32_t flags;  /* VC_ATTN_SEQUENTIAL or 0 */
+} vc_attn_params;
+
+/*
+ * vc_attn_fwd -- non-causal FP8 attention with ExpCast-FP8 (and V-Smooth's
+ * mean restoration when mu_scaled != NULL).
+ * [VC] §3.1 Eq. 1 (online softmax), §3.2 Eq. 6 (A <- aA + P_q R_q + r mu^T),
+ * §3.3 Eq. 7 (c = clip_[0,120](Round(8(u+8)+56+beta)), beta = -0.35);
+ * [OVC] "Scheduling around ExpCast" (true-score running max, scales folded
+ * into one FMA, 4 codes per register), "A consistent denominator",
+ * "Mid-window key traversal".
+ *
+ * For each query row i (tile qt = i / 128) and key block t in the order
+ *   start = min(qt + window, nblk - 1): start, start-1, ..., 0, start+1, ...,
+ * acc = FP8 dot products (matrix cores, fp32 accumulate);
+ * g = fl(fl(sm_scale * log2 e) * q_scale[qt]) * k_scale[t];
+ * M' = max(M, g * max acc); when M' > M the numerator and denominator are
+ * rescaled by 2^(M - M');
+ * code = Round(fma(8g, acc, 119.65 - 8M')) clipped below at 0 (an integer
+ * conversion, no exponential, no FP8 cast); keys >= S get code 0;
+ * A += P_code . V8 (matrix cores); r = sum of the decoded codes (the same
+ * bytes, through the matrix cores against a tile of ones); l += r;
+ * with V-Smooth A += r * mu_scaled[t].
+ * Output: O = bf16((A / l) * v_scale[d]) written to `o` ([B,S,H,D] strided),
+ * rows in the original query order.
+ * Inputs are those of vc_quantize (plain path: q8 .. v_scale from it) or, for
+ * V-Smooth, q8/q_scale from vc_quantize and k8/k_scale, v8 = r8,
+ * v_scale = r_scale, mu_scaled from vc_smooth_group.
+ * Requires |scores| well below 2^17 in log2 units so the code never exceeds
+ * 120 (the upper clip is then implicit).
+ */
+int32_t vc_attn_fwd(const vc_shape* shape, const vc_attn_params* p, const uint8_t* q8, const float* q_scale,
+                    const uint8_t* k8, const float* k_scale, const uint8_t* v8, const float* v_scale,
+                    const float* mu_scaled, const vc_bshd_out* o, void* stream);
+
+/* ----------------------------------------------------------------------- */
+
+/*
+ * vc_pack_v_bf16 -- key-contiguous copy of V for the BF16 baseline:
+ * vt uint16 (bf16 bits) [B][H][D][S_pad], keys >= S zero.  The FP8 path gets
+ * the same layout from vc_quantize; both preparations run outside the timed
+ * attention call, as on the pages ([VC] Appendix A).
+ */
+int32_t vc_pack_v_bf16(const vc_shape* shape, const vc_bshd* v, uint16_t* vt, void* stream);
+
+/*
+ * vc_attn_fwd_bf16 -- in-house BF16 flash-attention baseline on the same
+ * kernel skeleton as vc_attn_fwd (same tiling, traversal and epilogue):
+ * BF16 matrix-core products, fp32 exp2 online softmax ([VC] §3.1 Eq. 1),
+ * row sum of the bf16-rounded probabilities.  q, k bf16 [B,S,H,D] strided;
+ * vt from vc_pack_v_bf16; o bf16 [B,S,H,D] strided.
+ */
+int32_t vc_attn_fwd_bf16(const vc_shape* shape, const vc_attn_params* p, const vc_bshd* q, const vc_bshd* k,
+                         const uint16_t* vt, const vc_bshd_out* o, void* stream);
+
+/*
+ * vc_expcast_codes -- the ExpCast code map alone, for bit-exact checks
+ * ([VC] §3.3 Eq. 7): codes[i] = min(120, Round_even_clamped0(fma(a[r], x[i],
+ * b[r]))) with r = i / row_len, evaluated by the same device routine the
+ * attention kernel uses, plus the explicit upper clip.
+ * x: fp32 [n]; a, b: fp32 [n / row_len]; codes: uint8 [n].  n % row_len == 0.
+ */
+int32_t vc_expcast_codes(const float* x, const float* a, const float* b, int64_t n, int32_t row_len,
+                         uint8_t* codes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VC_ATTN_H */

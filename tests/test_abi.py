@@ -1,0 +1,146 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point the
+header declares, and rejects invalid arguments before touching the GPU (no
+compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vc_attn.h")
+LIB = os.path.join(ROOT, "bit_fp8_attention_amd", "libvcattn.so")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int32_t|size_t|const char\*)\s+(vc_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def vc():
+    if not os.path.exists(LIB):
+        pytest.fail("libvcattn.so not built (run __graft_entry__.build())")
+    import bit_fp8_attention_amd as m
+    return m
+
+
+def test_header_declares_the_calls():
+    names = _declared()
+    for n in ["vc_abi_version", "vc_status_str", "vc_quantize", "vc_smooth_group_workspace_size",
+              "vc_smooth_group", "vc_attn_fwd", "vc_pack_v_bf16", "vc_attn_fwd_bf16", "vc_expcast_codes"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(vc):
+    L = vc.lib()
+    for n in _declared():
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_status_strings(vc):
+    assert vc.vc_abi_version() == vc.ABI_VERSION == 1
+    assert vc.vc_status_str(0) == "VC_OK"
+    for s in range(1, 7):
+        assert vc.vc_status_str(s).startswith("VC_ERR_")
+    assert vc.vc_status_str(99) == "unknown vc_status"
+
+
+def _shape(B=1, H=2, S=256, D=128):
+    return vc_mod().vc_shape(B, H, S, D)
+
+
+def vc_mod():
+    import bit_fp8_attention_amd as m
+    return m
+
+
+FAKE = 1 << 20  # an aligned non-null address; never dereferenced (validation fails first)
+
+
+def test_quantize_validation(vc):
+    L, m = vc.lib(), vc
+    ok = m.vc_bshd(FAKE, 256 * 2 * 128, 2 * 128, 128)
+    none = m.vc_bshd(None, 0, 0, 0)
+    st = ctypes.c_void_p(0)
+    P = ctypes.c_void_p
+    assert L.vc_quantize(None, None, None, None, None, None, None, None, None, None, st) == 1
+    bad_d = m.vc_shape(1, 2, 256, 96)
+    assert L.vc_quantize(ctypes.byref(bad_d), ctypes.byref(ok), ctypes.byref(none), ctypes.byref(none),
+                         P(FAKE), P(FAKE), None, None, None, None, st) == 2
+    bad_s = m.vc_shape(1, 2, 0, 128)
+    assert L.vc_quantize(ctypes.byref(bad_s), ctypes.byref(ok), ctypes.byref(none), ctypes.byref(none),
+                         P(FAKE), P(FAKE), None, None, None, None, st) == 2
+    sh = _shape()
+    # q given without its outputs
+    assert L.vc_quantize(ctypes.byref(sh), ctypes.byref(ok), ctypes.byref(none), ctypes.byref(none),
+                         None, None, None, None, None, None, st) == 1
+    # misaligned input pointer and stride
+    mis = m.vc_bshd(FAKE + 2, 256 * 2 * 128, 2 * 128, 128)
+    assert L.vc_quantize(ctypes.byref(sh), ctypes.byref(mis), ctypes.byref(none), ctypes.byref(none),
+                         P(FAKE), P(FAKE), None, None, None, None, st) == 3
+    mis2 = m.vc_bshd(FAKE, 256 * 2 * 128, 2 * 128 + 4, 128)
+    assert L.vc_quantize(ctypes.byref(sh), ctypes.byref(mis2), ctypes.byref(none), ctypes.byref(none),
+                         P(FAKE), P(FAKE), None, None, None, None, st) == 3
+    # misaligned output codes
+    assert L.vc_quantize(ctypes.byref(sh), ctypes.byref(ok), ctypes.byref(none), ctypes.byref(none),
+                         P(FAKE + 8), P(FAKE), None, None, None, None, st) == 3
+
+
+def test_smooth_group_validation(vc):
+    L, m = vc.lib(), vc
+    P = ctypes.c_void_p
+    sh = _shape()
+    ok = m.vc_bshd(FAKE, 256 * 2 * 128, 2 * 128, 128)
+    st = ctypes.c_void_p(0)
+    ws = m.vc_smooth_group_workspace_size(1, 2, 256, 128, 64)
+    assert ws > 0
+    assert m.vc_smooth_group_workspace_size(1, 2, 256, 96, 64) == 0
+
+    def call(p, wsb=ws, ws_ptr=FAKE):
+        return L.vc_smooth_group(ctypes.byref(sh), ctypes.byref(ok), ctypes.byref(ok), ctypes.byref(p),
+                                 *[P(FAKE)] * 9, P(ws_ptr), wsb, st)
+    assert call(m.vc_group_params(0, 4, 0, 0)) == 4       # k < 1
+    assert call(m.vc_group_params(65, 4, 0, 0)) == 4      # k > 8192 / D
+    assert call(m.vc_group_params(64, 0, 0, 0)) == 4      # iters < 1
+    assert call(m.vc_group_params(64, 4, 0, 1)) == 4      # unknown flag
+    assert call(m.vc_group_params(64, 4, 0, 0), wsb=ws - 1) == 5
+    assert call(m.vc_group_params(64, 4, 0, 0), ws_ptr=FAKE + 16) == 3
+    small = m.vc_shape(1, 1, 10, 128)
+    assert L.vc_smooth_group(ctypes.byref(small), ctypes.byref(ok), ctypes.byref(ok),
+                             ctypes.byref(m.vc_group_params(11, 1, 0, 0)), *[P(FAKE)] * 9, P(FAKE), ws, st) == 4
+
+
+def test_attn_validation(vc):
+    L, m = vc.lib(), vc
+    P = ctypes.c_void_p
+    sh = _shape()
+    st = ctypes.c_void_p(0)
+    o = m.vc_bshd_out(FAKE, 256 * 2 * 128, 2 * 128, 128)
+    good = m.vc_attn_params(0.0, 2, 0)
+    args = [P(FAKE)] * 6
+    assert L.vc_attn_fwd(ctypes.byref(sh), None, *args, None, ctypes.byref(o), st) == 1
+    assert L.vc_attn_fwd(ctypes.byref(sh), ctypes.byref(good), P(FAKE), None, *[P(FAKE)] * 4, None,
+                         ctypes.byref(o), st) == 1
+    assert L.vc_attn_fwd(ctypes.byref(sh), ctypes.byref(m.vc_attn_params(0.0, -1, 0)), *args, None,
+                         ctypes.byref(o), st) == 4
+    assert L.vc_attn_fwd(ctypes.byref(sh), ctypes.byref(m.vc_attn_params(-1.0, 2, 0)), *args, None,
+                         ctypes.byref(o), st) == 4
+    assert L.vc_attn_fwd(ctypes.byref(sh), ctypes.byref(m.vc_attn_params(0.0, 2, 8)), *args, None,
+                         ctypes.byref(o), st) == 4
+    assert L.vc_attn_fwd(ctypes.byref(sh), ctypes.byref(good), P(FAKE + 4), *[P(FAKE)] * 5, None,
+                         ctypes.byref(o), st) == 3
+    assert L.vc_attn_fwd(ctypes.byref(sh), ctypes.byref(good), *args, None, None, st) == 1
+    assert L.vc_attn_fwd(ctypes.byref(m.vc_shape(1, 2, 256, 32)), ctypes.byref(good), *args, None,
+                         ctypes.byref(o), st) == 2
+
+
+def test_expcast_validation(vc):
+    L = vc.lib()
+    P = ctypes.c_void_p
+    st = ctypes.c_void_p(0)
+    assert L.vc_expcast_codes(P(FAKE), P(FAKE), P(FAKE), 10, 3, P(FAKE), st) == 2  # n % row_len
+    assert L.vc_expcast_codes(P(FAKE), P(FAKE), P(FAKE), -1, 1, P(FAKE), st) == 2
+    assert L.vc_expcast_codes(None, P(FAKE), P(FAKE), 4, 1, P(FAKE), st) == 1
+    assert L.vc_expcast_codes(P(FAKE + 2), P(FAKE), P(FAKE), 4, 1, P(FAKE), st) == 3

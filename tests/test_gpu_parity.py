@@ -1,0 +1,288 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bit-exact: ExpCast codes on identical fp32 inputs, vc_quantize codes and
+scales, k-means labels / centroids / permutation, block means, scaled means,
+residual codes and K' codes.  Attention output: relative L2 <= 1e-2 against
+the quantised-pipeline emulation (differences come only from the matrix
+cores' fp32 accumulation order flipping a code at a rounding boundary, and
+from exp2f versus exact alpha), and within the Eq. 15 envelope of the fp64
+softmax.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import vcsynth
+from oracle import exact
+
+pytestmark = pytest.mark.gpu
+
+REL_L2_TOL = 1e-2  # the stated tolerance for the attention output vs the emulation
+
+
+@pytest.fixture(scope="module")
+def vc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_fp8_attention_amd as m
+    m.lib()
+    return m
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _bf16_f32(t):
+    return t.detach().float().cpu().numpy()
+
+
+def _rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
+
+
+def test_abi_version(vc):
+    assert vc.vc_abi_version() == vc.ABI_VERSION
+
+
+# --------------------------------------------------------------------------- #
+# ExpCast code map
+# --------------------------------------------------------------------------- #
+
+def test_expcast_exhaustive_grid(vc):
+    u = (np.arange(-16 * 1024, 1) / 1024.0).astype(np.float32)  # all u in [-16, 0] step 1/1024
+    a = np.array([8.0], np.float32)
+    b = np.array([119.65], np.float32)
+    got = _np(vc.vc_expcast_codes(torch.from_numpy(u).cuda(), torch.from_numpy(a).cuda(),
+                                  torch.from_numpy(b).cuda(), u.size))
+    want = oracle.expcast_codes(u, a, b, u.size)
+    closed = np.array([oracle.expcast_code_u(float(x)) for x in u], np.uint8)
+    assert (got == want).all()
+    assert (got == closed).all()
+
+
+def test_expcast_random_rows(vc):
+    rng = np.random.default_rng(0)
+    R, L = 257, 128
+    x = (rng.standard_normal(R * L) * 30).astype(np.float32)
+    a = rng.uniform(0.05, 20, R).astype(np.float32)
+    b = rng.uniform(-60, 160, R).astype(np.float32)
+    got = _np(vc.vc_expcast_codes(torch.from_numpy(x).cuda(), torch.from_numpy(a).cuda(),
+                                  torch.from_numpy(b).cuda(), L))
+    assert (got == oracle.expcast_codes(x, a, b, L)).all()
+
+
+# --------------------------------------------------------------------------- #
+# quantizers
+# --------------------------------------------------------------------------- #
+
+@pytest.mark.parametrize("B,S,H,D,kind", [(1, 1024, 2, 64, "tiny"), (1, 1000, 3, 128, "t3"), (2, 300, 1, 64, "n"),
+                                          (1, 129, 2, 128, "n"), (1, 1, 1, 128, "n"), (1, 2048, 4, 128, "plain")])
+def test_quantize_bitexact(vc, B, S, H, D, kind):
+    print(f"case quantize B={B} S={S} H={H} D={D} {kind}", flush=True)
+    if kind == "tiny":
+        q, k, v = vcsynth.make_qkv("tiny")
+    elif kind == "plain":
+        q, k, v = vcsynth.make_qkv("plain", S=S, H=H)
+    else:
+        q, k, v = vcsynth.random_qkv(B, S, H, D, seed=S + H, v_kind="t3" if kind == "t3" else "normal")
+    out = vc.vc_quantize(q.cuda(), k.cuda(), v.cuda())
+    torch.cuda.synchronize()
+    qb, kb, vb = (vcsynth.bf16_bits(x) for x in (q, k, v))
+    for name, xb in (("q", qb), ("k", kb)):
+        codes, sc = oracle.quantize_qk(xb)
+        assert (_np(out[name + "8"]) == codes).all(), name
+        assert (_np(out[name + "_scale"]) == sc).all(), name
+    codes, sc = oracle.quantize_v(vb)
+    assert (_np(out["v8"]) == codes).all()
+    assert (_np(out["v_scale"]) == sc).all()
+
+
+def test_quantize_strided_views(vc):
+    # Q, K, V as views of one fused [B, S, 3, H, D] tensor
+    B, S, H, D = 1, 700, 3, 128
+    g = torch.Generator().manual_seed(5)
+    fused = torch.randn((B, S, 3, H, D), generator=g).to(torch.bfloat16)
+    fd = fused.cuda()
+    q, k, v = fd[:, :, 0], fd[:, :, 1], fd[:, :, 2]
+    out = vc.vc_quantize(q, k, v)
+    torch.cuda.synchronize()
+    for name, x in (("q", fused[:, :, 0]), ("k", fused[:, :, 1])):
+        codes, sc = oracle.quantize_qk(vcsynth.bf16_bits(x))
+        assert (_np(out[name + "8"]) == codes).all()
+        assert (_np(out[name + "_scale"]) == sc).all()
+    codes, sc = oracle.quantize_v(vcsynth.bf16_bits(fused[:, :, 2]))
+    assert (_np(out["v8"]) == codes).all() and (_np(out["v_scale"]) == sc).all()
+
+
+# --------------------------------------------------------------------------- #
+# attention, plain path
+# --------------------------------------------------------------------------- #
+
+def _plain_case(vc, q, k, v, sm_scale, window=2, sequential=False, rows_per_head=None, seed=0):
+    B, S, H, D = q.shape
+    qz = vc.vc_quantize(q.cuda(), k.cuda(), v.cuda())
+    o = vc.vc_attn_fwd(qz["q8"], qz["q_scale"], qz["k8"], qz["k_scale"], qz["v8"], qz["v_scale"], None, S=S,
+                       sm_scale=sm_scale, window=window, sequential=sequential)
+    torch.cuda.synchronize()
+    og = _bf16_f32(o)
+    qb, kb, vb = (vcsynth.bf16_bits(x) for x in (q, k, v))
+    rng = np.random.default_rng(seed)
+    errs = []
+    for b in range(B):
+        for h in range(H):
+            rows = np.arange(S) if rows_per_head is None else np.sort(rng.choice(S, rows_per_head, replace=False))
+            res = oracle.pipeline_head(qb, kb, vb, b, h, vsmooth=False, sm_scale=sm_scale, rows=rows, window=window,
+                                       flags=oracle.SEQUENTIAL if sequential else 0)
+            emu = oracle.bf16_bits_to_f32(res["out_bf16"])
+            errs.append(_rel_l2(og[b, rows, h], emu))
+    return max(errs), og
+
+
+@pytest.mark.parametrize("B,S,H,D,sm,window,seq", [
+    (1, 1024, 2, 64, 1 / 8, 2, False),
+    (1, 1000, 2, 128, 1 / math.sqrt(128), 2, False),
+    (1, 1000, 2, 128, 4 / math.sqrt(128), 0, False),
+    (2, 300, 1, 64, 0.3, 2, True),
+    (1, 129, 1, 128, 1 / math.sqrt(128), 5, False),
+    (1, 64, 2, 128, 1 / math.sqrt(128), 2, False),
+])
+def test_attn_plain_parity(vc, B, S, H, D, sm, window, seq):
+    print(f"case attn plain B={B} S={S} H={H} D={D} sm={sm:.4f} W={window} seq={seq}", flush=True)
+    q, k, v = vcsynth.random_qkv(B, S, H, D, seed=7 * S + D, v_kind="t3")
+    err, _ = _plain_case(vc, q, k, v, sm, window, seq)
+    assert err <= REL_L2_TOL, err
+
+
+def test_attn_plain_config_sampled_rows(vc):
+    # the plain workload's recipe (K bias, Student-t V) at S = 16384 on 2 heads
+    print("case attn plain-config S=16384 H=2 sampled", flush=True)
+    q, k, v = vcsynth.make_qkv("plain", H=2)
+    err, _ = _plain_case(vc, q, k, v, 1 / math.sqrt(128), rows_per_head=96, seed=3)
+    assert err <= REL_L2_TOL, err
+
+
+# --------------------------------------------------------------------------- #
+# V-Smooth grouping
+# --------------------------------------------------------------------------- #
+
+def _group_case(vc, k, v, clusters, iters, seed):
+    B, S, H, D = v.shape
+    g = vc.vc_smooth_group(k.cuda(), v.cuda(), clusters, iters, seed)
+    torch.cuda.synchronize()
+    kb, vb = vcsynth.bf16_bits(k), vcsynth.bf16_bits(v)
+    ref = oracle.smooth_group(kb, vb, clusters, iters, seed)
+    for (b, h), r in ref.items():
+        assert (_np(g["labels"][b, h]) == r["labels"]).all(), ("labels", b, h)
+        assert (_np(g["centroids"][b, h]) == r["centroids"]).all(), ("centroids", b, h)
+        assert (_np(g["perm"][b, h]) == r["perm"]).all(), ("perm", b, h)
+        assert (_np(g["k8"][b, h]) == r["k_codes"]).all(), ("k8", b, h)
+        assert (_np(g["k_scale"][b, h]) == r["k_scale"]).all(), ("k_scale", b, h)
+        assert (_np(g["mu_bf16"][b, h]).view(np.uint16) == r["mu_bf16"]).all(), ("mu", b, h)
+        assert (_np(g["mu_scaled"][b, h]) == r["mu_scaled"]).all(), ("mu_scaled", b, h)
+        assert (_np(g["r_scale"][b, h]) == r["r_scale"]).all(), ("r_scale", b, h)
+        assert (_np(g["r8"][b, h]) == r["r_codes"]).all(), ("r8", b, h)
+    return g, ref
+
+
+def test_smooth_group_tiny_bitexact(vc):
+    print("case group tiny k=8 iters=3", flush=True)
+    q, k, v = vcsynth.make_qkv("tiny")
+    _group_case(vc, k, v, 8, 3, 1000)
+
+
+@pytest.mark.parametrize("S,H,D,kc,iters", [(1000, 2, 128, 64, 4), (300, 1, 64, 128, 2), (5, 1, 128, 5, 3)])
+def test_smooth_group_edge_bitexact(vc, S, H, D, kc, iters):
+    print(f"case group S={S} H={H} D={D} k={kc} iters={iters}", flush=True)
+    q, k, v = vcsynth.random_qkv(1, S, H, D, seed=S, v_kind="t3")
+    _group_case(vc, k, v, kc, iters, 77)
+
+
+def test_smooth_group_video_bitexact(vc):
+    print("case group longcat-recipe H=1 S=32760 k=64 iters=4", flush=True)
+    q, k, v = vcsynth.make_qkv("longcat", H=1)
+    _group_case(vc, k, v, 64, 4, 1002)
+
+
+# --------------------------------------------------------------------------- #
+# attention, V-Smooth path
+# --------------------------------------------------------------------------- #
+
+def _vsmooth_case(vc, q, k, v, clusters, iters, seed, sm, rows_per_head=None, window=2):
+    B, S, H, D = q.shape
+    qz = vc.vc_quantize(q.cuda())
+    g = vc.vc_smooth_group(k.cuda(), v.cuda(), clusters, iters, seed)
+    o = vc.vc_attn_fwd(qz["q8"], qz["q_scale"], g["k8"], g["k_scale"], g["r8"], g["r_scale"], g["mu_scaled"], S=S,
+                       sm_scale=sm, window=window)
+    torch.cuda.synchronize()
+    og = _bf16_f32(o)
+    qb, kb, vb = (vcsynth.bf16_bits(x) for x in (q, k, v))
+    rng = np.random.default_rng(1)
+    errs, res_all = [], {}
+    for b in range(B):
+        for h in range(H):
+            rows = np.arange(S) if rows_per_head is None else np.sort(rng.choice(S, rows_per_head, replace=False))
+            res = oracle.pipeline_head(qb, kb, vb, b, h, vsmooth=True, nclust=clusters, iters=iters, seed=seed,
+                                       sm_scale=sm, rows=rows, window=window)
+            emu = oracle.bf16_bits_to_f32(res["out_bf16"])
+            errs.append(_rel_l2(og[b, rows, h], emu))
+            res_all[(b, h)] = res
+    return max(errs), og, res_all
+
+
+def test_attn_vsmooth_tiny_parity(vc):
+    print("case attn vsmooth tiny", flush=True)
+    q, k, v = vcsynth.make_qkv("tiny")
+    err, _, _ = _vsmooth_case(vc, q, k, v, 8, 3, 1000, 1 / 8)
+    assert err <= REL_L2_TOL, err
+
+
+def test_attn_vsmooth_ragged_parity(vc):
+    print("case attn vsmooth ragged S=1000 D=128", flush=True)
+    q, k, v = vcsynth.random_qkv(1, 1000, 2, 128, seed=11, v_kind="t3")
+    err, _, _ = _vsmooth_case(vc, q, k, v, 16, 3, 5, 2 / math.sqrt(128))
+    assert err <= REL_L2_TOL, err
+
+
+def test_attn_vsmooth_video_envelope(vc):
+    # longcat-recipe head, sampled rows: parity with the emulation and the
+    # Eq. 15 envelope against the fp64 softmax of the original values
+    print("case attn vsmooth longcat-recipe H=1 sampled + envelope", flush=True)
+    q, k, v = vcsynth.make_qkv("longcat", H=1)
+    S, D = q.shape[1], q.shape[3]
+    sm = 1 / math.sqrt(D)
+    err, og, res_all = _vsmooth_case(vc, q, k, v, 64, 4, 1002, sm, rows_per_head=48)
+    assert err <= REL_L2_TOL, err
+    res = res_all[(0, 0)]
+    rows = res["rows"]
+    qf = exact.to_f64(vcsynth.bf16_bits(q)[0, :, 0])
+    kf = exact.to_f64(vcsynth.bf16_bits(k)[0, :, 0])
+    vf = exact.to_f64(vcsynth.bf16_bits(v)[0, :, 0])
+    ref = exact.attention_rows(qf, kf, vf, sm, rows)
+    # dequantised operands: scores and values the FP8 path actually sees
+    blk = np.arange(S) // 128
+    qd = oracle.e4m3_decode(res["q_codes"][:S]) * res["q_scale"][blk][:, None]
+    perm = res["perm"]
+    kd_p = oracle.e4m3_decode(res["k_codes"][:S]) * res["k_scale"][blk][:, None]
+    vd_p = (oracle.e4m3_decode(res["r_codes"][:, :S]).T + res["mu_scaled"][blk]) * res["r_scale"][None, :]
+    inv = np.argsort(perm)
+    kd, vd = kd_p[inv], vd_p[inv]
+    vmax = np.linalg.norm(vf, axis=1).max()
+    diam_ub = 2 * np.linalg.norm(vd - vd.mean(0), axis=1).max()  # >= diam2 of the dequantised rows
+    dv = np.linalg.norm(vd - vf, axis=1).max()
+    for ri, i in enumerate(rows):
+        s_exact = (qf[i] @ kf.T) * sm
+        s_deq = (qd[i] @ kd.T) * sm
+        p_exact = np.exp(s_exact - s_exact.max())
+        p_exact /= p_exact.sum()
+        p_qk = np.exp(s_deq - s_deq.max())
+        p_qk /= p_qk.sum()
+        tv_qk = 0.5 * np.abs(p_exact - p_qk).sum()
+        _, tau = exact.row_tv_check(s_deq * exact.LOG2E)
+        bound = (0.0364 + tau + tv_qk + 1e-4) * diam_ub + dv + 1e-2 * vmax
+        assert np.linalg.norm(og[0, i, 0] - ref[ri]) <= bound, (i, bound)

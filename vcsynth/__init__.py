@@ -86,22 +86,21 @@ def _student_t3(shape, g, device):
 
 
 def _blur_axis(x: torch.Tensor, axis: int, sigma: float) -> torch.Tensor:
-    """Separable Gaussian blur along one spatial axis of x [F, T, Hl, Wl],
-    reflect padding."""
+    """Separable Gaussian blur along one spatial axis of x [F, T, Hl, Wl]
+    (reflect padding), written as a weighted sum of shifted slices."""
     r = int(math.ceil(3 * sigma))
-    t = torch.arange(-r, r + 1, dtype=torch.float32, device=x.device)
+    t = torch.arange(-r, r + 1, dtype=torch.float64)
     w = torch.exp(-0.5 * (t / sigma) ** 2)
-    w = (w / w.sum()).view(1, 1, -1)
-    xm = x.movedim(axis, -1)
-    shp = xm.shape
-    flat = xm.reshape(-1, 1, shp[-1])
-    pad = min(r, shp[-1] - 1)
-    if pad < r:  # axis shorter than the kernel radius: replicate instead
-        flat = torch.nn.functional.pad(flat, (r, r), mode="replicate")
-    else:
-        flat = torch.nn.functional.pad(flat, (r, r), mode="reflect")
-    out = torch.nn.functional.conv1d(flat, w)
-    return out.reshape(shp).movedim(-1, axis)
+    w = (w / w.sum()).tolist()
+    n = x.shape[axis]
+    idx = torch.arange(-r, n + r)
+    idx = idx.abs()  # reflect at 0
+    idx = torch.where(idx > n - 1, 2 * (n - 1) - idx, idx).clamp(0, n - 1)  # reflect at n-1
+    xp = x.index_select(axis, idx.to(x.device))
+    out = torch.zeros_like(x)
+    for i, wi in enumerate(w):
+        out += wi * xp.narrow(axis, i, n)
+    return out
 
 
 def _grf(F: int, grid, g, device, sigma=2.0, chunk=512):
