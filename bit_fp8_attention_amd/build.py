@@ -22,9 +22,17 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=o
          "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
 
 
+# The attention kernels never see NaN inputs by contract; without IEEE-mode
+# NaN quieting the running max compiles to v_max3_f32 chains.
+EXTRA = {
+    "vc_attn_fp8.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+    "vc_attn_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -23,27 +23,26 @@
 //    4 waves x 32 queries (two 16-query sub-tiles per wave), two workgroups
 //    per CU so that one wave's matrix-core chain overlaps another's VALU work;
 //  - S^T = K Q^T on v_mfma_f32_16x16x128_f8f6f4 (K = D = 128): the output
-//    puts one query and 4 keys in each lane, and the K rows of each MFMA are
-//    taken in the order that leaves lane group g holding keys 32g..32g+31 of
-//    the tile, which is exactly the A-operand layout of the P.V product, so
-//    codes go from the accumulator to the PV operand without any shuffle and
-//    V is read key-contiguous;
-//  - K and V tiles (16 KB each) stream HBM -> LDS with global_load_lds_dwordx4
-//    (no VGPR staging), double-buffered, in an XOR-swizzled layout that makes
-//    the 32-byte fragment reads bank-conflict free;
+//    puts one query and 4 keys in each lane; the packed V tile stores its keys
+//    in exactly the order in which those accumulators hand them to the P.V
+//    product's A operand, so codes go from the accumulator to the PV operand
+//    without any shuffle;
+//  - K and V are stored tile-major and pre-swizzled (the packed layouts of
+//    vc_attn.h), so each 16 KB tile streams HBM -> LDS as one straight copy
+//    with global_load_lds_dwordx4 (no VGPR staging, no per-tile address
+//    arithmetic), double-buffered, and the 32-byte fragment reads from LDS
+//    are bank-conflict free;
 //  - workgroup ids are remapped so each XCD works on a contiguous range of
 //    query tiles of one head, whose mid-window sweeps hit the same K/V in that
 //    XCD's L2.
 #include "vc_common.hpp"
 #include "vc_launch.hpp"
 
+#include <type_traits>
+
 namespace vc {
 
 namespace {
-
-// LDS swizzles (16-byte chunk index XOR), see the bank analysis in the design doc.
-VC_DEV int kswz(int r) { return ((r & 3) ^ ((r >> 6) & 1)) | (((r >> 5) & 1) << 2); }
-VC_DEV int vswz(int d) { return ((d >> 1) & 7) ^ ((d & 1) << 2); }
 
 template <int D>
 struct TileLds {
@@ -53,54 +52,58 @@ struct TileLds {
   static constexpr int BYTES = KB + VB;
 };
 
+// Issue the asynchronous copies of key tile `t` (two contiguous 16 KB
+// blocks in the packed layouts) into LDS buffer `buf`: wave w, copy r moves
+// bytes [(4r + w) KB, +1 KB), lane l its 16 bytes at + 16 l.
 template <int D>
-VC_DEV int kchunk(int row, int c) {
-  return D == 128 ? (c ^ kswz(row)) : (c ^ (kswz(row) & 3));
-}
-
-// Issue the asynchronous copies of key tile `t` into LDS buffer `buf`.
-template <int D>
-VC_DEV void issue_tile(uint8_t* buf, const uint8_t* __restrict__ kb, const uint8_t* __restrict__ vb, int64_t S_pad,
-                       int t, int w, int l) {
-  constexpr int NI = D * kBlk / 1024 / 4;  // 16-byte-per-lane wave instructions per wave per operand
+VC_DEV void issue_tile(uint8_t* buf, const uint8_t* __restrict__ kb, const uint8_t* __restrict__ vb, int t, int w,
+                       unsigned loff) {
+  constexpr int NI = D * kBlk / 1024 / 4;  // copies per wave per operand
   const uint8_t* kt = kb + (int64_t)t * kBlk * D;
-#pragma unroll
-  for (int r = 0; r < NI; ++r) {
-    int base = (r * 4 + w) * 1024;
-    int p = base + l * 16;
-    int row = p / D, pch = (p % D) / 16;
-    lds_dma16(kt + row * D + kchunk<D>(row, pch) * 16, buf + base);
-  }
-  const uint8_t* vt = vb + (int64_t)t * kBlk;
+  const uint8_t* vt = vb + (int64_t)t * kBlk * D;
   uint8_t* vbuf = buf + TileLds<D>::KB;
 #pragma unroll
   for (int r = 0; r < NI; ++r) {
-    int base = (r * 4 + w) * 1024;
-    int p = base + l * 16;
-    int d = p / kBlk, pch = (p % kBlk) / 16;
-    lds_dma16(vt + (int64_t)d * S_pad + ((pch ^ vswz(d)) * 16), vbuf + base);
+    const int base = (r * 4 + w) * 1024;
+    lds_dma16(kt + base + loff, buf + base);
+    lds_dma16(vt + base + loff, vbuf + base);
   }
 }
 
-// K fragment (A operand) of MFMA block t8: lane row i = lr holds key
-// 32*(i/4) + 4*t8 + i%4, bytes [32g, 32g+32) of its D.
+// Fragment reads.  For MFMA block t8 the A-operand lane row i = lr holds
+// key 16*t8 + lr: the 16 lanes of a group read 16 consecutive K rows, lane
+// group g taking logical chunks g and g + 4 (for D = 64: chunk g and zeros),
+// which also fixes which channels group g's 32 bytes carry -- Q is loaded
+// with the same mapping.  The row swizzle depends on the row's bits 0-3,
+// i.e. on lr alone, so every K read is a lane base + 16*t8*D.  For channel
+// block m lane column lr holds channel 16m + lr, lane group g chunks g and
+// g + 4 of its key row: every V read is a lane base + m*16*128.  The S^T
+// accumulator of block t8 holds, in lane group g and register v, key
+// 16*t8 + 4g + v -- the key the packed V tile stores at byte 4*t8 + v of
+// group g's 32 bytes, so the codes feed P.V unshuffled.
 template <int D>
-VC_DEV v8i kfrag(const uint8_t* kt, int t8, int lr, int g) {
-  int row = 32 * (lr >> 2) + 4 * t8 + (lr & 3);
-  if (D == 64 && g >= 2) return v8i{0, 0, 0, 0, 0, 0, 0, 0};
-  const uint8_t* rp = kt + row * D;
-  uint4 lo = *(const uint4*)(rp + kchunk<D>(row, 2 * g) * 16);
-  uint4 hi = *(const uint4*)(rp + kchunk<D>(row, 2 * g + 1) * 16);
+struct FragBase {
+  unsigned k0, k1;  // byte offsets of the two 16-byte K chunks (t8 = 0)
+  unsigned v0, v1;  // byte offsets of the two 16-byte V chunks (m = 0)
+  VC_DEV FragBase(int lr, int g) {
+    k0 = kpack_off<D>(lr, g);
+    k1 = D == 128 ? kpack_off<D>(lr, g + 4) : 0;
+    v0 = vpack_off(lr, g);
+    v1 = vpack_off(lr, g + 4);
+  }
+};
+
+template <int D>
+VC_DEV v8i kfrag(const uint8_t* kt, int t8, const FragBase<D>& fb) {
+  uint4 lo = *(const uint4*)(kt + fb.k0 + 16 * t8 * D);
+  uint4 hi = D == 128 ? *(const uint4*)(kt + fb.k1 + 16 * t8 * D) : make_uint4(0, 0, 0, 0);
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-// V fragment (B operand) of channel block m: lane column lr is channel
-// 16m + lr, bytes = keys [32g, 32g+32).
-VC_DEV v8i vfrag(const uint8_t* vt, int m, int lr, int g) {
-  int d = 16 * m + lr;
-  const uint8_t* rp = vt + d * kBlk;
-  uint4 lo = *(const uint4*)(rp + ((2 * g) ^ vswz(d)) * 16);
-  uint4 hi = *(const uint4*)(rp + ((2 * g + 1) ^ vswz(d)) * 16);
+template <int D>
+VC_DEV v8i vfrag(const uint8_t* vt, int m, const FragBase<D>& fb) {
+  uint4 lo = *(const uint4*)(vt + fb.v0 + m * 16 * kBlk);
+  uint4 hi = *(const uint4*)(vt + fb.v1 + m * 16 * kBlk);
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
@@ -114,54 +117,62 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2][TileLds<D>::BYTES];
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int qt = lin % nblk;
-  const int bh = lin / nblk;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, g = l >> 4;
+  const int qt = __builtin_amdgcn_readfirstlane(lin % nblk);  // workgroup-uniform, kept scalar
+  const int bh = __builtin_amdgcn_readfirstlane(lin / nblk);
+  const int tid = threadIdx.x, l = tid & 63, lr = l & 15, g = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
   const int64_t S_pad = (int64_t)nblk * kBlk;
   const uint8_t* qb = q8 + (int64_t)bh * S_pad * D;
   const uint8_t* kb = k8 + (int64_t)bh * S_pad * D;
-  const uint8_t* vb = v8 + (int64_t)bh * D * S_pad;
+  const uint8_t* vb = v8 + (int64_t)bh * D * S_pad;  // packed: tile t at + t * 128 * D
   const float* ksb = k_scale + (int64_t)bh * nblk;
   const float c2 = c1 * q_scale[(int64_t)bh * nblk + qt];
 
-  const int start = sequential ? 0 : min(qt + window, nblk - 1);
+  const int start = __builtin_amdgcn_readfirstlane(sequential ? 0 : min(qt + window, nblk - 1));
   auto tile_at = [&](int i) -> int { return sequential ? i : (i <= start ? start - i : i); };
 
-  issue_tile<D>(lds[0], kb, vb, S_pad, tile_at(0), w, l);
+  const unsigned loff = (unsigned)l * 16u;
+  const FragBase<D> fb(lr, g);
+  issue_tile<D>(lds[0], kb, vb, tile_at(0), w, loff);
 
-  // Q^T fragments (B operand), kept in registers for the whole kernel.
+  // Q^T fragments (B operand), kept in registers for the whole kernel; lane
+  // group g carries the channels of K chunks g and g + 4 (D = 64: chunk g).
   v8i qf[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int qrow = qt * kBlk + 32 * w + 16 * s + lr;
-    if (D == 64 && g >= 2) {
-      qf[s] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-    } else {
-      const uint4* qp = (const uint4*)(qb + (int64_t)qrow * D + 32 * g);
-      uint4 lo = qp[0], hi = qp[1];
-      qf[s] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
+    const uint8_t* qp = qb + (int64_t)qrow * D;
+    const uint4 lo = *(const uint4*)(qp + 16 * g);
+    const uint4 hi = D == 128 ? *(const uint4*)(qp + 64 + 16 * g) : make_uint4(0, 0, 0, 0);
+    qf[s] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   }
 
   const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                     0x38383838, 0x38383838, 0x38383838, 0x38383838};  // E4M3 1.0
   const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
-  float M[2] = {-INFINITY, -INFINITY};
+  float M[2] = {-INFINITY, -INFINITY};  // running max of query lr of each sub-tile (log2 units)
+  float Lq[2] = {0.f, 0.f};             // running denominator of query lr
   v4f O[2][NM];
-  v4f L[2] = {zero4, zero4};
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int m = 0; m < NM; ++m) O[s][m] = zero4;
+  // V-Smooth: row sums of the last tiles of the current 8-tile window, kept
+  // for the two window slots 2g, 2g+1 this lane feeds to the mean MFMA.
+  float rb[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
 
   const bool ragged = (S % kBlk) != 0;
 
-  for (int i = 0; i < nblk; ++i) {
+  // One key tile; TAIL marks the last, ragged tile, whose keys >= S get
+  // score -inf (code 0, no part in the maximum).  Instantiated twice so the
+  // common tiles carry no masking selects.
+  auto tile_body = [&](int i, auto tail_tag) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
     const int t = tile_at(i);
     const int buf = i & 1;
     wait_vm();
     __syncthreads();
-    if (i + 1 < nblk) issue_tile<D>(lds[buf ^ 1], kb, vb, S_pad, tile_at(i + 1), w, l);
+    if (i + 1 < nblk) issue_tile<D>(lds[buf ^ 1], kb, vb, tile_at(i + 1), w, loff);
     const uint8_t* Kt = lds[buf];
     const uint8_t* Vt = lds[buf] + TileLds<D>::KB;
 
@@ -169,17 +180,17 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
     v4f Sc[2][8];
 #pragma unroll
     for (int t8 = 0; t8 < 8; ++t8) {
-      v8i kf = kfrag<D>(Kt, t8, lr, g);
+      v8i kf = kfrag<D>(Kt, t8, fb);
       Sc[0][t8] = mfma_fp8(kf, qf[0], zero4);
       Sc[1][t8] = mfma_fp8(kf, qf[1], zero4);
     }
-    if (ragged && t == nblk - 1) {
+    if constexpr (TAIL) {
       const int lim = S - t * kBlk;  // valid keys in this tile
 #pragma unroll
       for (int t8 = 0; t8 < 8; ++t8)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-          if (32 * g + 4 * t8 + v >= lim) {
+          if (16 * t8 + 4 * g + v >= lim) {
             Sc[0][t8][v] = -INFINITY;
             Sc[1][t8][v] = -INFINITY;
           }
@@ -191,24 +202,26 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
     v8i P[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      float mx = fmaxf(fmaxf(Sc[s][0][0], Sc[s][0][1]), fmaxf(Sc[s][0][2], Sc[s][0][3]));
+      float mx = __builtin_fmaxf(Sc[s][0][0], Sc[s][0][1]);
 #pragma unroll
-      for (int t8 = 1; t8 < 8; ++t8)
-        mx = fmaxf(mx, fmaxf(fmaxf(Sc[s][t8][0], Sc[s][t8][1]), fmaxf(Sc[s][t8][2], Sc[s][t8][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float Mn = fmaxf(M[s], gk * mx);
+      for (int e = 2; e < 32; e += 2)  // one v_max3_f32 per two scores
+        mx = __builtin_fmaxf(__builtin_fmaxf(mx, Sc[s][e >> 2][e & 3]), Sc[s][(e + 1) >> 2][(e + 1) & 3]);
+      mx = max_over_groups(mx);
+      const float Mn = __builtin_fmaxf(M[s], gk * mx);
       if (__any(Mn > M[s])) {
         const float alpha = exp2f(M[s] - Mn);
+        Lq[s] *= alpha;
+        if (VS) {
+          rb[s][0] *= alpha;
+          rb[s][1] *= alpha;
+        }
         float a4[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) a4[v] = __shfl(alpha, 4 * g + v);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          L[s][v] *= a4[v];
+        for (int v = 0; v < 4; ++v)
 #pragma unroll
           for (int m = 0; m < NM; ++m) O[s][m][v] *= a4[v];
-        }
         M[s] = Mn;
       }
       const float bb = 119.65f - 8.0f * M[s];
@@ -223,32 +236,83 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
       }
     }
 
-    // ---- A += P V, row sums (and mean restoration) ------------------------
+    // ---- A += P V -------------------------------------------------------------
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      v8i vf = vfrag(Vt, m, lr, g);
+      v8i vf = vfrag<D>(Vt, m, fb);
       O[0][m] = mfma_fp8(P[0], vf, O[0][m]);
       O[1][m] = mfma_fp8(P[1], vf, O[1][m]);
     }
-    if (VS) {
-      const float* mut = mu + ((int64_t)bh * nblk + t) * D;
-      float muv[NM];
+    // ---- row sums over the same bytes: ones x P^T puts query lr's sum in
+    // every register of lane l (the layout of M, alpha and the mean MFMA) ----
+    const int slot = i & 7;
 #pragma unroll
-      for (int m = 0; m < NM; ++m) muv[m] = mut[16 * m + lr];
+    for (int s = 0; s < 2; ++s) {
+      const float r = mfma_fp8(ones, P[s], zero4)[0];
+      Lq[s] += r;
+      if (VS) {
+        if (slot == 2 * g) rb[s][0] = r;
+        if (slot == 2 * g + 1) rb[s][1] = r;
+      }
+    }
+    // ---- V-Smooth mean restoration, A += sum_t r_t mu_t^T, for 8 tiles at a
+    // time on the bf16 matrix cores: K slots (g, 4j + e) carry tile 2g + j of
+    // the window with (r_hi, r_lo, r_hi, 0) x (mu_hi, mu_hi, mu_lo, 0) ----
+    if (VS && (slot == 7 || i == nblk - 1)) {
+      v8bf Ar[2];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        v4f r = mfma_fp8(P[s], ones, zero4);
-        L[s] += r;
 #pragma unroll
-        for (int m = 0; m < NM; ++m)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) O[s][m][v] = __builtin_fmaf(r[v], muv[m], O[s][m][v]);
+        for (int j = 0; j < 2; ++j) {
+          const __bf16 hi = (__bf16)rb[s][j];
+          const __bf16 lo = (__bf16)(rb[s][j] - (float)hi);
+          Ar[s][4 * j + 0] = hi;
+          Ar[s][4 * j + 1] = lo;
+          Ar[s][4 * j + 2] = hi;
+          Ar[s][4 * j + 3] = (__bf16)0.0f;
+          rb[s][j] = 0.f;
+        }
       }
-    } else {
-      L[0] = mfma_fp8(P[0], ones, L[0]);
-      L[1] = mfma_fp8(P[1], ones, L[1]);
+      const int i0 = i - slot;  // visit index of window slot 0
+      const float* mut[2];
+      bool okj[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int iv = i0 + 2 * g + j;
+        okj[j] = iv <= i;
+        mut[j] = mu + ((int64_t)bh * nblk + tile_at(okj[j] ? iv : i)) * D;
+      }
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        v8bf Bm;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const float mv = okj[j] ? mut[j][16 * m + lr] : 0.0f;
+          const __bf16 hi = (__bf16)mv;
+          const __bf16 lo = (__bf16)(mv - (float)hi);
+          Bm[4 * j + 0] = hi;
+          Bm[4 * j + 1] = hi;
+          Bm[4 * j + 2] = lo;
+          Bm[4 * j + 3] = (__bf16)0.0f;
+        }
+        O[0][m] = mfma_bf16(Ar[0], Bm, O[0][m]);
+        O[1][m] = mfma_bf16(Ar[1], Bm, O[1][m]);
+      }
     }
+  };
+
+  // The ragged last key tile is visited either first (mid-window start
+  // clamped to the last block) or last; peel it so the loop body is unmasked.
+  const bool tail_first = ragged && tile_at(0) == nblk - 1;
+  const bool tail_last = ragged && !tail_first;
+  int i0 = 0, i1 = nblk;
+  if (tail_first) {
+    tile_body(0, std::true_type{});
+    i0 = 1;
   }
+  if (tail_last) i1 = nblk - 1;
+  for (int i = i0; i < i1; ++i) tile_body(i, std::false_type{});
+  if (tail_last) tile_body(nblk - 1, std::true_type{});
 
   // ---- epilogue: O = (A / l) * s_V, bf16, original query order -----------
   const int b = bh / H, h = bh % H;
@@ -259,8 +323,9 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int q = qt * kBlk + 32 * w + 16 * s + 4 * g + v;
+      const float lsum = __shfl(Lq[s], 4 * g + v);
       if (q >= S) continue;
-      const float inv = 1.0f / L[s][v];
+      const float inv = 1.0f / lsum;
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         const int d = 16 * m + lr;

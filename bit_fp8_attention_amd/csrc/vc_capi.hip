@@ -83,8 +83,8 @@ __attribute__((visibility("default"))) int32_t vc_quantize(const vc_shape* sh, c
     if (!aligned16(v8) || ((uintptr_t)v_scale & 3u)) return VC_ERR_ALIGN;
   }
   hipStream_t st = (hipStream_t)stream;
-  if (dq && (e = hip_status(vc::launch_qk_quant(*sh, as_bshd(q), q8, q_scale, st)))) return e;
-  if (dk && (e = hip_status(vc::launch_qk_quant(*sh, as_bshd(k), k8, k_scale, st)))) return e;
+  if (dq && (e = hip_status(vc::launch_qk_quant(*sh, as_bshd(q), q8, q_scale, false, st)))) return e;
+  if (dk && (e = hip_status(vc::launch_qk_quant(*sh, as_bshd(k), k8, k_scale, true, st)))) return e;
   if (dv && (e = hip_status(vc::launch_v_quant(*sh, as_bshd(v), v8, v_scale, st)))) return e;
   return VC_OK;
 }

@@ -44,6 +44,43 @@ VC_DEV u32 cvt4_fp8(float x0, float x1, float x2, float x3) {
 // clamped below at 0 by the integer conversion (v_cvt_pk_u8_f32).
 #define VC_EXPCAST_BYTE(word, a, x, b, sel) __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf((a), (x), (b)), (sel), (word))
 
+// Packed FP8 operand layouts (see vc_attn.h): each 128-key tile of K and of
+// V is one contiguous block, and inside it every 16-byte chunk sits at
+// chunk index (logical ^ swizzle(row)).  The attention kernel's fragment
+// reads have 16 lanes read 16 consecutive rows, lane group g taking logical
+// chunks g and g + 4 -- a pattern measured free of LDS bank conflicts on
+// gfx950 with this swizzle -- while the HBM -> LDS copy stays a straight
+// 16 KB block copy.  Inside a V tile the keys are stored in the order the
+// P.V operand wants: byte position p = 64 a + 16 g + 4 t + v of a channel
+// row holds key 64 a + 16 t + 4 g + v, the key the S^T = K Q^T accumulator
+// of MFMA block 4 a + t, register v, puts in lane group g.
+VC_DEV int rswz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+VC_DEV int kswz(int r) { return rswz(r); }
+VC_DEV int vswz(int d) { return rswz(d); }
+VC_DEV int vkey_of_pos(int p) { return (p & 64) + 16 * ((p >> 2) & 3) + 4 * ((p >> 4) & 3) + (p & 3); }
+template <int D>
+VC_DEV int kchunk(int row, int c) {
+  return D == 128 ? (c ^ kswz(row)) : (c ^ (kswz(row) & 3));
+}
+// byte offset of logical (row, 16-byte chunk c) inside a packed K tile
+template <int D>
+VC_DEV int kpack_off(int row, int c) { return row * D + kchunk<D>(row, c) * 16; }
+// byte offset of logical (channel d, position chunk c) inside a packed V tile
+VC_DEV int vpack_off(int d, int c) { return d * kBlk + ((c ^ vswz(d)) * 16); }
+
+// Max over the 4 lanes l, l^16, l^32, l^48 (the 4 lane groups holding one
+// query's keys) with gfx950's row-swap permutes: permlane16_swap exchanges
+// 16-lane rows 1<->0 and 3<->2, permlane32_swap the two 32-lane halves; with
+// both operands x, the max of the two results is the max over the pair.
+VC_DEV float max_over_groups(float x) {
+  int xi = __float_as_int(x);
+  auto p16 = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
+  x = __builtin_fmaxf(__int_as_float(p16[0]), __int_as_float(p16[1]));
+  xi = __float_as_int(x);
+  auto p32 = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  return __builtin_fmaxf(__int_as_float(p32[0]), __int_as_float(p32[1]));
+}
+
 VC_DEV float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

@@ -362,7 +362,7 @@ __global__ __launch_bounds__(256) void group_apply1(const uint16_t* __restrict__
       uint2 c;
       c.x = cvt4_fp8(bf16_lo(w.x) * inv, bf16_hi(w.x) * inv, bf16_lo(w.y) * inv, bf16_hi(w.y) * inv);
       c.y = cvt4_fp8(bf16_lo(w.z) * inv, bf16_hi(w.z) * inv, bf16_lo(w.w) * inv, bf16_hi(w.w) * inv);
-      *(uint2*)(kd + (rg * Mp::RPT + r) * D + ch * 8) = c;
+      *(uint2*)(kd + kpack_off<D>(rg * Mp::RPT + r, ch >> 1) + (ch & 1) * 8) = c;
     }
   }
   // ---- V' block mean ----
@@ -460,18 +460,18 @@ __global__ __launch_bounds__(256) void group_apply2(const uint16_t* __restrict__
     *(u32*)(tile + row * LD + ch * 8 + 4) = c1;
   }
   __syncthreads();
-  const int64_t S_pad = (int64_t)nblk * kBlk;
-  uint8_t* ob = r8 + bh * D * S_pad + (int64_t)j * kBlk;
+  uint8_t* ob = r8 + (bh * nblk + j) * (int64_t)D * kBlk;  // packed V tile j
   constexpr int TASKS = D * (kBlk / 16);
 #pragma unroll
   for (int i = 0; i < TASKS / 256; ++i) {
-    int task = t + 256 * i, d = task / (kBlk / 16), k0 = (task % (kBlk / 16)) * 16;
+    int task = t + 256 * i, d = task / (kBlk / 16), c = task % (kBlk / 16), k0 = c * 16;
     u32 wv[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      wv[q] = (u32)tile[(k0 + 4 * q) * LD + d] | ((u32)tile[(k0 + 4 * q + 1) * LD + d] << 8) |
-              ((u32)tile[(k0 + 4 * q + 2) * LD + d] << 16) | ((u32)tile[(k0 + 4 * q + 3) * LD + d] << 24);
-    *(uint4*)(ob + d * S_pad + k0) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+      wv[q] = (u32)tile[vkey_of_pos(k0 + 4 * q) * LD + d] | ((u32)tile[vkey_of_pos(k0 + 4 * q + 1) * LD + d] << 8) |
+             ((u32)tile[vkey_of_pos(k0 + 4 * q + 2) * LD + d] << 16) |
+             ((u32)tile[vkey_of_pos(k0 + 4 * q + 3) * LD + d] << 24);
+    *(uint4*)(ob + vpack_off(d, c)) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
   }
 }
 

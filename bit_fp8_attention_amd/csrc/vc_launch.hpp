@@ -20,7 +20,7 @@ struct BshdOut {
 };
 
 // vc_quantize.hip
-hipError_t launch_qk_quant(const vc_shape& sh, Bshd x, uint8_t* codes, float* scale, hipStream_t st);
+hipError_t launch_qk_quant(const vc_shape& sh, Bshd x, uint8_t* codes, float* scale, bool pack, hipStream_t st);
 hipError_t launch_v_quant(const vc_shape& sh, Bshd v, uint8_t* v8, float* v_scale, hipStream_t st);
 hipError_t launch_pack_v_bf16(const vc_shape& sh, Bshd v, uint16_t* vt, hipStream_t st);
 hipError_t launch_expcast_codes(const float* x, const float* a, const float* b, int64_t n, int32_t row_len,

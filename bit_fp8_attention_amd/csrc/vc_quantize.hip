@@ -56,8 +56,9 @@ VC_DEV void scale_pair(float amax, float& s, float& inv) {
   }
 }
 
-// Q or K: one workgroup per (block j, head h, batch b).
-template <int D>
+// Q or K: one workgroup per (block j, head h, batch b).  PACK writes the
+// packed K layout (chunk-swizzled rows), otherwise plain row-major codes.
+template <int D, bool PACK>
 __global__ __launch_bounds__(256) void qk_block_quant(const uint16_t* __restrict__ x, int64_t sB, int64_t sS,
                                                       int64_t sH, int S, int H, int nblk,
                                                       uint8_t* __restrict__ codes, float* __restrict__ scale) {
@@ -83,7 +84,8 @@ __global__ __launch_bounds__(256) void qk_block_quant(const uint16_t* __restrict
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     int c = t + 256 * i, row = c / CPR, ch = c % CPR;
-    *(uint2*)(cb + row * D + ch * 8) = codes8(v[i], inv);
+    const int off = PACK ? kpack_off<D>(row, ch >> 1) + (ch & 1) * 8 : row * D + ch * 8;
+    *(uint2*)(cb + off) = codes8(v[i], inv);
   }
 }
 
@@ -112,7 +114,8 @@ __global__ void v_amax_zero(float* v_scale, int BH, int D) {
   if (i < BH) v_scale[(int64_t)i * D] = 0.0f;
 }
 
-// V pass 2: convert one 128-token block and write it key-contiguous.
+// V pass 2: convert one 128-token block and write it as a packed V tile
+// (channel rows of 128 key bytes, chunk-swizzled).
 template <int D>
 __global__ __launch_bounds__(256) void v_convert(const uint16_t* __restrict__ x, int64_t sB, int64_t sS, int64_t sH,
                                                  int S, int H, int nblk, const float* __restrict__ v_scale,
@@ -135,18 +138,18 @@ __global__ __launch_bounds__(256) void v_convert(const uint16_t* __restrict__ x,
     *(u32*)(tile + row * LD + ch * 8 + 4) = cd.y;
   }
   __syncthreads();
-  const int64_t S_pad = (int64_t)nblk * kBlk;
-  uint8_t* ob = v8 + bh * D * S_pad + (int64_t)j * kBlk;
+  uint8_t* ob = v8 + (bh * nblk + j) * (int64_t)D * kBlk;  // packed V tile j
   constexpr int TASKS = D * (kBlk / 16);
 #pragma unroll
   for (int i = 0; i < TASKS / 256; ++i) {
-    int task = t + 256 * i, d = task / (kBlk / 16), k0 = (task % (kBlk / 16)) * 16;
+    int task = t + 256 * i, d = task / (kBlk / 16), c = task % (kBlk / 16), k0 = c * 16;
     u32 w[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      w[q] = (u32)tile[(k0 + 4 * q) * LD + d] | ((u32)tile[(k0 + 4 * q + 1) * LD + d] << 8) |
-             ((u32)tile[(k0 + 4 * q + 2) * LD + d] << 16) | ((u32)tile[(k0 + 4 * q + 3) * LD + d] << 24);
-    *(uint4*)(ob + d * S_pad + k0) = make_uint4(w[0], w[1], w[2], w[3]);
+      w[q] = (u32)tile[vkey_of_pos(k0 + 4 * q) * LD + d] | ((u32)tile[vkey_of_pos(k0 + 4 * q + 1) * LD + d] << 8) |
+             ((u32)tile[vkey_of_pos(k0 + 4 * q + 2) * LD + d] << 16) |
+             ((u32)tile[vkey_of_pos(k0 + 4 * q + 3) * LD + d] << 24);
+    *(uint4*)(ob + vpack_off(d, c)) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -160,7 +163,9 @@ __global__ void v_finalize(float* v_scale, int D) {
   for (int d = threadIdx.x; d < D; d += blockDim.x) v_scale[bh * D + d] = s;
 }
 
-// bf16 V -> key-contiguous bf16 (baseline preparation).
+// bf16 V -> packed bf16 V for the baseline: per (b, h), tile j, half hf
+// (64 keys): D rows of 64 keys, 8-key chunk c of row d at chunk
+// c ^ (vswz(d) & 7).
 template <int D>
 __global__ __launch_bounds__(256) void v_pack_bf16(const uint16_t* __restrict__ x, int64_t sB, int64_t sS,
                                                    int64_t sH, int S, int H, int nblk, uint16_t* __restrict__ vt) {
@@ -182,16 +187,16 @@ __global__ __launch_bounds__(256) void v_pack_bf16(const uint16_t* __restrict__ 
     dst[3] = w.w;
   }
   __syncthreads();
-  const int64_t S_pad = (int64_t)nblk * kBlk;
-  uint16_t* ob = vt + bh * D * S_pad + (int64_t)j * kBlk;
+  uint16_t* ob = vt + (bh * nblk + j) * (int64_t)kBlk * D;  // tile j: two 64-key halves of D x 64
   constexpr int TASKS = D * (kBlk / 8);
 #pragma unroll
   for (int i = 0; i < TASKS / 256; ++i) {
     int task = t + 256 * i, d = task / (kBlk / 8), k0 = (task % (kBlk / 8)) * 8;
+    const int hf = k0 / 64, c = (k0 % 64) / 8;
     u32 w[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) w[q] = (u32)tile[(k0 + 2 * q) * LD + d] | ((u32)tile[(k0 + 2 * q + 1) * LD + d] << 16);
-    *(uint4*)(ob + d * S_pad + k0) = make_uint4(w[0], w[1], w[2], w[3]);
+    *(uint4*)(ob + hf * D * 64 + d * 64 + ((c ^ vswz(d)) & 7) * 8) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -209,13 +214,20 @@ __global__ void expcast_codes_kernel(const float* __restrict__ x, const float* _
 
 }  // namespace
 
-hipError_t launch_qk_quant(const vc_shape& sh, Bshd x, uint8_t* codes, float* scale, hipStream_t st) {
+hipError_t launch_qk_quant(const vc_shape& sh, Bshd x, uint8_t* codes, float* scale, bool pack, hipStream_t st) {
   int nblk = (sh.S + kBlk - 1) / kBlk;
   dim3 grid(nblk, sh.H, sh.B);
-  if (sh.D == 128)
-    qk_block_quant<128><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nblk, codes, scale);
-  else
-    qk_block_quant<64><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nblk, codes, scale);
+  if (sh.D == 128) {
+    if (pack)
+      qk_block_quant<128, true><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nblk, codes, scale);
+    else
+      qk_block_quant<128, false><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nblk, codes, scale);
+  } else {
+    if (pack)
+      qk_block_quant<64, true><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nblk, codes, scale);
+    else
+      qk_block_quant<64, false><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nblk, codes, scale);
+  }
   return hipGetLastError();
 }
 

@@ -22,6 +22,21 @@
  *    base and all three strides must be multiples of 8 elements (16 bytes).
  *  - FP8 data is OCP E4M3 (E4M3FN: bias 7, max 448, no infinities), the
  *    format gfx950's matrix cores consume.
+ *  - Packed FP8 operand layouts.  K and V (and K', R) are stored tile-major
+ *    so that each 128-key tile is one contiguous block the attention kernel
+ *    copies HBM -> LDS as is; inside a tile each 16-byte chunk is placed at
+ *    a swizzled chunk index (this makes the kernel's LDS reads conflict-free)
+ *    and V keys are ordered as the kernel's P.V operand consumes them:
+ *      sw(r) = ((r >> 1) & 7) ^ ((r & 1) << 2)
+ *      packed K, per (b, h): byte ((b*H + h)*nblk + j)*128*D + r*D
+ *        + 16*(c ^ swK(r)) + e holds logical K code [128 j + r][16 c + e]
+ *        (r < 128, c < D/16, e < 16), swK = sw for D = 128, sw & 3 for
+ *        D = 64;
+ *      packed V, per (b, h): byte ((b*H + h)*nblk + j)*D*128 + d*128
+ *        + 16*(c ^ sw(d)) + e (c < 8, e < 16) holds the V code of channel d,
+ *        key 128 j + kappa(16 c + e), kappa(p) = (p & 64)
+ *        + 16*((p >> 2) & 3) + 4*((p >> 4) & 3) + (p & 3).
+ *    Both occupy B*H*S_pad*D bytes, the same as the row-major forms.
  *  - Validation of every argument happens before anything is enqueued; on
  *    error nothing is written and a vc_status other than VC_OK is returned.
  *    A failed launch returns VC_ERR_HIP (from hipGetLastError, no sync).
@@ -84,10 +99,11 @@ const char* vc_status_str(int32_t status);
  *   amax = max |x| over the block's valid rows; s = amax / 448 (fp32);
  *   code = E4M3_rne(x * (448 / amax)) (fp32 product, round-half-even);
  *   a block of zeros takes s = 1.  Rows >= S are written as code 0.
- *   q8, k8:       uint8 [B][H][S_pad][D]
+ *   q8:           uint8 [B][H][S_pad][D] row-major
+ *   k8:           packed K (B*H*S_pad*D bytes)
  *   q_scale, k_scale: fp32 [B][H][nblk]
  * For V: one amax per (b, h) over all S x D elements, same rule;
- *   v8:      uint8 [B][H][D][S_pad]  (key-contiguous; keys >= S are 0)
+ *   v8:      packed V (B*H*S_pad*D bytes; keys >= S are code 0)
  *   v_scale: fp32 [B][H][D]          (the head's scale repeated over d)
  * Any of q, k, v may have ptr == NULL to skip that operand (its outputs are
  * then ignored and may be NULL).  q8/k8/v8 must be 16-byte aligned.
@@ -130,8 +146,8 @@ size_t vc_smooth_group_workspace_size(const vc_shape* shape, int32_t clusters);
  *     amax_d) in fp32.  K' is quantised per 128-row block as in vc_quantize.
  * Outputs (all device, caller-owned):
  *   centroids fp32 [B][H][clusters][D]; labels, perm int32 [B][H][S];
- *   k8 uint8 [B][H][S_pad][D], k_scale fp32 [B][H][nblk];
- *   r8 uint8 [B][H][D][S_pad], r_scale fp32 [B][H][D];
+ *   k8 packed K, k_scale fp32 [B][H][nblk];
+ *   r8 packed V (the residual codes), r_scale fp32 [B][H][D];
  *   mu_bf16 uint16 [B][H][nblk][D]; mu_scaled fp32 [B][H][nblk][D].
  * workspace: >= vc_smooth_group_workspace_size(shape, clusters) bytes,
  * 256-byte aligned; its contents on entry do not matter.
@@ -186,10 +202,12 @@ int32_t vc_attn_fwd(const vc_shape* shape, const vc_attn_params* p, const uint8_
 /* ----------------------------------------------------------------------- */
 
 /*
- * vc_pack_v_bf16 -- key-contiguous copy of V for the BF16 baseline:
- * vt uint16 (bf16 bits) [B][H][D][S_pad], keys >= S zero.  The FP8 path gets
- * the same layout from vc_quantize; both preparations run outside the timed
- * attention call, as on the pages ([VC] Appendix A).
+ * vc_pack_v_bf16 -- key-contiguous, tile-major copy of V for the BF16
+ * baseline (B*H*S_pad*D bf16 values, keys >= S zero): per (b, h), tile j and
+ * half hf in {0, 1}, element ((b*H + h)*nblk + j)*128*D + hf*64*D + d*64
+ * + 8*(c ^ sw(d)) + e holds V[128 j + 64 hf + 8 c + e][d] (c < 8).
+ * The FP8 path gets its packed V from vc_quantize; both preparations run
+ * outside the timed attention call, as on the pages ([VC] Appendix A).
  */
 int32_t vc_pack_v_bf16(const vc_shape* shape, const vc_bshd* v, uint16_t* vt, void* stream);
 

@@ -17,6 +17,7 @@ import torch
 import oracle
 import vcsynth
 from oracle import exact
+from layouts import unpack_k, unpack_v
 
 pytestmark = pytest.mark.gpu
 
@@ -94,12 +95,14 @@ def test_quantize_bitexact(vc, B, S, H, D, kind):
     out = vc.vc_quantize(q.cuda(), k.cuda(), v.cuda())
     torch.cuda.synchronize()
     qb, kb, vb = (vcsynth.bf16_bits(x) for x in (q, k, v))
-    for name, xb in (("q", qb), ("k", kb)):
-        codes, sc = oracle.quantize_qk(xb)
-        assert (_np(out[name + "8"]) == codes).all(), name
-        assert (_np(out[name + "_scale"]) == sc).all(), name
+    codes, sc = oracle.quantize_qk(qb)
+    assert (_np(out["q8"]) == codes).all()
+    assert (_np(out["q_scale"]) == sc).all()
+    codes, sc = oracle.quantize_qk(kb)
+    assert (unpack_k(_np(out["k8"]), D) == codes).all()
+    assert (_np(out["k_scale"]) == sc).all()
     codes, sc = oracle.quantize_v(vb)
-    assert (_np(out["v8"]) == codes).all()
+    assert (unpack_v(_np(out["v8"]), D) == codes).all()
     assert (_np(out["v_scale"]) == sc).all()
 
 
@@ -112,12 +115,12 @@ def test_quantize_strided_views(vc):
     q, k, v = fd[:, :, 0], fd[:, :, 1], fd[:, :, 2]
     out = vc.vc_quantize(q, k, v)
     torch.cuda.synchronize()
-    for name, x in (("q", fused[:, :, 0]), ("k", fused[:, :, 1])):
-        codes, sc = oracle.quantize_qk(vcsynth.bf16_bits(x))
-        assert (_np(out[name + "8"]) == codes).all()
-        assert (_np(out[name + "_scale"]) == sc).all()
+    codes, sc = oracle.quantize_qk(vcsynth.bf16_bits(fused[:, :, 0]))
+    assert (_np(out["q8"]) == codes).all() and (_np(out["q_scale"]) == sc).all()
+    codes, sc = oracle.quantize_qk(vcsynth.bf16_bits(fused[:, :, 1]))
+    assert (unpack_k(_np(out["k8"]), D) == codes).all() and (_np(out["k_scale"]) == sc).all()
     codes, sc = oracle.quantize_v(vcsynth.bf16_bits(fused[:, :, 2]))
-    assert (_np(out["v8"]) == codes).all() and (_np(out["v_scale"]) == sc).all()
+    assert (unpack_v(_np(out["v8"]), D) == codes).all() and (_np(out["v_scale"]) == sc).all()
 
 
 # --------------------------------------------------------------------------- #
@@ -181,12 +184,12 @@ def _group_case(vc, k, v, clusters, iters, seed):
         assert (_np(g["labels"][b, h]) == r["labels"]).all(), ("labels", b, h)
         assert (_np(g["centroids"][b, h]) == r["centroids"]).all(), ("centroids", b, h)
         assert (_np(g["perm"][b, h]) == r["perm"]).all(), ("perm", b, h)
-        assert (_np(g["k8"][b, h]) == r["k_codes"]).all(), ("k8", b, h)
+        assert (unpack_k(_np(g["k8"][b, h]), D) == r["k_codes"]).all(), ("k8", b, h)
         assert (_np(g["k_scale"][b, h]) == r["k_scale"]).all(), ("k_scale", b, h)
         assert (_np(g["mu_bf16"][b, h]).view(np.uint16) == r["mu_bf16"]).all(), ("mu", b, h)
         assert (_np(g["mu_scaled"][b, h]) == r["mu_scaled"]).all(), ("mu_scaled", b, h)
         assert (_np(g["r_scale"][b, h]) == r["r_scale"]).all(), ("r_scale", b, h)
-        assert (_np(g["r8"][b, h]) == r["r_codes"]).all(), ("r8", b, h)
+        assert (unpack_v(_np(g["r8"][b, h]), D) == r["r_codes"]).all(), ("r8", b, h)
     return g, ref
 
 
@@ -286,3 +289,45 @@ def test_attn_vsmooth_video_envelope(vc):
         _, tau = exact.row_tv_check(s_deq * exact.LOG2E)
         bound = (0.0364 + tau + tv_qk + 1e-4) * diam_ub + dv + 1e-2 * vmax
         assert np.linalg.norm(og[0, i, 0] - ref[ri]) <= bound, (i, bound)
+
+
+# --------------------------------------------------------------------------- #
+# BF16 baseline on the same skeleton (checked against exact fp64 attention)
+# --------------------------------------------------------------------------- #
+
+BF16_TOL = 1e-2  # bf16 probabilities and output rounding, 2^-9 relative each
+
+
+@pytest.mark.parametrize("B,S,H,D,sm,seq", [(1, 1000, 2, 128, 1 / math.sqrt(128), False),
+                                            (1, 1024, 2, 64, 1 / 8, False), (2, 300, 1, 64, 0.3, True),
+                                            (1, 129, 1, 128, 2 / math.sqrt(128), False),
+                                            (1, 64, 1, 128, 1 / math.sqrt(128), False)])
+def test_attn_bf16_baseline_vs_exact(vc, B, S, H, D, sm, seq):
+    print(f"case bf16 baseline B={B} S={S} H={H} D={D} seq={seq}", flush=True)
+    q, k, v = vcsynth.random_qkv(B, S, H, D, seed=3 * S + D, v_kind="t3")
+    vt = vc.vc_pack_v_bf16(v.cuda())
+    o = vc.vc_attn_fwd_bf16(q.cuda(), k.cuda(), vt, sm_scale=sm, sequential=seq)
+    torch.cuda.synchronize()
+    og = _bf16_f32(o)
+    qb, kb, vb = (vcsynth.bf16_bits(x) for x in (q, k, v))
+    for b in range(B):
+        for h in range(H):
+            ref = exact.attention_rows(exact.to_f64(qb[b, :, h]), exact.to_f64(kb[b, :, h]),
+                                       exact.to_f64(vb[b, :, h]), sm)
+            assert _rel_l2(og[b, :, h], ref) <= BF16_TOL
+
+
+def test_attn_bf16_baseline_plain_config(vc):
+    print("case bf16 baseline plain-config S=16384 H=2 sampled", flush=True)
+    q, k, v = vcsynth.make_qkv("plain", H=2)
+    sm = 1 / math.sqrt(128)
+    vt = vc.vc_pack_v_bf16(v.cuda())
+    o = vc.vc_attn_fwd_bf16(q.cuda(), k.cuda(), vt, sm_scale=sm)
+    torch.cuda.synchronize()
+    og = _bf16_f32(o)
+    qb, kb, vb = (vcsynth.bf16_bits(x) for x in (q, k, v))
+    rows = np.sort(np.random.default_rng(4).choice(q.shape[1], 128, replace=False))
+    for h in range(2):
+        ref = exact.attention_rows(exact.to_f64(qb[0, :, h]), exact.to_f64(kb[0, :, h]), exact.to_f64(vb[0, :, h]),
+                                   sm, rows)
+        assert _rel_l2(og[0, rows, h], ref) <= BF16_TOL
