@@ -19,8 +19,7 @@
  * plain * and / otherwise); sums the matrix cores accumulate are done here
  * in fp64.
  *
- * Readings where the pages leave a step open are stated at each function and
- * collected in the design doc.
+ * Readings where the pages leave a step open are stated at each function.
  */
 #include <math.h>
 #include <stdint.h>
