@@ -114,7 +114,11 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
     const float* __restrict__ mu, uint16_t* __restrict__ o, int64_t oB, int64_t oS, int64_t oH, int S, int H,
     int nblk, float c1, int window, int sequential) {
   constexpr int NM = D / 16;  // channel blocks of the output
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2][TileLds<D>::BYTES];
+  // two separate LDS objects (not one array indexed by parity), so the
+  // compiler can tell the buffer being filled by DMA from the one being read
+  // and does not wait for the copy in flight before reading the other
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[TileLds<D>::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[TileLds<D>::BYTES];
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int qt = __builtin_amdgcn_readfirstlane(lin % nblk);  // workgroup-uniform, kept scalar
@@ -133,7 +137,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
 
   const unsigned loff = (unsigned)l * 16u;
   const FragBase<D> fb(lr, g);
-  issue_tile<D>(lds[0], kb, vb, tile_at(0), w, loff);
+  issue_tile<D>(lds0, kb, vb, tile_at(0), w, loff);
 
   // Q^T fragments (B operand), kept in registers for the whole kernel; lane
   // group g carries the channels of K chunks g and g + 4 (D = 64: chunk g).
@@ -166,15 +170,14 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
   // One key tile; TAIL marks the last, ragged tile, whose keys >= S get
   // score -inf (code 0, no part in the maximum).  Instantiated twice so the
   // common tiles carry no masking selects.
-  auto tile_body = [&](int i, auto tail_tag) {
+  auto tile_body = [&](int i, uint8_t* cur, uint8_t* nxt, auto tail_tag) {
     constexpr bool TAIL = decltype(tail_tag)::value;
     const int t = tile_at(i);
-    const int buf = i & 1;
     wait_vm();
     __syncthreads();
-    if (i + 1 < nblk) issue_tile<D>(lds[buf ^ 1], kb, vb, tile_at(i + 1), w, loff);
-    const uint8_t* Kt = lds[buf];
-    const uint8_t* Vt = lds[buf] + TileLds<D>::KB;
+    if (i + 1 < nblk) issue_tile<D>(nxt, kb, vb, tile_at(i + 1), w, loff);
+    const uint8_t* Kt = cur;
+    const uint8_t* Vt = cur + TileLds<D>::KB;
 
     // ---- S^T = K Q^T ------------------------------------------------------
     v4f Sc[2][8];
@@ -307,12 +310,30 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
   const bool tail_last = ragged && !tail_first;
   int i0 = 0, i1 = nblk;
   if (tail_first) {
-    tile_body(0, std::true_type{});
+    tile_body(0, lds0, lds1, std::true_type{});
     i0 = 1;
   }
   if (tail_last) i1 = nblk - 1;
-  for (int i = i0; i < i1; ++i) tile_body(i, std::false_type{});
-  if (tail_last) tile_body(nblk - 1, std::true_type{});
+  // unrolled by two so each buffer is a fixed LDS object in each half
+  int i = i0;
+  if (i & 1) {
+    if (i < i1) tile_body(i, lds1, lds0, std::false_type{});
+    ++i;
+  }
+  for (; i + 1 < i1; i += 2) {
+    tile_body(i, lds0, lds1, std::false_type{});
+    tile_body(i + 1, lds1, lds0, std::false_type{});
+  }
+  if (i < i1) {
+    tile_body(i, lds0, lds1, std::false_type{});
+    ++i;
+  }
+  if (tail_last) {
+    if ((nblk - 1) & 1)
+      tile_body(nblk - 1, lds1, lds0, std::true_type{});
+    else
+      tile_body(nblk - 1, lds0, lds1, std::true_type{});
+  }
 
   // ---- epilogue: O = (A / l) * s_V, bf16, original query order -----------
   const int b = bh / H, h = bh % H;
@@ -340,8 +361,8 @@ hipError_t launch_t(const vc_shape& sh, float c1, int window, int seq, const uin
                     BshdOut o, hipStream_t st) {
   const int nblk = (sh.S + kBlk - 1) / kBlk;
   const int64_t n = (int64_t)nblk * sh.H * sh.B;
-  attn_fp8_kernel<D, VS><<<(unsigned)n, 256, 0, st>>>(q8, qs, k8, ks, v8, vs, mu, o.p, o.sB, o.sS, o.sH, sh.S,
-                                                       sh.H, nblk, c1, window, seq);
+  attn_fp8_kernel<D, VS><<<(unsigned)n, 256, 0, st>>>(q8, qs, k8, ks, v8, vs, mu, o.p, o.sB, o.sS, o.sH, sh.S, sh.H,
+                                                       nblk, c1, window, seq);
   return hipGetLastError();
 }
 
