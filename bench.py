@@ -16,6 +16,8 @@ is timed on a bounded sample of the same workload (`cpu_baseline`), and the
 in-house BF16 baseline on the same kernel skeleton gives the speedup.
 
 Usage: python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--workload wan]
+       python bench.py --traffic-job          (under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)
+       python bench.py --traffic-summary FETCH_DIR WRITE_DIR OUT_JSON COMMAND
 """
 from __future__ import annotations
 
@@ -56,6 +58,82 @@ def traffic_from_profile():
     if t.get("kernel_source_sha256") != _sha(ATTN_SRC):
         return None
     return t.get("bytes_per_launch")
+
+
+COPY_BYTES = 1 << 30  # calibration copy: reads and writes exactly this many bytes
+
+
+def traffic_job(w):
+    """One V-Smooth attention launch on the workload, then one plain device
+    copy of COPY_BYTES as the very last dispatch.  Meant to run under
+    `rocprofv3 --pmc FETCH_SIZE` (then WRITE_SIZE); `--traffic-summary` turns
+    the two runs into HBM bytes per attention launch, scaled by what the same
+    counter reads for the copy of known size."""
+    import torch
+
+    import bit_fp8_attention_amd as vc
+    import vcsynth
+    q, k, v = vcsynth.make_qkv(w.name, device="cuda")
+    qz = vc.vc_quantize(q)
+    g = vc.vc_smooth_group(k, v, w.clusters, w.iters, w.seed)
+    o = torch.empty_like(q)
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    vc.vc_attn_fwd(qz["q8"], qz["q_scale"], g["k8"], g["k_scale"], g["r8"], g["r_scale"], g["mu_scaled"], S=w.S,
+                   out=o, sm_scale=w.sm_scale)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    log("traffic job done")
+
+
+def _counter_rows(d, counter):
+    import csv
+    import glob
+    rows = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                did = int(r["Dispatch_Id"])
+                name, val = rows.get(did, (r["Kernel_Name"], 0.0))
+                rows[did] = (name, val + float(r["Counter_Value"]))
+    if not rows:
+        raise SystemExit(f"no {counter} rows under {d}")
+    return rows
+
+
+def traffic_summary(fetch_dir, write_dir, out_path, command):
+    """Per-launch HBM traffic of the attention kernel from the two counter
+    runs of `--traffic-job`: each counter (KiB per dispatch) is scaled by
+    COPY_BYTES / (what it reads for the final copy dispatch)."""
+    res = {}
+    for key, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = _counter_rows(d, counter)
+        attn = [(i, v) for i, v in rows.items() if "attn_fp8_kernel" in v[0]]
+        if len(attn) != 1:
+            raise SystemExit(f"expected one attention dispatch in {d}, found {len(attn)}")
+        copy_id = max(rows)
+        copy_name, copy_kib = rows[copy_id]
+        attn_kib = attn[0][1][1]
+        factor = COPY_BYTES / (copy_kib * 1024.0)
+        res[key] = {"counter": counter, "attn_kib": attn_kib, "copy_kib": copy_kib, "copy_kernel": copy_name[:80],
+                    "factor": factor, "bytes": attn_kib * 1024.0 * factor}
+    rec = {
+        "kernel": "attn_fp8_kernel<128,true>",
+        "workload": "wan: B=1 H=40 S=75600 D=128, V-Smooth",
+        "kernel_source_sha256": _sha(ATTN_SRC),
+        "fetch_bytes": res["fetch"]["bytes"],
+        "write_bytes": res["write"]["bytes"],
+        "bytes_per_launch": res["fetch"]["bytes"] + res["write"]["bytes"],
+        "calibration": f"{COPY_BYTES}-byte device copy, last dispatch of the job",
+        "counters": res,
+        "command": command,
+    }
+    with open(out_path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
 
 
 def cpu_baseline(w, q, k, v, target_s=12.0):
@@ -109,7 +187,14 @@ def main():
     ap.add_argument("--workload", default="wan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--traffic-job", action="store_true",
+                    help="one attention launch + calibration copy, for rocprofv3 --pmc runs")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON", "COMMAND"),
+                    help="write the per-launch traffic record from the two counter runs")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -123,6 +208,9 @@ def main():
     w = vcsynth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.traffic_job:
+        traffic_job(w)
+        return
     t0 = time.perf_counter()
     q, k, v = vcsynth.make_qkv(w.name, device=dev)
     torch.cuda.synchronize()

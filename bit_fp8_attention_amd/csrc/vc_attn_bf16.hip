@@ -43,7 +43,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
   constexpr int KBYTES = kHalf * D * 2;
   constexpr int VBYTES = D * kHalf * 2;
   constexpr int NI = KBYTES / 1024 / 4;  // DMA copies per wave per operand
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2][KBYTES + VBYTES];
+  // two separate LDS objects so the DMA into one does not make the compiler
+  // wait before reads of the other
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[KBYTES + VBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[KBYTES + VBYTES];
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int qt = __builtin_amdgcn_readfirstlane(lin % nblk);
@@ -109,16 +112,15 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
 
   const int nsteps = 2 * nblk;
   const bool ragged = (S % kBlk) != 0;
-  issue(0, lds[0]);
+  issue(0, lds0);
 
-  auto step_body = [&](int st, auto tail_tag) {
+  auto step_body = [&](int st, uint8_t* cur, uint8_t* nxt, auto tail_tag) {
     constexpr bool TAIL = decltype(tail_tag)::value;
-    const int buf = st & 1;
     wait_vm();
     __syncthreads();
-    if (st + 1 < nsteps) issue(st + 1, lds[buf ^ 1]);
-    const uint8_t* Kt = lds[buf];
-    const uint8_t* Vt = lds[buf] + KBYTES;
+    if (st + 1 < nsteps) issue(st + 1, nxt);
+    const uint8_t* Kt = cur;
+    const uint8_t* Vt = cur + KBYTES;
     const int key0 = tile_at(st >> 1) * kBlk + (st & 1) * kHalf;
 
     v4f Sc[2][4];
@@ -198,15 +200,19 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
   const bool tail_last = ragged && !tail_first;
   int s0 = 0, s1 = nsteps;
   if (tail_first) {
-    step_body(0, std::true_type{});
-    step_body(1, std::true_type{});
+    step_body(0, lds0, lds1, std::true_type{});
+    step_body(1, lds1, lds0, std::true_type{});
     s0 = 2;
   }
   if (tail_last) s1 = nsteps - 2;
-  for (int st = s0; st < s1; ++st) step_body(st, std::false_type{});
+  // s0, s1 and nsteps are even: even steps read lds0, odd steps lds1
+  for (int st = s0; st < s1; st += 2) {
+    step_body(st, lds0, lds1, std::false_type{});
+    step_body(st + 1, lds1, lds0, std::false_type{});
+  }
   if (tail_last) {
-    step_body(nsteps - 2, std::true_type{});
-    step_body(nsteps - 1, std::true_type{});
+    step_body(nsteps - 2, lds0, lds1, std::true_type{});
+    step_body(nsteps - 1, lds1, lds0, std::true_type{});
   }
 
   uint16_t* ob = o + b * oB + h * oH;
