@@ -58,7 +58,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
   const uint16_t* kbp = k + b * kB + h * kH;
   const uint8_t* vb = (const uint8_t*)(vt + (int64_t)bh * nblk * kBlk * D);
 
-  const int start = __builtin_amdgcn_readfirstlane(sequential ? 0 : min(qt + window, nblk - 1));
+  // the FP8 kernel's order: `window` blocks past the diagonal of the
+  // query-tile pair (qt | 1)
+  const int start = __builtin_amdgcn_readfirstlane(sequential ? 0 : min((qt | 1) + window, nblk - 1));
   auto tile_at = [&](int i) -> int { return sequential ? i : (i <= start ? start - i : i); };
 
   // per-lane DMA sources of the K half-tile: LDS byte p = (4r + w) KB + 16 l

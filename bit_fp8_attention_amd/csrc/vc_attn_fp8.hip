@@ -19,9 +19,11 @@
 //  - keys are visited mid-window ([OVC] "Mid-window key traversal").
 //
 // MI355X mapping:
-//  - one workgroup = one 128-query tile (the Q-scale block) of one (b, h):
-//    4 waves x 32 queries (two 16-query sub-tiles per wave), two workgroups
-//    per CU so that one wave's matrix-core chain overlaps another's VALU work;
+//  - one workgroup = two 128-query tiles (each its own Q-scale block) of one
+//    (b, h), 8 waves x 32 queries; the two 4-wave halves share one stream of
+//    K/V tiles and run their matrix-core and VALU phases one phase apart
+//    (barrier ping-pong), so on every SIMD one wave's products overlap the
+//    other wave's codes;
 //  - S^T = K Q^T on v_mfma_f32_16x16x128_f8f6f4 (K = D = 128): the output
 //    puts one query and 4 keys in each lane; the packed V tile stores its keys
 //    in exactly the order in which those accumulators hand them to the P.V
@@ -30,7 +32,7 @@
 //  - K and V are stored tile-major and pre-swizzled (the packed layouts of
 //    vc_attn.h), so each 16 KB tile streams HBM -> LDS as one straight copy
 //    with global_load_lds_dwordx4 (no VGPR staging, no per-tile address
-//    arithmetic), double-buffered, and the 32-byte fragment reads from LDS
+//    arithmetic) into 3-stage rings, and the 32-byte fragment reads from LDS
 //    are bank-conflict free;
 //  - workgroup ids are remapped so each XCD works on a contiguous range of
 //    query tiles of one head, whose mid-window sweeps hit the same K/V in that
@@ -51,24 +53,6 @@ struct TileLds {
   static constexpr int VB = D * kBlk;
   static constexpr int BYTES = KB + VB;
 };
-
-// Issue the asynchronous copies of key tile `t` (two contiguous 16 KB
-// blocks in the packed layouts) into LDS buffer `buf`: wave w, copy r moves
-// bytes [(4r + w) KB, +1 KB), lane l its 16 bytes at + 16 l.
-template <int D>
-VC_DEV void issue_tile(uint8_t* buf, const uint8_t* __restrict__ kb, const uint8_t* __restrict__ vb, int t, int w,
-                       unsigned loff) {
-  constexpr int NI = D * kBlk / 1024 / 4;  // copies per wave per operand
-  const uint8_t* kt = kb + (int64_t)t * kBlk * D;
-  const uint8_t* vt = vb + (int64_t)t * kBlk * D;
-  uint8_t* vbuf = buf + TileLds<D>::KB;
-#pragma unroll
-  for (int r = 0; r < NI; ++r) {
-    const int base = (r * 4 + w) * 1024;
-    lds_dma16(kt + base + loff, buf + base);
-    lds_dma16(vt + base + loff, vbuf + base);
-  }
-}
 
 // Fragment reads.  For MFMA block t8 the A-operand lane row i = lr holds
 // key 16*t8 + lr: the 16 lanes of a group read 16 consecutive K rows, lane
@@ -107,24 +91,101 @@ VC_DEV v8i vfrag(const uint8_t* vt, int m, const FragBase<D>& fb) {
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
+// ---------------------------------------------------------------------------
+// Two-query-tile ping-pong kernel.
+//
+// One workgroup of 8 waves holds two 128-query tiles of one (b, h) that share
+// one stream of K/V tiles ([OVC] "A warp-specialized pipeline": each CTA holds
+// two query tiles that alternate).  Half A (waves 0-3) takes query tile 2p,
+// half B (waves 4-7) tile 2p + 1; waves w and w + 4 share a SIMD.  Each wave
+// alternates two phases per key tile j:
+//   M(j): matrix cores -- P_{j-1} V_{j-1}, the row sums of P_{j-1}, and
+//         S_j^T = K_j Q^T;
+//   V(j): VALU -- running max, rescale, ExpCast codes P_j.
+// Half B runs one phase behind half A (one extra barrier at the start, A one
+// at the end), so on every SIMD one wave's matrix-core chain runs while the
+// other wave computes codes.  K and V tiles go through two 3-stage LDS rings;
+// half B issues all copies, in its V phase (it reads no LDS there): at V(j)
+// it loads K_{j+3} into K_j's stage and V_{j+2} into V_{j-1}'s stage, both
+// read for the last time in M(j).  A copy has four phases to land.
+// ---------------------------------------------------------------------------
+
+// The same 16-byte global -> LDS copy as lds_dma16 (lane i lands at
+// lds_base + 16 i), issued as inline asm.  The hardware counts these copies
+// on vmcnt only (an outstanding copy does not hold lgkmcnt, measured), but
+// the compiler's wait insertion, seeing one, stops trusting partial lgkmcnt
+// counts and drains every LDS read before its first use.  Hidden from it,
+// the fragment reads get exact partial waits; the kernel orders the copies
+// itself with explicit vmcnt waits and barriers.
+VC_DEV void lds_dma16_raw(const void* g, void* lds_base) {
+  const unsigned lds = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)LDS_PTR(lds_base));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, class F>
+VC_DEV void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Barrier between phases: waits for this wave's own LDS reads and scalar
+// loads only.  The copies in flight are waited for by the waves that issued
+// them (a fence here would wait for every outstanding copy).  The barrier
+// is inline asm with a memory clobber so the compiler moves no memory access
+// across it, and the scheduling barriers pin every other instruction.
+VC_DEV void phase_sync() {
+  __builtin_amdgcn_sched_barrier(0);  // no instruction moves across a phase boundary
+  // lgkmcnt(0), vmcnt and expcnt at their maxima; as a builtin, so the
+  // compiler's own wait insertion knows every LDS and scalar load is done
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// s_waitcnt with vmcnt = N, other counters at their maxima (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+VC_DEV void wait_vm_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
+}
+
 template <int D, bool VS>
-__global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
+__global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ q_scale, const uint8_t* __restrict__ k8,
     const float* __restrict__ k_scale, const uint8_t* __restrict__ v8, const float* __restrict__ v_scale,
     const float* __restrict__ mu, uint16_t* __restrict__ o, int64_t oB, int64_t oS, int64_t oH, int S, int H,
-    int nblk, float c1, int window, int sequential) {
-  constexpr int NM = D / 16;  // channel blocks of the output
-  // two separate LDS objects (not one array indexed by parity), so the
-  // compiler can tell the buffer being filled by DMA from the one being read
-  // and does not wait for the copy in flight before reading the other
-  __shared__ __attribute__((aligned(1024))) uint8_t lds0[TileLds<D>::BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds1[TileLds<D>::BYTES];
+    int nblk, int npair, float c1, int window, int sequential) {
+  constexpr int NM = D / 16;             // channel blocks of the output
+  constexpr int TB = kBlk * D;           // bytes of one K or V tile
+  constexpr int NI = TB / 1024 / 4;      // 1 KB copies per issuing wave per tile
+  // six separate LDS objects, so the compiler can tell every stage apart
+  __shared__ __attribute__((aligned(1024))) uint8_t kst0[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t kst1[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t kst2[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t vst0[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t vst1[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t vst2[TB];
+  // V-Smooth: ring of the scaled block-mean rows of the last 16 visited
+  // tiles (one 8-tile restoration window plus the rows in flight)
+  constexpr int MR = VS ? 16 : 1;
+  __shared__ __attribute__((aligned(1024))) float mring[MR][D];
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int qt = __builtin_amdgcn_readfirstlane(lin % nblk);  // workgroup-uniform, kept scalar
-  const int bh = __builtin_amdgcn_readfirstlane(lin / nblk);
+  const int pr = __builtin_amdgcn_readfirstlane(lin % npair);
+  const int bh = __builtin_amdgcn_readfirstlane(lin / npair);
   const int tid = threadIdx.x, l = tid & 63, lr = l & 15, g = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
+  const bool hb = w >= 4;                                  // half B
+  const int wq = w & 3;                                    // wave within the half
+  const int n = nblk;
+  // with an odd number of query tiles, half B of the last pair repeats half
+  // A's tile (it must take part in every barrier) and stores nothing
+  const bool live = 2 * pr + (hb ? 1 : 0) < nblk;
+  const int qt = __builtin_amdgcn_readfirstlane(live ? 2 * pr + (hb ? 1 : 0) : nblk - 1);
   const int64_t S_pad = (int64_t)nblk * kBlk;
   const uint8_t* qb = q8 + (int64_t)bh * S_pad * D;
   const uint8_t* kb = k8 + (int64_t)bh * S_pad * D;
@@ -132,19 +193,65 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
   const float* ksb = k_scale + (int64_t)bh * nblk;
   const float c2 = c1 * q_scale[(int64_t)bh * nblk + qt];
 
-  const int start = __builtin_amdgcn_readfirstlane(sequential ? 0 : min(qt + window, nblk - 1));
+  // mid-window order of the pair: start a few tiles past the pair's diagonal
+  const int start = __builtin_amdgcn_readfirstlane(sequential ? 0 : min(2 * pr + 1 + window, nblk - 1));
   auto tile_at = [&](int i) -> int { return sequential ? i : (i <= start ? start - i : i); };
 
   const unsigned loff = (unsigned)l * 16u;
-  const FragBase<D> fb(lr, g);
-  issue_tile<D>(lds0, kb, vb, tile_at(0), w, loff);
+  // copies of half B, wave wq: 1 KB blocks 4r + wq of a tile; with V-Smooth
+  // also bytes [wq D, (wq + 1) D) of the tile's mean row (D / 16 lanes),
+  // issued first in a group, so that a read of the ring waits for no tile
+  auto issue_mu = [&](int i) {
+    if (VS) {
+      const uint8_t* msrc = (const uint8_t*)(mu + ((int64_t)bh * nblk + tile_at(i)) * D) + wq * D;
+      if (l < D / 16) lds_dma16_raw(msrc + loff, (uint8_t*)&mring[i & (MR - 1)][0] + wq * D);
+    }
+  };
+  auto issue_k = [&](uint8_t* dst, int i) {
+    const uint8_t* src = kb + (int64_t)tile_at(i) * TB;
+#pragma unroll
+    for (int r = 0; r < NI; ++r) {
+      const int base = (r * 4 + wq) * 1024;
+      lds_dma16_raw(src + base + loff, dst + base);
+    }
+  };
+  auto issue_v = [&](uint8_t* dst, int i) {
+    const uint8_t* src = vb + (int64_t)tile_at(i) * TB;
+#pragma unroll
+    for (int r = 0; r < NI; ++r) {
+      const int base = (r * 4 + wq) * 1024;
+      lds_dma16_raw(src + base + loff, dst + base);
+    }
+  };
+  constexpr int GRP = 2 * NI + (VS ? 1 : 0);  // copies per wave per full group
 
-  // Q^T fragments (B operand), kept in registers for the whole kernel; lane
-  // group g carries the channels of K chunks g and g + 4 (D = 64: chunk g).
+  const FragBase<D> fb(lr, g);
+  const bool ragged = (S % kBlk) != 0;
+  const bool tail_first = ragged && tile_at(0) == n - 1;
+  const bool tail_last = ragged && !tail_first;  // then tile_at(n - 1) == n - 1
+
+  if (VS) {  // rows never written must read as finite zeros
+    float* mz = &mring[0][0];
+    for (int e = tid; e < MR * D; e += 512) mz[e] = 0.f;
+    __syncthreads();
+  }
+  // prologue: mean row 0, K_0, V_0, K_1; K_0 must have landed before M(0)
+  if (hb) {
+    issue_mu(0);
+    issue_k(kst0, 0);
+    issue_v(vst0, 0);
+    if (n > 1) {
+      issue_k(kst1, 1);
+      wait_vm_n<2 * NI>();
+    } else {
+      wait_vm();
+    }
+  }
+
   v8i qf[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    const int qrow = qt * kBlk + 32 * w + 16 * s + lr;
+    const int qrow = qt * kBlk + 32 * wq + 16 * s + lr;
     const uint8_t* qp = qb + (int64_t)qrow * D;
     const uint4 lo = *(const uint4*)(qp + 16 * g);
     const uint4 hi = D == 128 ? *(const uint4*)(qp + 64 + 16 * g) : make_uint4(0, 0, 0, 0);
@@ -161,33 +268,120 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int m = 0; m < NM; ++m) O[s][m] = zero4;
-  // V-Smooth: row sums of the last tiles of the current 8-tile window, kept
-  // for the two window slots 2g, 2g+1 this lane feeds to the mean MFMA.
+  // V-Smooth: row sums of the window slots 2g, 2g + 1 that lane group g
+  // feeds to the mean product
   float rb[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+  v4f Sc[2][8];                               // S^T of the current tile
+  float ksv = ksb[tile_at(0)];                // key scale of the current tile
+  v8i P[2];                                   // codes of the previous tile
 
-  const bool ragged = (S % kBlk) != 0;
-
-  // One key tile; TAIL marks the last, ragged tile, whose keys >= S get
-  // score -inf (code 0, no part in the maximum).  Instantiated twice so the
-  // common tiles carry no masking selects.
-  auto tile_body = [&](int i, uint8_t* cur, uint8_t* nxt, auto tail_tag) {
-    constexpr bool TAIL = decltype(tail_tag)::value;
-    const int t = tile_at(i);
-    wait_vm();
-    __syncthreads();
-    if (i + 1 < nblk) issue_tile<D>(nxt, kb, vb, tile_at(i + 1), w, loff);
-    const uint8_t* Kt = cur;
-    const uint8_t* Vt = cur + TileLds<D>::KB;
-
-    // ---- S^T = K Q^T ------------------------------------------------------
-    v4f Sc[2][8];
+  // ---- M phase: row sums of P_{j-1}, P_{j-1} V_{j-1}, then S_j^T = K_j Q^T.
+  // Fragment k of a phase is V channel block k (k < NM), then K key block
+  // k - NM; each is read from LDS two MFMA pairs ahead of its use, so the LDS
+  // latency hides behind matrix-core work.  PV / QK are std::true_type or
+  // std::false_type, so every index is a compile-time constant. ----
+  auto mphase = [&](int j, const uint8_t* Kt, const uint8_t* Vt, auto pv_tag, auto qk_tag) {
+    constexpr bool PV = decltype(pv_tag)::value;
+    constexpr bool QK = decltype(qk_tag)::value;
+    constexpr int K0 = PV ? 0 : NM;
+    constexpr int K1 = QK ? NM + 8 : NM;
+    constexpr int KD = D == 128 ? 2 : 1;  // LDS reads of one K fragment
+    auto frag = [&](auto kk) -> v8i {
+      constexpr int k = decltype(kk)::value;
+      if constexpr (k < NM)
+        return vfrag<D>(Vt, k, fb);
+      else
+        return kfrag<D>(Kt, k - NM, fb);
+    };
+    auto nds = [](int k) { return k < NM ? 2 : KD; };
+    v8i fr[3];
+    if constexpr (K0 < K1) fr[K0 % 3] = frag(std::integral_constant<int, K0>{});
+    if constexpr (K0 + 1 < K1) fr[(K0 + 1) % 3] = frag(std::integral_constant<int, K0 + 1>{});
+    float rr[2] = {0.f, 0.f};
+    if constexpr (PV) {
 #pragma unroll
-    for (int t8 = 0; t8 < 8; ++t8) {
-      v8i kf = kfrag<D>(Kt, t8, fb);
-      Sc[0][t8] = mfma_fp8(kf, qf[0], zero4);
-      Sc[1][t8] = mfma_fp8(kf, qf[1], zero4);
+      for (int s = 0; s < 2; ++s) rr[s] = mfma_fp8(ones, P[s], zero4)[0];
     }
-    if constexpr (TAIL) {
+    static_for<K0, K1>([&](auto kk) {
+      constexpr int k = decltype(kk)::value;
+      if constexpr (k + 2 < K1) fr[(k + 2) % 3] = frag(std::integral_constant<int, k + 2>{});
+      const v8i f = fr[k % 3];
+      if constexpr (k < NM) {
+        O[0][k] = mfma_fp8(P[0], f, O[0][k]);
+        O[1][k] = mfma_fp8(P[1], f, O[1][k]);
+      } else {
+        Sc[0][k - NM] = mfma_fp8(f, qf[0], zero4);
+        Sc[1][k - NM] = mfma_fp8(f, qf[1], zero4);
+      }
+    });
+    // issue order: the first two fragments' reads, the row sums, then per
+    // fragment k the reads of k + 2 and the two products of k
+    if constexpr (K0 < K1) {
+      __builtin_amdgcn_sched_group_barrier(0x100, nds(K0) + (K0 + 1 < K1 ? nds(K0 + 1) : 0), 0);
+      if constexpr (PV) __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      static_for<K0, K1>([&](auto kk) {
+        constexpr int k = decltype(kk)::value;
+        if constexpr (k + 2 < K1) __builtin_amdgcn_sched_group_barrier(0x100, nds(k + 2), 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      });
+    }
+    if constexpr (PV) {
+      const int i = j - 1;
+      const int slot = i & 7;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        Lq[s] += rr[s];
+        if (VS) {
+          if (slot == 2 * g) rb[s][0] = rr[s];
+          if (slot == 2 * g + 1) rb[s][1] = rr[s];
+        }
+      }
+      // V-Smooth mean restoration for the 8-tile window ending at tile i:
+      // K slots (g, 4j + e) carry tile 2g + j of the window with
+      // (r_hi, r_lo, r_hi, 0) x (mu_hi, mu_hi, mu_lo, 0)
+      if (VS && (slot == 7 || i == n - 1)) {
+        v8bf Ar[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const __bf16 hi = (__bf16)rb[s][jj];
+            const __bf16 lo = (__bf16)(rb[s][jj] - (float)hi);
+            Ar[s][4 * jj + 0] = hi;
+            Ar[s][4 * jj + 1] = lo;
+            Ar[s][4 * jj + 2] = hi;
+            Ar[s][4 * jj + 3] = (__bf16)0.0f;
+            rb[s][jj] = 0.f;
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          v8bf Bm;
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            // window slot 2g + jj is visit i - slot + 2g + jj; slots past i
+            // hold zero row sums, so whatever finite row the ring holds there
+            // adds nothing
+            const float mvv = mring[(i - slot + 2 * g + jj) & (MR - 1)][16 * m + lr];
+            const __bf16 hi = (__bf16)mvv;
+            const __bf16 lo = (__bf16)(mvv - (float)hi);
+            Bm[4 * jj + 0] = hi;
+            Bm[4 * jj + 1] = hi;
+            Bm[4 * jj + 2] = lo;
+            Bm[4 * jj + 3] = (__bf16)0.0f;
+          }
+          O[0][m] = mfma_bf16(Ar[0], Bm, O[0][m]);
+          O[1][m] = mfma_bf16(Ar[1], Bm, O[1][m]);
+        }
+      }
+    }
+  };
+
+  // ---- V phase: running max, rescale, codes of tile j; half B then issues
+  // the copies of K_{j+3} and V_{j+2} into the stages M(j) last read ----
+  auto vphase = [&](int j, uint8_t* Kdst, uint8_t* Vdst, bool tail) {
+    const int t = tile_at(j);
+    if (tail) {
       const int lim = S - t * kBlk;  // valid keys in this tile
 #pragma unroll
       for (int t8 = 0; t8 < 8; ++t8)
@@ -198,11 +392,8 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
             Sc[1][t8][v] = -INFINITY;
           }
     }
-
-    // ---- running max, rescale, codes ---------------------------------------
-    const float gk = c2 * ksb[t];
+    const float gk = c2 * ksv;
     const float a8 = 8.0f * gk;
-    v8i P[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       float mx = __builtin_fmaxf(Sc[s][0][0], Sc[s][0][1]);
@@ -238,104 +429,87 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
         P[s][t8] = (int)wd;
       }
     }
-
-    // ---- A += P V -------------------------------------------------------------
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      v8i vf = vfrag<D>(Vt, m, fb);
-      O[0][m] = mfma_fp8(P[0], vf, O[0][m]);
-      O[1][m] = mfma_fp8(P[1], vf, O[1][m]);
-    }
-    // ---- row sums over the same bytes: ones x P^T puts query lr's sum in
-    // every register of lane l (the layout of M, alpha and the mean MFMA) ----
-    const int slot = i & 7;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const float r = mfma_fp8(ones, P[s], zero4)[0];
-      Lq[s] += r;
-      if (VS) {
-        if (slot == 2 * g) rb[s][0] = r;
-        if (slot == 2 * g + 1) rb[s][1] = r;
-      }
-    }
-    // ---- V-Smooth mean restoration, A += sum_t r_t mu_t^T, for 8 tiles at a
-    // time on the bf16 matrix cores: K slots (g, 4j + e) carry tile 2g + j of
-    // the window with (r_hi, r_lo, r_hi, 0) x (mu_hi, mu_hi, mu_lo, 0) ----
-    if (VS && (slot == 7 || i == nblk - 1)) {
-      v8bf Ar[2];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const __bf16 hi = (__bf16)rb[s][j];
-          const __bf16 lo = (__bf16)(rb[s][j] - (float)hi);
-          Ar[s][4 * j + 0] = hi;
-          Ar[s][4 * j + 1] = lo;
-          Ar[s][4 * j + 2] = hi;
-          Ar[s][4 * j + 3] = (__bf16)0.0f;
-          rb[s][j] = 0.f;
-        }
-      }
-      const int i0 = i - slot;  // visit index of window slot 0
-      const float* mut[2];
-      bool okj[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int iv = i0 + 2 * g + j;
-        okj[j] = iv <= i;
-        mut[j] = mu + ((int64_t)bh * nblk + tile_at(okj[j] ? iv : i)) * D;
-      }
-#pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        v8bf Bm;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const float mv = okj[j] ? mut[j][16 * m + lr] : 0.0f;
-          const __bf16 hi = (__bf16)mv;
-          const __bf16 lo = (__bf16)(mv - (float)hi);
-          Bm[4 * j + 0] = hi;
-          Bm[4 * j + 1] = hi;
-          Bm[4 * j + 2] = lo;
-          Bm[4 * j + 3] = (__bf16)0.0f;
-        }
-        O[0][m] = mfma_bf16(Ar[0], Bm, O[0][m]);
-        O[1][m] = mfma_bf16(Ar[1], Bm, O[1][m]);
-      }
+    // the next tile's key scale, a whole phase before it is needed
+    if (j + 1 < n) ksv = ksb[tile_at(j + 1)];
+    if (hb) {
+      if (j + 2 < n) issue_mu(j + 2);
+      if (j + 3 < n) issue_k(Kdst, j + 3);
+      if (j + 2 < n) issue_v(Vdst, j + 2);
     }
   };
 
-  // The ragged last key tile is visited either first (mid-window start
-  // clamped to the last block) or last; peel it so the loop body is unmasked.
-  const bool tail_first = ragged && tile_at(0) == nblk - 1;
-  const bool tail_last = ragged && !tail_first;
-  int i0 = 0, i1 = nblk;
-  if (tail_first) {
-    tile_body(0, lds0, lds1, std::true_type{});
-    i0 = 1;
-  }
-  if (tail_last) i1 = nblk - 1;
-  // unrolled by two so each buffer is a fixed LDS object in each half
-  int i = i0;
-  if (i & 1) {
-    if (i < i1) tile_body(i, lds1, lds0, std::false_type{});
-    ++i;
-  }
-  for (; i + 1 < i1; i += 2) {
-    tile_body(i, lds0, lds1, std::false_type{});
-    tile_body(i + 1, lds1, lds0, std::false_type{});
-  }
-  if (i < i1) {
-    tile_body(i, lds0, lds1, std::false_type{});
-    ++i;
-  }
-  if (tail_last) {
-    if ((nblk - 1) & 1)
-      tile_body(nblk - 1, lds1, lds0, std::true_type{});
-    else
-      tile_body(nblk - 1, lds0, lds1, std::true_type{});
+  // end of an M phase in half B: the copies issued one V phase earlier may
+  // stay in flight, every older copy must have landed (the next phase of
+  // half A reads it)
+  auto mwait = [&](int j) {
+    if (hb) {
+      if (j + 2 < n)
+        wait_vm_n<GRP>();
+      else
+        wait_vm();
+    }
+  };
+
+  phase_sync();  // prologue copies visible
+  // half B: one phase behind; it issues K_2 and V_1 in this slot
+  if (hb) {
+    if (1 < n) issue_mu(1);
+    if (2 < n) issue_k(kst2, 2);
+    if (1 < n) issue_v(vst1, 1);
+    phase_sync();
   }
 
+  // j = 0 (may be the ragged tile; no P.V yet)
+  mphase(0, kst0, vst2, std::false_type{}, std::true_type{});
+  mwait(0);
+  phase_sync();
+  vphase(0, kst0, vst2, tail_first);
+  phase_sync();
+
+  // steady state, j = 1 .. n - 2: stages fixed per unrolled copy (j mod 3)
+  int j = 1;
+  while (true) {
+    if (j >= n - 1) break;
+    mphase(j, kst1, vst0, std::true_type{}, std::true_type{});
+    mwait(j);
+    phase_sync();
+    vphase(j, kst1, vst0, false);
+    phase_sync();
+    ++j;
+    if (j >= n - 1) break;
+    mphase(j, kst2, vst1, std::true_type{}, std::true_type{});
+    mwait(j);
+    phase_sync();
+    vphase(j, kst2, vst1, false);
+    phase_sync();
+    ++j;
+    if (j >= n - 1) break;
+    mphase(j, kst0, vst2, std::true_type{}, std::true_type{});
+    mwait(j);
+    phase_sync();
+    vphase(j, kst0, vst2, false);
+    phase_sync();
+    ++j;
+  }
+  // j = n - 1 (may be the ragged tile); stages chosen at run time
+  const int cl = (n - 1) % 3;
+  uint8_t* const Kl = cl == 0 ? kst0 : (cl == 1 ? kst1 : kst2);
+  uint8_t* const Vp = cl == 0 ? vst2 : (cl == 1 ? vst0 : vst1);  // V_{n-2}
+  uint8_t* const Vl = cl == 0 ? vst0 : (cl == 1 ? vst1 : vst2);  // V_{n-1}
+  if (n >= 2) {
+    mphase(n - 1, Kl, Vp, std::true_type{}, std::true_type{});
+    mwait(n - 1);
+    phase_sync();
+    vphase(n - 1, Kl, Vp, tail_last);
+    phase_sync();
+  }
+  // M(n): the last P.V
+  mphase(n, nullptr, Vl, std::true_type{}, std::false_type{});
+  if (!hb) phase_sync();  // half A's extra barrier, matching half B's first
+  if (hb) wait_vm();      // no copy may outlive the workgroup's LDS
+
   // ---- epilogue: O = (A / l) * s_V, bf16, original query order -----------
+  if (!live) return;
   const int b = bh / H, h = bh % H;
   const float* vsb = v_scale + (int64_t)bh * D;
   uint16_t* ob = o + b * oB + h * oH;
@@ -343,7 +517,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int q = qt * kBlk + 32 * w + 16 * s + 4 * g + v;
+      const int q = qt * kBlk + 32 * wq + 16 * s + 4 * g + v;
       const float lsum = __shfl(Lq[s], 4 * g + v);
       if (q >= S) continue;
       const float inv = 1.0f / lsum;
@@ -360,9 +534,10 @@ hipError_t launch_t(const vc_shape& sh, float c1, int window, int seq, const uin
                     const uint8_t* k8, const float* ks, const uint8_t* v8, const float* vs, const float* mu,
                     BshdOut o, hipStream_t st) {
   const int nblk = (sh.S + kBlk - 1) / kBlk;
-  const int64_t n = (int64_t)nblk * sh.H * sh.B;
-  attn_fp8_kernel<D, VS><<<(unsigned)n, 256, 0, st>>>(q8, qs, k8, ks, v8, vs, mu, o.p, o.sB, o.sS, o.sH, sh.S, sh.H,
-                                                       nblk, c1, window, seq);
+  const int npair = (nblk + 1) / 2;
+  const int64_t n = (int64_t)npair * sh.H * sh.B;
+  attn_fp8_kernel<D, VS><<<(unsigned)n, 512, 0, st>>>(q8, qs, k8, ks, v8, vs, mu, o.p, o.sB, o.sS, o.sH, sh.S,
+                                                          sh.H, nblk, npair, c1, window, seq);
   return hipGetLastError();
 }
 

@@ -177,7 +177,11 @@ typedef struct vc_attn_params {
  * "Mid-window key traversal".
  *
  * For each query row i (tile qt = i / 128) and key block t in the order
- *   start = min(qt + window, nblk - 1): start, start-1, ..., 0, start+1, ...,
+ *   start = min((qt | 1) + window, nblk - 1): start, start-1, ..., 0,
+ *   start+1, ..., nblk-1
+ * (query tiles 2p and 2p+1 are processed together and share one pass over
+ * K/V -- [OVC] "A warp-specialized pipeline" -- so the start lies `window`
+ * blocks past the pair's second diagonal block),
  * acc = FP8 dot products (matrix cores, fp32 accumulate);
  * g = fl(fl(sm_scale * log2 e) * q_scale[qt]) * k_scale[t];
  * M' = max(M, g * max acc); when M' > M the numerator and denominator are

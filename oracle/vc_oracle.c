@@ -388,13 +388,19 @@ EXPORT void vco_smooth_apply(const uint16_t* k, int64_t ldk, const uint16_t* v, 
 /*  - mid-window key order: [OVC] "Mid-window key traversal".               */
 /* ------------------------------------------------------------------------ */
 
-/* Visit order of the key blocks for query tile qt. */
+/* Visit order of the key blocks for query tile qt.  The kernel holds two    */
+/* 128-row query tiles, 2p and 2p + 1, that share one pass over K/V ([OVC] */
+/* "A warp-specialized pipeline"), so the mid-window start is taken past   */
+/* the pair's diagonal: start = min((qt | 1) + window, nblk - 1), then     */
+/* down to block 0, then the blocks after start ([OVC] "Mid-window key     */
+/* traversal").                                                            */
 EXPORT void vco_tile_order(int32_t qt, int32_t nblk, int32_t window, int32_t sequential, int32_t* order) {
   if (sequential) {
     for (int32_t i = 0; i < nblk; ++i) order[i] = i;
     return;
   }
-  int32_t start = qt + window < nblk - 1 ? qt + window : nblk - 1;
+  int32_t last = qt | 1; /* diagonal block of the pair's second tile */
+  int32_t start = last + window < nblk - 1 ? last + window : nblk - 1;
   int32_t n = 0;
   for (int32_t t = start; t >= 0; --t) order[n++] = t;
   for (int32_t t = start + 1; t < nblk; ++t) order[n++] = t;

@@ -81,15 +81,24 @@ def test_exact_special_cases():
 # --------------------------------------------------------------------------- #
 
 def test_tile_order_mid_window():
-    assert list(oracle.tile_order(0, 5, 2)) == [2, 1, 0, 3, 4]
+    # query tiles 2p and 2p + 1 share one order, started `window` blocks past
+    # the pair's second diagonal block
+    assert list(oracle.tile_order(0, 5, 2)) == [3, 2, 1, 0, 4]
+    assert list(oracle.tile_order(1, 5, 2)) == [3, 2, 1, 0, 4]
     assert list(oracle.tile_order(1, 6, 2)) == [3, 2, 1, 0, 4, 5]
     assert list(oracle.tile_order(4, 5, 2)) == [4, 3, 2, 1, 0]
-    assert list(oracle.tile_order(2, 5, 0)) == [2, 1, 0, 3, 4]
+    assert list(oracle.tile_order(2, 5, 0)) == [3, 2, 1, 0, 4]
+    assert list(oracle.tile_order(2, 6, 1)) == [4, 3, 2, 1, 0, 5]
     assert list(oracle.tile_order(3, 5, 2, sequential=True)) == [0, 1, 2, 3, 4]
+    assert list(oracle.tile_order(0, 1, 2)) == [0]
     for qt in range(30):
         o = oracle.tile_order(qt, 30, 3)
         assert sorted(o) == list(range(30))  # every block exactly once
-        assert o[0] == min(qt + 3, 29)
+        assert o[0] == min(2 * (qt // 2) + 1 + 3, 29)
+        # down from the start to block 0, then upwards
+        k = list(o).index(0)
+        assert list(o[:k + 1]) == list(range(o[0], -1, -1))
+        assert list(o[k + 1:]) == list(range(o[0] + 1, 30))
 
 
 # --------------------------------------------------------------------------- #
