@@ -275,7 +275,12 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
   float ksv = ksb[tile_at(0)];                // key scale of the current tile
   v8i P[2];                                   // codes of the previous tile
 
-  // ---- M phase: row sums of P_{j-1}, P_{j-1} V_{j-1}, then S_j^T = K_j Q^T.
+  // ---- M phase: row sums of P_{j-1}, A^T += V_{j-1}^T P_{j-1}^T, then
+  // S_j^T = K_j Q^T.  The output is accumulated transposed: the V fragment is
+  // the A operand and the codes the B operand, so lane (g, lr) holds channels
+  // 16m + 4g + v of query lr -- the query whose max, rescale factor and
+  // denominator the lane already holds from S^T, so a rescale needs no
+  // cross-lane movement.
   // Fragment k of a phase is V channel block k (k < NM), then K key block
   // k - NM; each is read from LDS two MFMA pairs ahead of its use, so the LDS
   // latency hides behind matrix-core work.  PV / QK are std::true_type or
@@ -307,8 +312,8 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
       if constexpr (k + 2 < K1) fr[(k + 2) % 3] = frag(std::integral_constant<int, k + 2>{});
       const v8i f = fr[k % 3];
       if constexpr (k < NM) {
-        O[0][k] = mfma_fp8(P[0], f, O[0][k]);
-        O[1][k] = mfma_fp8(P[1], f, O[1][k]);
+        O[0][k] = mfma_fp8(f, P[0], O[0][k]);
+        O[1][k] = mfma_fp8(f, P[1], O[1][k]);
       } else {
         Sc[0][k - NM] = mfma_fp8(f, qf[0], zero4);
         Sc[1][k - NM] = mfma_fp8(f, qf[1], zero4);
@@ -370,8 +375,8 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
             Bm[4 * jj + 2] = lo;
             Bm[4 * jj + 3] = (__bf16)0.0f;
           }
-          O[0][m] = mfma_bf16(Ar[0], Bm, O[0][m]);
-          O[1][m] = mfma_bf16(Ar[1], Bm, O[1][m]);
+          O[0][m] = mfma_bf16(Bm, Ar[0], O[0][m]);
+          O[1][m] = mfma_bf16(Bm, Ar[1], O[1][m]);
         }
       }
     }
@@ -409,13 +414,11 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
           rb[s][0] *= alpha;
           rb[s][1] *= alpha;
         }
-        float a4[4];
+        // whole-vector multiplies (lane-wise: alpha is the lane's own query);
+        // per-element updates led the register allocator to keep two copies
+        // of the accumulators and spill
 #pragma unroll
-        for (int v = 0; v < 4; ++v) a4[v] = __shfl(alpha, 4 * g + v);
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-#pragma unroll
-          for (int m = 0; m < NM; ++m) O[s][m][v] *= a4[v];
+        for (int m = 0; m < NM; ++m) O[s][m] = O[s][m] * alpha;
         M[s] = Mn;
       }
       const float bb = 119.65f - 8.0f * M[s];
@@ -513,20 +516,21 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
   const int b = bh / H, h = bh % H;
   const float* vsb = v_scale + (int64_t)bh * D;
   uint16_t* ob = o + b * oB + h * oH;
+  // lane (g, lr) holds query lr of each sub-tile, channels 16m + 4g + v
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
+  for (int s = 0; s < 2; ++s) {
+    const int q = qt * kBlk + 32 * wq + 16 * s + lr;
+    if (q >= S) continue;
+    const float inv = 1.0f / Lq[s];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int q = qt * kBlk + 32 * wq + 16 * s + 4 * g + v;
-      const float lsum = __shfl(Lq[s], 4 * g + v);
-      if (q >= S) continue;
-      const float inv = 1.0f / lsum;
-#pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        const int d = 16 * m + lr;
-        ob[(int64_t)q * oS + d] = f32_to_bf16((O[s][m][v] * inv) * vsb[d]);
-      }
+    for (int m = 0; m < NM; ++m) {
+      const int d = 16 * m + 4 * g;
+      const float4 sv = *(const float4*)(vsb + d);
+      const u32 lo = (u32)f32_to_bf16((O[s][m][0] * inv) * sv.x) | ((u32)f32_to_bf16((O[s][m][1] * inv) * sv.y) << 16);
+      const u32 hi = (u32)f32_to_bf16((O[s][m][2] * inv) * sv.z) | ((u32)f32_to_bf16((O[s][m][3] * inv) * sv.w) << 16);
+      *(uint2*)(ob + (int64_t)q * oS + d) = make_uint2(lo, hi);
     }
+  }
 }
 
 template <int D, bool VS>
