@@ -9,7 +9,8 @@ no GPU is present, calls fail loudly.
 
 Entry points (same names as the C ABI): vc_abi_version, vc_status_str,
 vc_quantize, vc_smooth_group_workspace_size, vc_smooth_group, vc_attn_fwd,
-vc_pack_v_bf16, vc_attn_fwd_bf16, vc_expcast_codes.
+vc_pack_v_bf16, vc_attn_fwd_bf16, vc_expcast_codes; and vsmooth_schedule, the
+host-side rule for which denoising steps group, reuse or run plain.
 """
 from __future__ import annotations
 
@@ -25,6 +26,8 @@ _lib = None
 
 VC_OK = 0
 VC_ATTN_SEQUENTIAL = 1
+VC_GROUP_WARM_START = 1
+VC_GROUP_REUSE_PERM = 2
 ABI_VERSION = 1
 
 
@@ -166,17 +169,41 @@ def vc_smooth_group_workspace_size(B: int, H: int, S: int, D: int, clusters: int
     return int(lib().vc_smooth_group_workspace_size(ctypes.byref(sh), clusters))
 
 
-def vc_smooth_group(k, v, clusters: int, iters: int, seed: int, *, workspace=None, out=None):
+def vc_smooth_group(k, v, clusters: int, iters: int, seed: int, *, workspace=None, out=None, warm_start=None,
+                    reuse_perm=None):
     """V-Smooth grouping.  k, v: bf16 [B,S,H,D].  Returns dict with centroids,
-    labels, perm, k8, k_scale, r8, r_scale, mu_bf16, mu_scaled."""
+    labels, perm, k8, k_scale, r8, r_scale, mu_bf16, mu_scaled.
+
+    warm_start: fp32 [B,H,clusters,D] centroids to start k-means from
+    (VC_GROUP_WARM_START); it is copied into the returned centroids.
+    reuse_perm: int32 [B,H,S] permutation of an earlier call
+    (VC_GROUP_REUSE_PERM): no k-means, no sort; only the gather, block means
+    and residual codes run on k, v; centroids and labels are not produced."""
+    if warm_start is not None and reuse_perm is not None:
+        raise ValueError("warm_start and reuse_perm exclude each other")
     sh = _shape_of(v)
     B, H, S, D = sh.B, sh.H, sh.S, sh.D
     nb = nblk_of(S)
     dev = v.device
     o = dict(out or {})
-    o.setdefault("centroids", torch.empty((B, H, clusters, D), dtype=torch.float32, device=dev))
-    o.setdefault("labels", torch.empty((B, H, S), dtype=torch.int32, device=dev))
-    o.setdefault("perm", torch.empty((B, H, S), dtype=torch.int32, device=dev))
+    flags = 0
+    if reuse_perm is None:
+        o.setdefault("centroids", torch.empty((B, H, clusters, D), dtype=torch.float32, device=dev))
+        o.setdefault("labels", torch.empty((B, H, S), dtype=torch.int32, device=dev))
+        o.setdefault("perm", torch.empty((B, H, S), dtype=torch.int32, device=dev))
+        if warm_start is not None:
+            if tuple(warm_start.shape) != (B, H, clusters, D) or warm_start.dtype != torch.float32:
+                raise ValueError("warm_start must be fp32 [B,H,clusters,D]")
+            if warm_start.data_ptr() != o["centroids"].data_ptr():
+                o["centroids"].copy_(warm_start)
+            flags = VC_GROUP_WARM_START
+    else:
+        if tuple(reuse_perm.shape) != (B, H, S) or reuse_perm.dtype != torch.int32 or not reuse_perm.is_contiguous():
+            raise ValueError("reuse_perm must be contiguous int32 [B,H,S]")
+        o["perm"] = reuse_perm
+        o.pop("centroids", None)
+        o.pop("labels", None)
+        flags = VC_GROUP_REUSE_PERM
     o.setdefault("k8", torch.empty((B, H, nb * 128, D), dtype=torch.uint8, device=dev))
     o.setdefault("k_scale", torch.empty((B, H, nb), dtype=torch.float32, device=dev))
     o.setdefault("r8", torch.empty((B, H, D, nb * 128), dtype=torch.uint8, device=dev))
@@ -186,15 +213,29 @@ def vc_smooth_group(k, v, clusters: int, iters: int, seed: int, *, workspace=Non
     wsb = vc_smooth_group_workspace_size(B, H, S, D, clusters)
     if workspace is None:
         workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
-    p = vc_group_params(clusters, iters, seed, 0)
+    p = vc_group_params(clusters, iters, seed, flags)
     kd, vd = _bshd(k), _bshd(v)
     st = lib().vc_smooth_group(ctypes.byref(sh), ctypes.byref(kd), ctypes.byref(vd), ctypes.byref(p),
-                               _ptr(o["centroids"]), _ptr(o["labels"]), _ptr(o["perm"]), _ptr(o["k8"]),
+                               _ptr(o.get("centroids")), _ptr(o.get("labels")), _ptr(o["perm"]), _ptr(o["k8"]),
                                _ptr(o["k_scale"]), _ptr(o["r8"]), _ptr(o["r_scale"]), _ptr(o["mu_bf16"]),
                                _ptr(o["mu_scaled"]), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                _stream())
     _check(st, "vc_smooth_group")
     return o
+
+
+def vsmooth_schedule(n_steps: int, step: int, reuse: int = 4) -> str:
+    """What the V-Smooth schedule does at denoising step `step` of `n_steps`
+    ([VC] §3.4 and Appendix A): grouping and demeaning run on the first
+    ceil(n_steps / 4) steps; inside that window the permutation is computed
+    at every `reuse`-th step ("group") and reused in between ("reuse"); the
+    later steps run plain FP8 ExpCast attention ("plain")."""
+    if n_steps < 1 or not 0 <= step < n_steps or reuse < 1:
+        raise ValueError("need n_steps >= 1, 0 <= step < n_steps, reuse >= 1")
+    window = -(-n_steps // 4)
+    if step >= window:
+        return "plain"
+    return "group" if step % reuse == 0 else "reuse"
 
 
 # --------------------------------------------------------------------------- #

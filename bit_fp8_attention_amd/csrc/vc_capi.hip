@@ -102,9 +102,12 @@ __attribute__((visibility("default"))) int32_t vc_smooth_group(
   if (e) return e;
   if ((e = check_bshd(k)) || (e = check_bshd(v))) return e;
   if (!p) return VC_ERR_NULL;
-  if (!centroids || !labels || !perm || !k8 || !k_scale || !r8 || !r_scale || !mu_bf16 || !mu_scaled || !workspace)
+  if (p->flags & ~(VC_GROUP_WARM_START | VC_GROUP_REUSE_PERM)) return VC_ERR_UNSUPPORTED;
+  if ((p->flags & VC_GROUP_WARM_START) && (p->flags & VC_GROUP_REUSE_PERM)) return VC_ERR_UNSUPPORTED;
+  const bool reuse = (p->flags & VC_GROUP_REUSE_PERM) != 0;
+  if ((!reuse && (!centroids || !labels)) || !perm || !k8 || !k_scale || !r8 || !r_scale || !mu_bf16 ||
+      !mu_scaled || !workspace)
     return VC_ERR_NULL;
-  if (p->flags != 0) return VC_ERR_UNSUPPORTED;
   const int kmax = 8192 / sh->D;
   if (p->clusters < 1 || p->clusters > kmax || p->clusters > sh->S) return VC_ERR_UNSUPPORTED;
   if (p->iters < 1 || p->iters > 64) return VC_ERR_UNSUPPORTED;

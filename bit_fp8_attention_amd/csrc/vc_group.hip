@@ -74,12 +74,25 @@ VC_DEV float fx24_mean(long long s, long long n) {
 // Forgy initialisation, centroids, norms; zero the accumulators.
 template <int D>
 __global__ __launch_bounds__(256) void group_init(const uint16_t* __restrict__ v, int64_t sB, int64_t sS, int64_t sH,
-                                                  int S, int H, int k, uint64_t seed, float* __restrict__ cent,
-                                                  GroupWs ws) {
+                                                  int S, int H, int k, uint64_t seed, int warm,
+                                                  float* __restrict__ cent, GroupWs ws) {
   __shared__ int mpos[512], mval[512];
   __shared__ int idx[256];
   const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const int64_t bh = (int64_t)b * H + h;
+  if (warm) {
+    // warm start: the caller's centroids are the first iterate
+    float* cb = cent + bh * k * D;
+    for (int e = t; e < k * D; e += 256) ws.sums[bh * k * D + e] = 0;
+    for (int e = t; e < k; e += 256) ws.counts[bh * k + e] = 0;
+    for (int e = t; e < D; e += 256) ws.r_amax[bh * D + e] = 0u;
+    for (int c = t; c < k; c += 256) {
+      float n2 = 0.0f;
+      for (int d = 0; d < D; ++d) n2 = __builtin_fmaf(cb[c * D + d], cb[c * D + d], n2);
+      ws.norms[bh * k + c] = n2;
+    }
+    return;
+  }
   if (t == 0) {
     // partial Fisher-Yates over the identity [0, S), the touched positions
     // kept in a small map (position -> value)
@@ -120,6 +133,13 @@ __global__ __launch_bounds__(256) void group_init(const uint16_t* __restrict__ v
     }
     ws.norms[bh * k + c] = n2;
   }
+}
+
+// Zeroes the per-channel residual amax of each (b, h): the only state the
+// gather/means/residual passes need when the permutation is given.
+__global__ __launch_bounds__(256) void amax_reset(int D, GroupWs ws) {
+  const int64_t bh = blockIdx.x;
+  for (int e = threadIdx.x; e < D; e += 256) ws.r_amax[bh * D + e] = 0u;
 }
 
 // Assignment of kAssignTokens tokens, member sums accumulated in LDS and
@@ -482,15 +502,21 @@ hipError_t launch_group_t(const vc_shape& sh, Bshd k, Bshd v, const vc_group_par
   const int S = sh.S, H = sh.H, B = sh.B, kc = p.clusters;
   const int nblk = (S + kBlk - 1) / kBlk, nchunk = (S + kChunk - 1) / kChunk;
   const int BH = B * H;
-  group_init<D><<<dim3(H, B), 256, 0, st>>>(v.p, v.sB, v.sS, v.sH, S, H, kc, p.seed, cent, ws);
-  const dim3 ga((S + kAssignTokens - 1) / kAssignTokens, H, B);
-  for (int it = 0; it < p.iters; ++it) {
-    kmeans_assign<D><<<ga, 256, 0, st>>>(v.p, v.sB, v.sS, v.sH, S, H, kc, cent, labels, ws);
-    kmeans_update<D><<<BH, 256, 0, st>>>(kc, cent, ws);
+  if (p.flags & VC_GROUP_REUSE_PERM) {
+    // the caller's permutation: only the gather, block means and residual codes
+    amax_reset<<<BH, 256, 0, st>>>(D, ws);
+  } else {
+    group_init<D><<<dim3(H, B), 256, 0, st>>>(v.p, v.sB, v.sS, v.sH, S, H, kc, p.seed,
+                                              (p.flags & VC_GROUP_WARM_START) ? 1 : 0, cent, ws);
+    const dim3 ga((S + kAssignTokens - 1) / kAssignTokens, H, B);
+    for (int it = 0; it < p.iters; ++it) {
+      kmeans_assign<D><<<ga, 256, 0, st>>>(v.p, v.sB, v.sS, v.sH, S, H, kc, cent, labels, ws);
+      kmeans_update<D><<<BH, 256, 0, st>>>(kc, cent, ws);
+    }
+    label_hist<<<dim3(nchunk, H, B), 256, 0, st>>>(labels, S, H, kc, nchunk, ws);
+    hist_scan<<<BH, 1024, 0, st>>>(kc, nchunk, ws);
+    label_scatter<<<dim3(nchunk, H, B), 256, 0, st>>>(labels, S, H, kc, nchunk, ws, perm);
   }
-  label_hist<<<dim3(nchunk, H, B), 256, 0, st>>>(labels, S, H, kc, nchunk, ws);
-  hist_scan<<<BH, 1024, 0, st>>>(kc, nchunk, ws);
-  label_scatter<<<dim3(nchunk, H, B), 256, 0, st>>>(labels, S, H, kc, nchunk, ws, perm);
   group_apply1<D><<<dim3(nblk, H, B), 256, 0, st>>>(k.p, k.sB, k.sS, k.sH, v.p, v.sB, v.sS, v.sH, S, H, nblk, perm,
                                                     k8, k_scale, mu_bf16, ws);
   group_apply2<D><<<dim3(nblk, H, B), 256, 0, st>>>(v.p, v.sB, v.sS, v.sH, S, H, nblk, perm, mu_bf16, ws, r8,

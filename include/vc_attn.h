@@ -118,8 +118,20 @@ typedef struct vc_group_params {
   int32_t clusters; /* k in [1, min(S, 8192 / D)] */
   int32_t iters;    /* Lloyd iterations, [1, 64] */
   uint64_t seed;    /* seeds the Forgy initialisation */
-  uint32_t flags;   /* must be 0 */
+  uint32_t flags;   /* 0, VC_GROUP_WARM_START or VC_GROUP_REUSE_PERM */
 } vc_group_params;
+
+/* Warm start ([VC] §3.2, "Unbalanced clusters cost little": each step starts
+ * from the previous step's centroids): `centroids` is read as the first
+ * iterate instead of the Forgy draw, then overwritten with the result; the
+ * seed is unused. */
+#define VC_GROUP_WARM_START 1u
+/* Permutation reuse ([VC] §3.4 and Appendix A: pi is computed once and
+ * reused for the following steps of the window): no k-means and no sort;
+ * `perm` is read (a permutation of [0, S) per (b, h)) and only step 3 runs
+ * on the given K, V.  `centroids` and `labels` are not touched and may be
+ * NULL; `clusters` and `iters` are not used but must still be valid. */
+#define VC_GROUP_REUSE_PERM 2u
 
 /* Bytes of device workspace vc_smooth_group needs for this shape. */
 size_t vc_smooth_group_workspace_size(const vc_shape* shape, int32_t clusters);
@@ -144,6 +156,9 @@ size_t vc_smooth_group_workspace_size(const vc_shape* shape, int32_t clusters);
  *     R = V' - 1 mu_j^T in fp32; per-channel s_R[d] = amax_d |R| / 448;
  *     r8 = E4M3_rne(R * (448 / amax_d)); mu_scaled[j][d] = mu_j[d] * (448 /
  *     amax_d) in fp32.  K' is quantised per 128-row block as in vc_quantize.
+ * With VC_GROUP_WARM_START, step 1 starts from the given centroids; with
+ * VC_GROUP_REUSE_PERM, steps 1 and 2 are skipped and perm is an input.  The
+ * two flags exclude each other (VC_ERR_UNSUPPORTED).
  * Outputs (all device, caller-owned):
  *   centroids fp32 [B][H][clusters][D]; labels, perm int32 [B][H][S];
  *   k8 packed K, k_scale fp32 [B][H][nblk];

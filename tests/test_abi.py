@@ -104,7 +104,15 @@ def test_smooth_group_validation(vc):
     assert call(m.vc_group_params(0, 4, 0, 0)) == 4       # k < 1
     assert call(m.vc_group_params(65, 4, 0, 0)) == 4      # k > 8192 / D
     assert call(m.vc_group_params(64, 0, 0, 0)) == 4      # iters < 1
-    assert call(m.vc_group_params(64, 4, 0, 1)) == 4      # unknown flag
+    assert call(m.vc_group_params(64, 4, 0, 4)) == 4      # unknown flag
+    assert call(m.vc_group_params(64, 4, 0, 3)) == 4      # warm start and permutation reuse together
+
+    def call_ptrs(p, ptrs):
+        return L.vc_smooth_group(ctypes.byref(sh), ctypes.byref(ok), ctypes.byref(ok), ctypes.byref(p),
+                                 *[P(x) for x in ptrs], P(FAKE), ws, st)
+    no_perm = [FAKE, FAKE, None] + [FAKE] * 6
+    assert call_ptrs(m.vc_group_params(64, 4, 0, 2), no_perm) == 1      # reuse needs perm
+    assert call_ptrs(m.vc_group_params(64, 4, 0, 1), [None] + [FAKE] * 8) == 1  # warm start needs centroids
     assert call(m.vc_group_params(64, 4, 0, 0), wsb=ws - 1) == 5
     assert call(m.vc_group_params(64, 4, 0, 0), ws_ptr=FAKE + 16) == 3
     small = m.vc_shape(1, 1, 10, 128)

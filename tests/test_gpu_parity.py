@@ -212,6 +212,74 @@ def test_smooth_group_video_bitexact(vc):
     _group_case(vc, k, v, 64, 4, 1002)
 
 
+def _next_step(x, seed, sigma=0.05):
+    """bf16 activations of a following denoising step: x plus small noise."""
+    g = torch.Generator().manual_seed(seed)
+    return (x.float() + sigma * torch.randn(x.shape, generator=g)).to(torch.bfloat16)
+
+
+def _apply_matches(g, ref, b, h, D):
+    assert (unpack_k(_np(g["k8"][b, h]), D) == ref["k_codes"]).all(), ("k8", b, h)
+    assert (_np(g["k_scale"][b, h]) == ref["k_scale"]).all(), ("k_scale", b, h)
+    assert (_np(g["mu_bf16"][b, h]).view(np.uint16) == ref["mu_bf16"]).all(), ("mu", b, h)
+    assert (_np(g["mu_scaled"][b, h]) == ref["mu_scaled"]).all(), ("mu_scaled", b, h)
+    assert (_np(g["r_scale"][b, h]) == ref["r_scale"]).all(), ("r_scale", b, h)
+    assert (unpack_v(_np(g["r8"][b, h]), D) == ref["r_codes"]).all(), ("r8", b, h)
+
+
+@pytest.mark.parametrize("S,H,D,kc,iters", [(1024, 2, 64, 8, 3), (1000, 2, 128, 64, 2)])
+def test_smooth_group_warm_start_bitexact(vc, S, H, D, kc, iters):
+    # step t groups cold; step t+1 (perturbed K, V) starts k-means from step t's centroids
+    print(f"case group warm start S={S} H={H} D={D} k={kc} iters={iters}", flush=True)
+    q, k, v = vcsynth.random_qkv(1, S, H, D, seed=S + 1, v_kind="t3")
+    g1 = vc.vc_smooth_group(k.cuda(), v.cuda(), kc, iters, 5)
+    k2, v2 = _next_step(k, 11), _next_step(v, 12)
+    g2 = vc.vc_smooth_group(k2.cuda(), v2.cuda(), kc, iters, 0, warm_start=g1["centroids"])
+    torch.cuda.synchronize()
+    kb, vb = vcsynth.bf16_bits(k2), vcsynth.bf16_bits(v2)
+    for b in range(1):
+        for h in range(H):
+            init = _np(g1["centroids"][b, h])
+            labels, cent = oracle.kmeans_head(np.ascontiguousarray(vb[b, :, h]), kc, iters, 0, b, h, H, init=init)
+            perm = oracle.argsort_labels(labels, kc)
+            assert (_np(g2["labels"][b, h]) == labels).all(), ("labels", b, h)
+            assert (_np(g2["centroids"][b, h]) == cent).all(), ("centroids", b, h)
+            assert (_np(g2["perm"][b, h]) == perm).all(), ("perm", b, h)
+            ref = oracle.smooth_apply_head(np.ascontiguousarray(kb[b, :, h]), np.ascontiguousarray(vb[b, :, h]), perm)
+            _apply_matches(g2, ref, b, h, D)
+
+
+def test_smooth_group_warm_start_composes_on_gpu(vc):
+    # cold a + b iterations == cold a, then b iterations warm-started from it
+    print("case group warm composition S=2048 H=2 D=128 k=32", flush=True)
+    q, k, v = vcsynth.random_qkv(1, 2048, 2, 128, seed=9, v_kind="t3")
+    kc, vcu = k.cuda(), v.cuda()
+    g_ab = vc.vc_smooth_group(kc, vcu, 32, 3, 42)
+    g_a = vc.vc_smooth_group(kc, vcu, 32, 1, 42)
+    g_w = vc.vc_smooth_group(kc, vcu, 32, 2, 0, warm_start=g_a["centroids"])
+    torch.cuda.synchronize()
+    for key in ("labels", "centroids", "perm", "k8", "r8", "mu_scaled", "r_scale"):
+        assert torch.equal(g_w[key], g_ab[key]), key
+
+
+@pytest.mark.parametrize("S,H,D", [(1024, 2, 64), (1000, 2, 128), (129, 1, 128)])
+def test_smooth_group_reuse_perm_bitexact(vc, S, H, D):
+    # the permutation of step t applied to step t+1's K, V: no k-means, no sort
+    print(f"case group reuse perm S={S} H={H} D={D}", flush=True)
+    q, k, v = vcsynth.random_qkv(1, S, H, D, seed=S + 2, v_kind="t3")
+    kc = min(16, S)
+    g1 = vc.vc_smooth_group(k.cuda(), v.cuda(), kc, 2, 3)
+    k2, v2 = _next_step(k, 21), _next_step(v, 22)
+    g2 = vc.vc_smooth_group(k2.cuda(), v2.cuda(), kc, 2, 3, reuse_perm=g1["perm"])
+    torch.cuda.synchronize()
+    assert "labels" not in g2 and "centroids" not in g2
+    kb, vb = vcsynth.bf16_bits(k2), vcsynth.bf16_bits(v2)
+    for h in range(H):
+        perm = _np(g1["perm"][0, h])
+        ref = oracle.smooth_apply_head(np.ascontiguousarray(kb[0, :, h]), np.ascontiguousarray(vb[0, :, h]), perm)
+        _apply_matches(g2, ref, 0, h, D)
+
+
 # --------------------------------------------------------------------------- #
 # attention, V-Smooth path
 # --------------------------------------------------------------------------- #

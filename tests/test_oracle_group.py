@@ -167,3 +167,21 @@ def test_sorting_raises_the_energy_share_of_the_means():
         return float((128 * (b.mean(1) ** 2).sum(-1)).sum() / (b ** 2).sum())
     seq, srt = share(vf), share(vf[perm])
     assert srt > seq + 0.1, (seq, srt)
+
+
+def test_kmeans_warm_start_continues_a_cold_run():
+    # warm start (VC-Attention paper §3.2, "Unbalanced clusters cost little":
+    # each step starts from the previous step's centroids).  Lloyd iterations
+    # compose: a cold run of a + b iterations equals a cold run of a
+    # iterations followed by b iterations started from its centroids --
+    # labels and centroids bit for bit.
+    for name, S, k, a, b in [("tiny", None, 8, 1, 2), ("longcat", 4096, 64, 2, 2)]:
+        vh = _v_head(name, S=S, H=1)
+        lab_ab, cent_ab = oracle.kmeans_head(vh, k, a + b, 1000, 0, 0, 1)
+        _, cent_a = oracle.kmeans_head(vh, k, a, 1000, 0, 0, 1)
+        lab_w, cent_w = oracle.kmeans_head(vh, k, b, 999, 0, 0, 1, init=cent_a)  # seed unused when warm
+        assert (lab_w == lab_ab).all()
+        assert (cent_w == cent_ab).all()
+        # and the warm start does not reuse the Forgy draw: from other centroids the result differs
+        lab_o, _ = oracle.kmeans_head(vh, k, b, 1000, 0, 0, 1, init=np.roll(cent_a, 1, axis=1))
+        assert not (lab_o == lab_ab).all()
