@@ -110,49 +110,6 @@ VC_DEV v8i vfrag(const uint8_t* vt, int m, const FragBase<D>& fb) {
 // read for the last time in M(j).  A copy has four phases to land.
 // ---------------------------------------------------------------------------
 
-// The same 16-byte global -> LDS copy as lds_dma16 (lane i lands at
-// lds_base + 16 i), issued as inline asm.  The hardware counts these copies
-// on vmcnt only (an outstanding copy does not hold lgkmcnt, measured), but
-// the compiler's wait insertion, seeing one, stops trusting partial lgkmcnt
-// counts and drains every LDS read before its first use.  Hidden from it,
-// the fragment reads get exact partial waits; the kernel orders the copies
-// itself with explicit vmcnt waits and barriers.
-VC_DEV void lds_dma16_raw(const void* g, void* lds_base) {
-  const unsigned lds = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)LDS_PTR(lds_base));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
-}
-
-// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
-template <int B, int E, class F>
-VC_DEV void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
-
-// Barrier between phases: waits for this wave's own LDS reads and scalar
-// loads only.  The copies in flight are waited for by the waves that issued
-// them (a fence here would wait for every outstanding copy).  The barrier
-// is inline asm with a memory clobber so the compiler moves no memory access
-// across it, and the scheduling barriers pin every other instruction.
-VC_DEV void phase_sync() {
-  __builtin_amdgcn_sched_barrier(0);  // no instruction moves across a phase boundary
-  // lgkmcnt(0), vmcnt and expcnt at their maxima; as a builtin, so the
-  // compiler's own wait insertion knows every LDS and scalar load is done
-  __builtin_amdgcn_s_waitcnt(0xc07f);
-  asm volatile("s_barrier" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// s_waitcnt with vmcnt = N, other counters at their maxima (gfx9 encoding:
-// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
-template <int N>
-VC_DEV void wait_vm_n() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
-}
-
 template <int D, bool VS>
 __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ q_scale, const uint8_t* __restrict__ k8,
