@@ -80,7 +80,7 @@ def traffic_job(w):
     a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
     torch.cuda.synchronize()
-    vc.vc_attn_fwd(qz["q8"], qz["q_scale"], g["k8"], g["k_scale"], g["r8"], g["r_scale"], g["mu_scaled"], S=w.S,
+    vc.vc_attn_fwd(qz["q8"], qz["q_scale"], g["k8"], g["k_scale"], g["r8"], g["r_scale"], g["mu_split"], S=w.S,
                    out=o, sm_scale=w.sm_scale)
     b.copy_(a)
     torch.cuda.synchronize()
@@ -235,7 +235,7 @@ def main():
             if e: e[1].record()
             vc.vc_smooth_group(k, v, clusters, iters, w.seed, workspace=ws, out=g)
             if e: e[2].record()
-            vc.vc_attn_fwd(qz["q8"], qz["q_scale"], g["k8"], g["k_scale"], g["r8"], g["r_scale"], g["mu_scaled"],
+            vc.vc_attn_fwd(qz["q8"], qz["q_scale"], g["k8"], g["k_scale"], g["r8"], g["r_scale"], g["mu_split"],
                            S=w.S, out=o, sm_scale=w.sm_scale)
         else:
             vc.vc_quantize(q, k, v, out=qz)

@@ -28,7 +28,7 @@ VC_OK = 0
 VC_ATTN_SEQUENTIAL = 1
 VC_GROUP_WARM_START = 1
 VC_GROUP_REUSE_PERM = 2
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 class VcError(RuntimeError):
@@ -172,7 +172,9 @@ def vc_smooth_group_workspace_size(B: int, H: int, S: int, D: int, clusters: int
 def vc_smooth_group(k, v, clusters: int, iters: int, seed: int, *, workspace=None, out=None, warm_start=None,
                     reuse_perm=None):
     """V-Smooth grouping.  k, v: bf16 [B,S,H,D].  Returns dict with centroids,
-    labels, perm, k8, k_scale, r8, r_scale, mu_bf16, mu_scaled.
+    labels, perm, k8, k_scale, r8, r_scale, mu_bf16, mu_split (int32 storage
+    of the uint32 pairs bf16(m) | bf16(m - bf16(m)) << 16 of each scaled block
+    mean m).
 
     warm_start: fp32 [B,H,clusters,D] centroids to start k-means from
     (VC_GROUP_WARM_START); it is copied into the returned centroids.
@@ -209,7 +211,7 @@ def vc_smooth_group(k, v, clusters: int, iters: int, seed: int, *, workspace=Non
     o.setdefault("r8", torch.empty((B, H, D, nb * 128), dtype=torch.uint8, device=dev))
     o.setdefault("r_scale", torch.empty((B, H, D), dtype=torch.float32, device=dev))
     o.setdefault("mu_bf16", torch.empty((B, H, nb, D), dtype=torch.int16, device=dev))
-    o.setdefault("mu_scaled", torch.empty((B, H, nb, D), dtype=torch.float32, device=dev))
+    o.setdefault("mu_split", torch.empty((B, H, nb, D), dtype=torch.int32, device=dev))
     wsb = vc_smooth_group_workspace_size(B, H, S, D, clusters)
     if workspace is None:
         workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
@@ -218,7 +220,7 @@ def vc_smooth_group(k, v, clusters: int, iters: int, seed: int, *, workspace=Non
     st = lib().vc_smooth_group(ctypes.byref(sh), ctypes.byref(kd), ctypes.byref(vd), ctypes.byref(p),
                                _ptr(o.get("centroids")), _ptr(o.get("labels")), _ptr(o["perm"]), _ptr(o["k8"]),
                                _ptr(o["k_scale"]), _ptr(o["r8"]), _ptr(o["r_scale"]), _ptr(o["mu_bf16"]),
-                               _ptr(o["mu_scaled"]), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _ptr(o["mu_split"]), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                _stream())
     _check(st, "vc_smooth_group")
     return o
@@ -242,7 +244,7 @@ def vsmooth_schedule(n_steps: int, step: int, reuse: int = 4) -> str:
 # vc_attn_fwd
 # --------------------------------------------------------------------------- #
 
-def vc_attn_fwd(q8, q_scale, k8, k_scale, v8, v_scale, mu_scaled=None, *, S: int, out=None, sm_scale: float = 0.0,
+def vc_attn_fwd(q8, q_scale, k8, k_scale, v8, v_scale, mu_split=None, *, S: int, out=None, sm_scale: float = 0.0,
                 window: int = 2, sequential: bool = False):
     """FP8 ExpCast attention.  Codes and scales as produced by vc_quantize /
     vc_smooth_group; S is the token count.  Returns bf16 [B,S,H,D]."""
@@ -254,7 +256,7 @@ def vc_attn_fwd(q8, q_scale, k8, k_scale, v8, v_scale, mu_scaled=None, *, S: int
     p = vc_attn_params(sm_scale, window, VC_ATTN_SEQUENTIAL if sequential else 0)
     od = _bshd_out(out)
     st = lib().vc_attn_fwd(ctypes.byref(sh), ctypes.byref(p), _ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale),
-                           _ptr(v8), _ptr(v_scale), _ptr(mu_scaled), ctypes.byref(od), _stream())
+                           _ptr(v8), _ptr(v_scale), _ptr(mu_split), ctypes.byref(od), _stream())
     _check(st, "vc_attn_fwd")
     return out
 

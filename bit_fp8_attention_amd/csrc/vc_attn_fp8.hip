@@ -114,7 +114,7 @@ template <int D, bool VS>
 __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ q_scale, const uint8_t* __restrict__ k8,
     const float* __restrict__ k_scale, const uint8_t* __restrict__ v8, const float* __restrict__ v_scale,
-    const float* __restrict__ mu, uint16_t* __restrict__ o, int64_t oB, int64_t oS, int64_t oH, int S, int H,
+    const u32* __restrict__ mu, uint16_t* __restrict__ o, int64_t oB, int64_t oS, int64_t oH, int S, int H,
     int nblk, int npair, float c1, int window, int sequential) {
   constexpr int NM = D / 16;             // channel blocks of the output
   constexpr int TB = kBlk * D;           // bytes of one K or V tile
@@ -126,10 +126,11 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t vst0[TB];
   __shared__ __attribute__((aligned(1024))) uint8_t vst1[TB];
   __shared__ __attribute__((aligned(1024))) uint8_t vst2[TB];
-  // V-Smooth: ring of the scaled block-mean rows of the last 16 visited
-  // tiles (one 8-tile restoration window plus the rows in flight)
+  // V-Smooth: ring of the scaled block-mean rows (bf16 hi | lo << 16 per
+  // channel) of the last 16 visited tiles (one 8-tile restoration window
+  // plus the rows in flight)
   constexpr int MR = VS ? 16 : 1;
-  __shared__ __attribute__((aligned(1024))) float mring[MR][D];
+  __shared__ __attribute__((aligned(1024))) u32 mring[MR][D];
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int pr = __builtin_amdgcn_readfirstlane(lin % npair);
@@ -188,8 +189,8 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
   const bool tail_last = ragged && !tail_first;  // then tile_at(n - 1) == n - 1
 
   if (VS) {  // rows never written must read as finite zeros
-    float* mz = &mring[0][0];
-    for (int e = tid; e < MR * D; e += 512) mz[e] = 0.f;
+    u32* mz = &mring[0][0];
+    for (int e = tid; e < MR * D; e += 512) mz[e] = 0u;
     __syncthreads();
   }
   // prologue: mean row 0, K_0, V_0, K_1; K_0 must have landed before M(0)
@@ -298,9 +299,13 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
           if (slot == 2 * g + 1) rb[s][1] = rr[s];
         }
       }
-      // V-Smooth mean restoration for the 8-tile window ending at tile i:
-      // K slots (g, 4j + e) carry tile 2g + j of the window with
-      // (r_hi, r_lo, r_hi, 0) x (mu_hi, mu_hi, mu_lo, 0)
+      // V-Smooth mean restoration for the 8-tile window ending at tile i.
+      // Lane group g carries window slots 2g (mean pair m0, row sum r0) and
+      // 2g + 1 (m1, r1) in K slots 8g .. 8g + 7 as
+      //   mean side: (m0.hi, m0.lo, m1.hi, m1.lo, m0.hi, 0, m1.hi, 0)
+      //   sum side:  (r0.hi, r0.hi, r1.hi, r1.hi, r0.lo, 0, r1.lo, 0)
+      // i.e. r.hi * (hi + lo) + r.lo * hi per slot; the mean side is the two
+      // stored pairs as read plus their hi halves
       if (VS && (slot == 7 || i == n - 1)) {
         v8bf Ar[2];
 #pragma unroll
@@ -309,29 +314,21 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
           for (int jj = 0; jj < 2; ++jj) {
             const __bf16 hi = (__bf16)rb[s][jj];
             const __bf16 lo = (__bf16)(rb[s][jj] - (float)hi);
-            Ar[s][4 * jj + 0] = hi;
-            Ar[s][4 * jj + 1] = lo;
-            Ar[s][4 * jj + 2] = hi;
-            Ar[s][4 * jj + 3] = (__bf16)0.0f;
+            Ar[s][2 * jj + 0] = hi;
+            Ar[s][2 * jj + 1] = hi;
+            Ar[s][4 + 2 * jj + 0] = lo;
+            Ar[s][4 + 2 * jj + 1] = (__bf16)0.0f;
             rb[s][jj] = 0.f;
           }
         }
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-          v8bf Bm;
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            // window slot 2g + jj is visit i - slot + 2g + jj; slots past i
-            // hold zero row sums, so whatever finite row the ring holds there
-            // adds nothing
-            const float mvv = mring[(i - slot + 2 * g + jj) & (MR - 1)][16 * m + lr];
-            const __bf16 hi = (__bf16)mvv;
-            const __bf16 lo = (__bf16)(mvv - (float)hi);
-            Bm[4 * jj + 0] = hi;
-            Bm[4 * jj + 1] = hi;
-            Bm[4 * jj + 2] = lo;
-            Bm[4 * jj + 3] = (__bf16)0.0f;
-          }
+          // window slot 2g + jj is visit i - slot + 2g + jj; slots past i
+          // hold zero row sums, so whatever finite row the ring holds there
+          // adds nothing
+          const u32 m0 = mring[(i - slot + 2 * g) & (MR - 1)][16 * m + lr];
+          const u32 m1 = mring[(i - slot + 2 * g + 1) & (MR - 1)][16 * m + lr];
+          const v8bf Bm = __builtin_bit_cast(v8bf, (v4u){m0, m1, m0 & 0xffffu, m1 & 0xffffu});
           O[0][m] = mfma_bf16(Bm, Ar[0], O[0][m]);
           O[1][m] = mfma_bf16(Bm, Ar[1], O[1][m]);
         }
@@ -492,7 +489,7 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
 
 template <int D, bool VS>
 hipError_t launch_t(const vc_shape& sh, float c1, int window, int seq, const uint8_t* q8, const float* qs,
-                    const uint8_t* k8, const float* ks, const uint8_t* v8, const float* vs, const float* mu,
+                    const uint8_t* k8, const float* ks, const uint8_t* v8, const float* vs, const u32* mu,
                     BshdOut o, hipStream_t st) {
   const int nblk = (sh.S + kBlk - 1) / kBlk;
   const int npair = (nblk + 1) / 2;
@@ -506,14 +503,14 @@ hipError_t launch_t(const vc_shape& sh, float c1, int window, int seq, const uin
 
 hipError_t launch_attn_fp8(const vc_shape& sh, float sm_scale, int window, uint32_t flags, const uint8_t* q8,
                            const float* q_scale, const uint8_t* k8, const float* k_scale, const uint8_t* v8,
-                           const float* v_scale, const float* mu_scaled, BshdOut o, hipStream_t st) {
+                           const float* v_scale, const u32* mu_split, BshdOut o, hipStream_t st) {
   const float c1 = sm_scale * 1.44269504088896340736f;  // fl32(sm_scale * fl32(log2 e))
   const int seq = (flags & VC_ATTN_SEQUENTIAL) ? 1 : 0;
   if (sh.D == 128) {
-    if (mu_scaled) return launch_t<128, true>(sh, c1, window, seq, q8, q_scale, k8, k_scale, v8, v_scale, mu_scaled, o, st);
+    if (mu_split) return launch_t<128, true>(sh, c1, window, seq, q8, q_scale, k8, k_scale, v8, v_scale, mu_split, o, st);
     return launch_t<128, false>(sh, c1, window, seq, q8, q_scale, k8, k_scale, v8, v_scale, nullptr, o, st);
   }
-  if (mu_scaled) return launch_t<64, true>(sh, c1, window, seq, q8, q_scale, k8, k_scale, v8, v_scale, mu_scaled, o, st);
+  if (mu_split) return launch_t<64, true>(sh, c1, window, seq, q8, q_scale, k8, k_scale, v8, v_scale, mu_split, o, st);
   return launch_t<64, false>(sh, c1, window, seq, q8, q_scale, k8, k_scale, v8, v_scale, nullptr, o, st);
 }
 

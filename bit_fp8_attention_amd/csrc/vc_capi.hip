@@ -97,7 +97,7 @@ __attribute__((visibility("default"))) size_t vc_smooth_group_workspace_size(con
 __attribute__((visibility("default"))) int32_t vc_smooth_group(
     const vc_shape* sh, const vc_bshd* k, const vc_bshd* v, const vc_group_params* p, float* centroids,
     int32_t* labels, int32_t* perm, uint8_t* k8, float* k_scale, uint8_t* r8, float* r_scale, uint16_t* mu_bf16,
-    float* mu_scaled, void* workspace, size_t workspace_bytes, void* stream) {
+    uint32_t* mu_split, void* workspace, size_t workspace_bytes, void* stream) {
   int32_t e = check_shape(sh);
   if (e) return e;
   if ((e = check_bshd(k)) || (e = check_bshd(v))) return e;
@@ -106,39 +106,39 @@ __attribute__((visibility("default"))) int32_t vc_smooth_group(
   if ((p->flags & VC_GROUP_WARM_START) && (p->flags & VC_GROUP_REUSE_PERM)) return VC_ERR_UNSUPPORTED;
   const bool reuse = (p->flags & VC_GROUP_REUSE_PERM) != 0;
   if ((!reuse && (!centroids || !labels)) || !perm || !k8 || !k_scale || !r8 || !r_scale || !mu_bf16 ||
-      !mu_scaled || !workspace)
+      !mu_split || !workspace)
     return VC_ERR_NULL;
   const int kmax = 8192 / sh->D;
   if (p->clusters < 1 || p->clusters > kmax || p->clusters > sh->S) return VC_ERR_UNSUPPORTED;
   if (p->iters < 1 || p->iters > 64) return VC_ERR_UNSUPPORTED;
   if (!aligned16(k8) || !aligned16(r8) || ((uintptr_t)workspace & 255u)) return VC_ERR_ALIGN;
   if (((uintptr_t)centroids | (uintptr_t)labels | (uintptr_t)perm | (uintptr_t)k_scale | (uintptr_t)r_scale |
-       (uintptr_t)mu_scaled) & 3u)
+       (uintptr_t)mu_split) & 3u)
     return VC_ERR_ALIGN;
   if (((uintptr_t)mu_bf16) & 1u) return VC_ERR_ALIGN;
   if (workspace_bytes < vc::group_workspace_bytes(*sh, p->clusters)) return VC_ERR_WORKSPACE;
   return hip_status(vc::launch_smooth_group(*sh, as_bshd(k), as_bshd(v), *p, centroids, labels, perm, k8, k_scale,
-                                            r8, r_scale, mu_bf16, mu_scaled, workspace, (hipStream_t)stream));
+                                            r8, r_scale, mu_bf16, mu_split, workspace, (hipStream_t)stream));
 }
 
 __attribute__((visibility("default"))) int32_t vc_attn_fwd(const vc_shape* sh, const vc_attn_params* p,
                                                             const uint8_t* q8, const float* q_scale,
                                                             const uint8_t* k8, const float* k_scale,
                                                             const uint8_t* v8, const float* v_scale,
-                                                            const float* mu_scaled, const vc_bshd_out* o,
+                                                            const uint32_t* mu_split, const vc_bshd_out* o,
                                                             void* stream) {
   int32_t e = check_shape(sh);
   if (e) return e;
   if (!p || !q8 || !q_scale || !k8 || !k_scale || !v8 || !v_scale) return VC_ERR_NULL;
   if ((e = check_out(o))) return e;
   if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8)) return VC_ERR_ALIGN;
-  if (((uintptr_t)q_scale | (uintptr_t)k_scale | (uintptr_t)v_scale | (uintptr_t)mu_scaled) & 3u) return VC_ERR_ALIGN;
+  if (((uintptr_t)q_scale | (uintptr_t)k_scale | (uintptr_t)v_scale | (uintptr_t)mu_split) & 3u) return VC_ERR_ALIGN;
   if (p->window < 0 || (p->flags & ~VC_ATTN_SEQUENTIAL)) return VC_ERR_UNSUPPORTED;
   if (!(p->sm_scale >= 0.0f) || isinf(p->sm_scale)) return VC_ERR_UNSUPPORTED;
   const float sm = p->sm_scale == 0.0f ? 1.0f / sqrtf((float)sh->D) : p->sm_scale;
   BshdOut ob{(uint16_t*)o->ptr, o->sB, o->sS, o->sH};
   return hip_status(vc::launch_attn_fp8(*sh, sm, p->window, p->flags, q8, q_scale, k8, k_scale, v8, v_scale,
-                                        mu_scaled, ob, (hipStream_t)stream));
+                                        mu_split, ob, (hipStream_t)stream));
 }
 
 __attribute__((visibility("default"))) int32_t vc_pack_v_bf16(const vc_shape* sh, const vc_bshd* v, uint16_t* vt,

@@ -431,14 +431,16 @@ __global__ __launch_bounds__(256) void group_apply1(const uint16_t* __restrict__
   }
 }
 
-// Pass 2: residual codes in the key-contiguous layout; scaled means.
+// Pass 2: residual codes in the key-contiguous layout; scaled means as bf16
+// (hi, lo) pairs: m = mu * 448 / amax in fp32, hi = bf16(m), lo = bf16(m - hi)
+// (both round-half-even; m - hi is exact), stored hi | lo << 16.
 template <int D>
 __global__ __launch_bounds__(256) void group_apply2(const uint16_t* __restrict__ vx, int64_t vB, int64_t vS,
                                                     int64_t vH, int S, int H, int nblk,
                                                     const int32_t* __restrict__ perm,
                                                     const uint16_t* __restrict__ mu_bf16, GroupWs ws,
                                                     uint8_t* __restrict__ r8, float* __restrict__ r_scale,
-                                                    float* __restrict__ mu_scaled) {
+                                                    u32* __restrict__ mu_split) {
   using Mp = ApplyMap<D>;
   constexpr int LD = D + 4;
   __shared__ uint8_t tile[kBlk * LD];
@@ -455,7 +457,10 @@ __global__ __launch_bounds__(256) void group_apply2(const uint16_t* __restrict__
     inv_l[t] = inv;
     float mu = bf16_to_f32(mu_bf16[(bh * nblk + j) * D + t]);
     mu_l[t] = mu;
-    mu_scaled[(bh * nblk + j) * D + t] = mu * inv;
+    const float ms = mu * inv;
+    const uint16_t hi = f32_to_bf16(ms);
+    const uint16_t lo = f32_to_bf16(ms - bf16_to_f32(hi));
+    mu_split[(bh * nblk + j) * D + t] = (u32)hi | ((u32)lo << 16);
     if (j == 0) r_scale[bh * D + t] = s;
   }
   __syncthreads();
@@ -498,7 +503,7 @@ __global__ __launch_bounds__(256) void group_apply2(const uint16_t* __restrict__
 template <int D>
 hipError_t launch_group_t(const vc_shape& sh, Bshd k, Bshd v, const vc_group_params& p, float* cent, int32_t* labels,
                           int32_t* perm, uint8_t* k8, float* k_scale, uint8_t* r8, float* r_scale,
-                          uint16_t* mu_bf16, float* mu_scaled, GroupWs ws, hipStream_t st) {
+                          uint16_t* mu_bf16, u32* mu_split, GroupWs ws, hipStream_t st) {
   const int S = sh.S, H = sh.H, B = sh.B, kc = p.clusters;
   const int nblk = (S + kBlk - 1) / kBlk, nchunk = (S + kChunk - 1) / kChunk;
   const int BH = B * H;
@@ -520,7 +525,7 @@ hipError_t launch_group_t(const vc_shape& sh, Bshd k, Bshd v, const vc_group_par
   group_apply1<D><<<dim3(nblk, H, B), 256, 0, st>>>(k.p, k.sB, k.sS, k.sH, v.p, v.sB, v.sS, v.sH, S, H, nblk, perm,
                                                     k8, k_scale, mu_bf16, ws);
   group_apply2<D><<<dim3(nblk, H, B), 256, 0, st>>>(v.p, v.sB, v.sS, v.sH, S, H, nblk, perm, mu_bf16, ws, r8,
-                                                    r_scale, mu_scaled);
+                                                    r_scale, mu_split);
   return hipGetLastError();
 }
 
@@ -534,12 +539,12 @@ size_t group_workspace_bytes(const vc_shape& sh, int clusters) {
 
 hipError_t launch_smooth_group(const vc_shape& sh, Bshd k, Bshd v, const vc_group_params& p, float* centroids,
                                int32_t* labels, int32_t* perm, uint8_t* k8, float* k_scale, uint8_t* r8,
-                               float* r_scale, uint16_t* mu_bf16, float* mu_scaled, void* ws, hipStream_t st) {
+                               float* r_scale, uint16_t* mu_bf16, uint32_t* mu_split, void* ws, hipStream_t st) {
   GroupWs g = carve(ws, sh, p.clusters, nullptr);
   if (sh.D == 128)
-    return launch_group_t<128>(sh, k, v, p, centroids, labels, perm, k8, k_scale, r8, r_scale, mu_bf16, mu_scaled, g,
+    return launch_group_t<128>(sh, k, v, p, centroids, labels, perm, k8, k_scale, r8, r_scale, mu_bf16, mu_split, g,
                                st);
-  return launch_group_t<64>(sh, k, v, p, centroids, labels, perm, k8, k_scale, r8, r_scale, mu_bf16, mu_scaled, g, st);
+  return launch_group_t<64>(sh, k, v, p, centroids, labels, perm, k8, k_scale, r8, r_scale, mu_bf16, mu_split, g, st);
 }
 
 }  // namespace vc

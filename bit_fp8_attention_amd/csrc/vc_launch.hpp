@@ -30,12 +30,12 @@ hipError_t launch_expcast_codes(const float* x, const float* a, const float* b, 
 size_t group_workspace_bytes(const vc_shape& sh, int clusters);
 hipError_t launch_smooth_group(const vc_shape& sh, Bshd k, Bshd v, const vc_group_params& p, float* centroids,
                                int32_t* labels, int32_t* perm, uint8_t* k8, float* k_scale, uint8_t* r8,
-                               float* r_scale, uint16_t* mu_bf16, float* mu_scaled, void* ws, hipStream_t st);
+                               float* r_scale, uint16_t* mu_bf16, uint32_t* mu_split, void* ws, hipStream_t st);
 
 // vc_attn_fp8.hip
 hipError_t launch_attn_fp8(const vc_shape& sh, float sm_scale, int window, uint32_t flags, const uint8_t* q8,
                            const float* q_scale, const uint8_t* k8, const float* k_scale, const uint8_t* v8,
-                           const float* v_scale, const float* mu_scaled, BshdOut o, hipStream_t st);
+                           const float* v_scale, const uint32_t* mu_split, BshdOut o, hipStream_t st);
 
 // vc_attn_bf16.hip
 hipError_t launch_attn_bf16(const vc_shape& sh, float sm_scale, int window, uint32_t flags, Bshd q, Bshd k,

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define VC_ABI_VERSION 1
+#define VC_ABI_VERSION 2
 
 typedef enum vc_status {
   VC_OK = 0,
@@ -154,8 +154,11 @@ size_t vc_smooth_group_workspace_size(const vc_shape* shape, int32_t clusters);
  *  2. perm = stable argsort(labels)  (K' = K[perm], V' = V[perm]).
  *  3. For each 128-row block j of V': mu_j = bf16(mean of its valid rows);
  *     R = V' - 1 mu_j^T in fp32; per-channel s_R[d] = amax_d |R| / 448;
- *     r8 = E4M3_rne(R * (448 / amax_d)); mu_scaled[j][d] = mu_j[d] * (448 /
- *     amax_d) in fp32.  K' is quantised per 128-row block as in vc_quantize.
+ *     r8 = E4M3_rne(R * (448 / amax_d)); the scaled mean m = mu_j[d] *
+ *     (448 / amax_d) in fp32 is stored as a bf16 pair mu_split[j][d] =
+ *     hi | lo << 16, hi = bf16_rne(m), lo = bf16_rne(m - hi) (m - hi is
+ *     exact), the form the attention kernel's mean product reads.  K' is
+ *     quantised per 128-row block as in vc_quantize.
  * With VC_GROUP_WARM_START, step 1 starts from the given centroids; with
  * VC_GROUP_REUSE_PERM, steps 1 and 2 are skipped and perm is an input.  The
  * two flags exclude each other (VC_ERR_UNSUPPORTED).
@@ -163,13 +166,13 @@ size_t vc_smooth_group_workspace_size(const vc_shape* shape, int32_t clusters);
  *   centroids fp32 [B][H][clusters][D]; labels, perm int32 [B][H][S];
  *   k8 packed K, k_scale fp32 [B][H][nblk];
  *   r8 packed V (the residual codes), r_scale fp32 [B][H][D];
- *   mu_bf16 uint16 [B][H][nblk][D]; mu_scaled fp32 [B][H][nblk][D].
+ *   mu_bf16 uint16 [B][H][nblk][D]; mu_split uint32 [B][H][nblk][D].
  * workspace: >= vc_smooth_group_workspace_size(shape, clusters) bytes,
  * 256-byte aligned; its contents on entry do not matter.
  */
 int32_t vc_smooth_group(const vc_shape* shape, const vc_bshd* k, const vc_bshd* v, const vc_group_params* p,
                         float* centroids, int32_t* labels, int32_t* perm, uint8_t* k8, float* k_scale,
-                        uint8_t* r8, float* r_scale, uint16_t* mu_bf16, float* mu_scaled, void* workspace,
+                        uint8_t* r8, float* r_scale, uint16_t* mu_bf16, uint32_t* mu_split, void* workspace,
                         size_t workspace_bytes, void* stream);
 
 /* ----------------------------------------------------------------------- */
@@ -184,7 +187,7 @@ typedef struct vc_attn_params {
 
 /*
  * vc_attn_fwd -- non-causal FP8 attention with ExpCast-FP8 (and V-Smooth's
- * mean restoration when mu_scaled != NULL).
+ * mean restoration when mu_split != NULL).
  * [VC] §3.1 Eq. 1 (online softmax), §3.2 Eq. 6 (A <- aA + P_q R_q + r mu^T),
  * §3.3 Eq. 7 (c = clip_[0,120](Round(8(u+8)+56+beta)), beta = -0.35);
  * [OVC] "Scheduling around ExpCast" (true-score running max, scales folded
@@ -205,18 +208,20 @@ typedef struct vc_attn_params {
  * conversion, no exponential, no FP8 cast); keys >= S get code 0;
  * A += P_code . V8 (matrix cores); r = sum of the decoded codes (the same
  * bytes, through the matrix cores against a tile of ones); l += r;
- * with V-Smooth A += r * mu_scaled[t].
+ * with V-Smooth A += r * (hi + lo) of mu_split[t], as the three bf16
+ * products r_hi hi + r_hi lo + r_lo hi on the matrix cores (r_hi = bf16(r),
+ * r_lo = bf16(r - r_hi)), once per 8 visited tiles.
  * Output: O = bf16((A / l) * v_scale[d]) written to `o` ([B,S,H,D] strided),
  * rows in the original query order.
  * Inputs are those of vc_quantize (plain path: q8 .. v_scale from it) or, for
  * V-Smooth, q8/q_scale from vc_quantize and k8/k_scale, v8 = r8,
- * v_scale = r_scale, mu_scaled from vc_smooth_group.
+ * v_scale = r_scale, mu_split from vc_smooth_group.
  * Requires |scores| well below 2^17 in log2 units so the code never exceeds
  * 120 (the upper clip is then implicit).
  */
 int32_t vc_attn_fwd(const vc_shape* shape, const vc_attn_params* p, const uint8_t* q8, const float* q_scale,
                     const uint8_t* k8, const float* k_scale, const uint8_t* v8, const float* v_scale,
-                    const float* mu_scaled, const vc_bshd_out* o, void* stream);
+                    const uint32_t* mu_split, const vc_bshd_out* o, void* stream);
 
 /* ----------------------------------------------------------------------- */
 
