@@ -353,14 +353,29 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
     }
     const float gk = c2 * ksv;
     const float a8 = 8.0f * gk;
+    // the lane's 32 scores of each sub-tile: a max tree of depth 4 (one
+    // v_max3_f32 per two scores, as a chain would take, but 4 dependent
+    // steps instead of 16), both sub-tiles before either rescale, so the
+    // two trees and the two cross-lane reductions overlap
+    float mx[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      float mx = __builtin_fmaxf(Sc[s][0][0], Sc[s][0][1]);
+      auto x = [&](int e) { return Sc[s][e >> 2][e & 3]; };
+      float u[11];
 #pragma unroll
-      for (int e = 2; e < 32; e += 2)  // one v_max3_f32 per two scores
-        mx = __builtin_fmaxf(__builtin_fmaxf(mx, Sc[s][e >> 2][e & 3]), Sc[s][(e + 1) >> 2][(e + 1) & 3]);
-      mx = max_over_groups(mx);
-      const float Mn = __builtin_fmaxf(M[s], gk * mx);
+      for (int k = 0; k < 10; ++k) u[k] = __builtin_fmaxf(__builtin_fmaxf(x(3 * k), x(3 * k + 1)), x(3 * k + 2));
+      u[10] = __builtin_fmaxf(x(30), x(31));
+      const float w0 = __builtin_fmaxf(__builtin_fmaxf(u[0], u[1]), u[2]);
+      const float w1 = __builtin_fmaxf(__builtin_fmaxf(u[3], u[4]), u[5]);
+      const float w2 = __builtin_fmaxf(__builtin_fmaxf(u[6], u[7]), u[8]);
+      const float w3 = __builtin_fmaxf(u[9], u[10]);
+      mx[s] = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(w0, w1), w2), w3);
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) mx[s] = max_over_groups(mx[s]);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const float Mn = __builtin_fmaxf(M[s], gk * mx[s]);
       if (__any(Mn > M[s])) {
         const float alpha = exp2f(M[s] - Mn);
         Lq[s] *= alpha;

@@ -7,11 +7,13 @@
 // (Eq. 4), and the means are stored divided by the per-channel scale
 // (Appendix B).  "Unbalanced clusters cost little": plain Lloyd k-means.
 //
-// Determinism by construction, so labels / pi / codes are bit-identical to a
-// sequential CPU run: every distance is one fp32 fmaf chain over d = 0..D-1
-// in a fixed order; cluster and block sums are 64-bit fixed point (24
-// fraction bits), which makes atomics order-independent; pi is a stable
-// counting sort.
+// Labels / pi / codes are bit-identical to a sequential CPU run of the rule:
+// each distance is one fp32 fmaf chain over d = 0..D-1 in a fixed order,
+// ties to the lowest cluster.  The assignment computes the distances on the
+// matrix cores and settles every token whose winner is not certain under a
+// proven error bound with that exact chain (kmeans_assign_mx).  Cluster and
+// block sums are 64-bit fixed point (24 fraction bits), which makes atomics
+// order-independent; pi is a stable counting sort.
 //
 // Kernels per call: init (Forgy indices by partial Fisher-Yates on
 // SplitMix64, centroids, norms, zeroed accumulators) -> iters x (assign +
@@ -19,6 +21,8 @@
 // apply pass 1 (gather K, V by pi; K' per-block codes; block means; residual
 // channel maxima) -> apply pass 2 (residual codes, key-contiguous; scaled
 // means).
+#include <algorithm>
+
 #include "vc_common.hpp"
 #include "vc_launch.hpp"
 
@@ -30,11 +34,11 @@ constexpr int kAssignTokens = 2048;  // tokens per assign workgroup
 constexpr int kChunk = 256;          // tokens per histogram / scatter chunk
 
 struct GroupWs {
-  long long* sums;     // [BH][k][D]
-  long long* counts;   // [BH][k]
-  float* norms;        // [BH][k]
-  int* hist;           // [BH][k][nchunk]
-  unsigned* r_amax;    // [BH][D]
+  long long* sums;      // [BH][k][D]
+  long long* counts;    // [BH][k]
+  float* norms;         // [BH][k]
+  int* hist;            // [BH][k][nchunk]
+  unsigned* r_amax;     // [BH][D]
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -69,6 +73,81 @@ VC_DEV long long fx24(float v) { return (long long)rint((double)v * 16777216.0);
 
 VC_DEV float fx24_mean(long long s, long long n) {
   return (float)(((double)s * (1.0 / 16777216.0)) / (double)n);
+}
+
+// fx24 of a bf16 value (its bit pattern b16) with |v| < 128: v * 2^24 is the
+// bit pattern with 24 added to the exponent field (a zero or subnormal lands
+// far below 1/2 and rounds to 0), rounded to nearest even in fp32 -- the
+// same integer as fx24 -- and converted exactly (|v * 2^24| < 2^31).
+VC_DEV long long fx24_small(u32 b16) {
+  return (long long)(int)__builtin_rintf(__uint_as_float((b16 << 16) + (24u << 23)));
+}
+
+// The oracle's assignment rule for one token: one fp32 fmaf chain per
+// centroid over d = 0..D-1, distance fmaf(-2, dot, |c|^2), ties to the
+// lowest cluster index.
+template <int D>
+VC_DEV int exact_label(const float (&x)[D], const float* __restrict__ cb, const float* __restrict__ nb, int k) {
+  int best = 0;
+  float bd = 0.0f;
+  int c = 0;
+  for (; c + 4 <= k; c += 4) {
+    float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+    const float* c0 = cb + (c + 0) * D;
+    const float* c1 = cb + (c + 1) * D;
+    const float* c2 = cb + (c + 2) * D;
+    const float* c3 = cb + (c + 3) * D;
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      d0 = __builtin_fmaf(x[d], c0[d], d0);
+      d1 = __builtin_fmaf(x[d], c1[d], d1);
+      d2 = __builtin_fmaf(x[d], c2[d], d2);
+      d3 = __builtin_fmaf(x[d], c3[d], d3);
+    }
+    float e0 = __builtin_fmaf(-2.0f, d0, nb[c + 0]);
+    float e1 = __builtin_fmaf(-2.0f, d1, nb[c + 1]);
+    float e2 = __builtin_fmaf(-2.0f, d2, nb[c + 2]);
+    float e3 = __builtin_fmaf(-2.0f, d3, nb[c + 3]);
+    if (c == 0 || e0 < bd) { bd = e0; best = c; }
+    if (e1 < bd) { bd = e1; best = c + 1; }
+    if (e2 < bd) { bd = e2; best = c + 2; }
+    if (e3 < bd) { bd = e3; best = c + 3; }
+  }
+  for (; c < k; ++c) {
+    const float* cc = cb + c * D;
+    float d0 = 0.f;
+#pragma unroll
+    for (int d = 0; d < D; ++d) d0 = __builtin_fmaf(x[d], cc[d], d0);
+    float e0 = __builtin_fmaf(-2.0f, d0, nb[c]);
+    if (c == 0 || e0 < bd) { bd = e0; best = c; }
+  }
+  return best;
+}
+
+template <int D>
+VC_DEV void load_row_f32(const uint16_t* row, float (&x)[D]) {
+#pragma unroll
+  for (int c8 = 0; c8 < D / 8; ++c8) {
+    uint4 w = ((const uint4*)row)[c8];
+    x[8 * c8 + 0] = bf16_lo(w.x);
+    x[8 * c8 + 1] = bf16_hi(w.x);
+    x[8 * c8 + 2] = bf16_lo(w.y);
+    x[8 * c8 + 3] = bf16_hi(w.y);
+    x[8 * c8 + 4] = bf16_lo(w.z);
+    x[8 * c8 + 5] = bf16_hi(w.z);
+    x[8 * c8 + 6] = bf16_lo(w.w);
+    x[8 * c8 + 7] = bf16_hi(w.w);
+  }
+}
+
+// A reduction over the four lane groups l, l^16, l^32, l^48 (the lanes that
+// hold one token's MFMA outputs): row swaps of 16, then of 32 lanes.
+template <class F>
+VC_DEV u32 over_groups(u32 x, F f) {
+  auto p16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = f(p16[0], p16[1]);
+  auto p32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return f(p32[0], p32[1]);
 }
 
 // Forgy initialisation, centroids, norms; zero the accumulators.
@@ -142,84 +221,291 @@ __global__ __launch_bounds__(256) void amax_reset(int D, GroupWs ws) {
   for (int e = threadIdx.x; e < D; e += 256) ws.r_amax[bh * D + e] = 0u;
 }
 
-// Assignment of kAssignTokens tokens, member sums accumulated in LDS and
-// flushed with 64-bit atomics.
-template <int D>
-__global__ __launch_bounds__(256) void kmeans_assign(const uint16_t* __restrict__ v, int64_t sB, int64_t sS,
-                                                     int64_t sH, int S, int H, int k,
-                                                     const float* __restrict__ cent, int32_t* __restrict__ labels,
-                                                     GroupWs ws) {
-  __shared__ unsigned long long lsum[8192];  // k * D <= 8192
-  __shared__ int lcnt[256];
+// Assignment on the matrix cores, with the exact rule's result.
+//
+// Every centroid c is split exactly into three bf16 parts (hi = bf16(c),
+// mid = bf16(c - hi), lo = c - hi - mid: each difference is exact in fp32 and
+// the last fits in 8 bits), so bf16 products x_d * part are exact and
+// v_mfma_f32_16x16x32_bf16 sums the 3D products of q = x . c in fp32.
+// However the matrix core orders and rounds that sum, it stays within
+// gamma_{3D+12}(2^-23) (1 + 2^-7) S of x . c, S = sum_d |x_d c_d| <= |x| |c|
+// (each addition off by at most 2^-23 relative); the oracle's fmaf chain p
+// stays within gamma_D(2^-24) S.  With a = fl(|c|^2 - 2q) and e the exact
+// rule's fl(|c|^2 - 2p), for D <= 128
+//   |a_c - e_c| <= 1.11e-4 |x| |c| + 2^-23 |a_c| (+ flushed tiny products),
+// and the kernel takes over twice that,
+//   beta_c = |x| |c| 1.0625 2^-12 + |a_c| 2^-22 + 2^-96,
+// with |x| and |c| rounded up.  The exact argmin c* then has
+// a_c* - beta_c* <= e_c* <= e_c <= a_c + beta_c for every c, so it lies in
+// {c : a_c - beta_c <= min_c' (a_c' + beta_c')}.  A token whose set has one
+// member takes it; the others go on the workgroup's list in LDS and are
+// settled at its end with the exact rule over their candidates only.
+//
+// Work: 512 threads, kAssignTokens tokens per workgroup; wave w takes 16 TBW
+// tokens per step; lane (g, lr) loads channels 32 kc + 8 g .. + 7 of token
+// 16 tb + lr (the B operand) and, after the products, holds centroids
+// 16 cb + 4 g + v of that token.
+template <int D, int NCB>
+__global__ __launch_bounds__(512) void kmeans_assign_mx(const uint16_t* __restrict__ v, int64_t sB, int64_t sS,
+                                                        int64_t sH, int S, int H, int k,
+                                                        const float* __restrict__ cent, int32_t* __restrict__ labels,
+                                                        GroupWs ws) {
+  constexpr int NKC = D / 32;             // 32-channel chunks
+  constexpr int NF = NCB * NKC * 3;       // A fragments (centroid block, chunk, part)
+  constexpr int TBW = NCB <= 4 ? 4 : 2;   // 16-token blocks per wave step
+  constexpr int KP = 16 * NCB;            // centroids, padded
+  constexpr int LD = D + 1;               // member-sum row stride (bank spread)
+  constexpr int NIT = kAssignTokens / (8 * 16 * TBW);
+  constexpr int NW = (KP + 31) / 32;      // 32-bit words of a candidate set
+  __shared__ uint4 cfrag[NF * 64];
+  __shared__ unsigned long long lsum[KP * LD];
+  __shared__ int lcnt[KP];
+  __shared__ __attribute__((aligned(16))) float lnrm[KP], lbc[KP];
+  __shared__ unsigned short otok[kAssignTokens];  // open tokens (offset in the workgroup's range)
+  __shared__ u32 omask[kAssignTokens * NW];       // and their candidate sets
+  __shared__ unsigned lmisc[2];                   // max |c|^2 (bits), open-list length
   const int h = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const int l = t & 63, lr = l & 15, g = l >> 4, w = t >> 6;
   const int64_t bh = (int64_t)b * H + h;
-  for (int e = t; e < k * D; e += 256) lsum[e] = 0ull;
-  for (int e = t; e < k; e += 256) lcnt[e] = 0;
-  __syncthreads();
-  const uint16_t* vb = v + b * sB + h * sH;
+  const int base = blockIdx.x * kAssignTokens;
   const float* __restrict__ cb = cent + bh * k * D;
-  const float* __restrict__ nb = ws.norms + bh * k;
-  for (int i = 0; i < kAssignTokens / 256; ++i) {
-    const int tok = blockIdx.x * kAssignTokens + i * 256 + t;
-    if (tok >= S) break;
-    float x[D];
-    const uint4* row = (const uint4*)(vb + (int64_t)tok * sS);
+  for (int e = t; e < KP * LD; e += 512) lsum[e] = 0ull;
+  for (int c = t; c < KP; c += 512) {
+    lcnt[c] = 0;
+    const float n2 = c < k ? ws.norms[bh * k + c] : INFINITY;  // padded centroids never win
+    lnrm[c] = n2;
+    lbc[c] = __builtin_sqrtf(n2) * (1.0f + 0x1p-10f) * 0x1.1p-12f;  // >= |c| times the bound's factor
+  }
+  if (t < 2) lmisc[t] = 0u;
+  for (int q = t; q < KP * (D / 8); q += 512) {
+    const int c = q / (D / 8), u = q % (D / 8);  // centroid c, channels 8u .. 8u + 7
+    u32 pw[3][4];
 #pragma unroll
-    for (int c8 = 0; c8 < D / 8; ++c8) {
-      uint4 w = row[c8];
-      x[8 * c8 + 0] = bf16_lo(w.x);
-      x[8 * c8 + 1] = bf16_hi(w.x);
-      x[8 * c8 + 2] = bf16_lo(w.y);
-      x[8 * c8 + 3] = bf16_hi(w.y);
-      x[8 * c8 + 4] = bf16_lo(w.z);
-      x[8 * c8 + 5] = bf16_hi(w.z);
-      x[8 * c8 + 6] = bf16_lo(w.w);
-      x[8 * c8 + 7] = bf16_hi(w.w);
-    }
-    int best = 0;
-    float bd = 0.0f;
-    int c = 0;
-    for (; c + 4 <= k; c += 4) {
-      float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
-      const float* c0 = cb + (c + 0) * D;
-      const float* c1 = cb + (c + 1) * D;
-      const float* c2 = cb + (c + 2) * D;
-      const float* c3 = cb + (c + 3) * D;
+    for (int e = 0; e < 8; e += 2) {
+      u32 lo16[3], hi16[3];
 #pragma unroll
-      for (int d = 0; d < D; ++d) {
-        d0 = __builtin_fmaf(x[d], c0[d], d0);
-        d1 = __builtin_fmaf(x[d], c1[d], d1);
-        d2 = __builtin_fmaf(x[d], c2[d], d2);
-        d3 = __builtin_fmaf(x[d], c3[d], d3);
+      for (int j = 0; j < 2; ++j) {
+        const float x = c < k ? cb[c * D + 8 * u + e + j] : 0.f;
+        const uint16_t p0 = f32_to_bf16(x);
+        const float r1 = x - bf16_to_f32(p0);
+        const uint16_t p1 = f32_to_bf16(r1);
+        const uint16_t p2 = f32_to_bf16(r1 - bf16_to_f32(p1));
+        (j ? hi16 : lo16)[0] = p0;
+        (j ? hi16 : lo16)[1] = p1;
+        (j ? hi16 : lo16)[2] = p2;
       }
-      float e0 = __builtin_fmaf(-2.0f, d0, nb[c + 0]);
-      float e1 = __builtin_fmaf(-2.0f, d1, nb[c + 1]);
-      float e2 = __builtin_fmaf(-2.0f, d2, nb[c + 2]);
-      float e3 = __builtin_fmaf(-2.0f, d3, nb[c + 3]);
-      if (c == 0 || e0 < bd) { bd = e0; best = c; }
-      if (e1 < bd) { bd = e1; best = c + 1; }
-      if (e2 < bd) { bd = e2; best = c + 2; }
-      if (e3 < bd) { bd = e3; best = c + 3; }
-    }
-    for (; c < k; ++c) {
-      const float* cc = cb + c * D;
-      float d0 = 0.f;
 #pragma unroll
-      for (int d = 0; d < D; ++d) d0 = __builtin_fmaf(x[d], cc[d], d0);
-      float e0 = __builtin_fmaf(-2.0f, d0, nb[c]);
-      if (c == 0 || e0 < bd) { bd = e0; best = c; }
+      for (int part = 0; part < 3; ++part) pw[part][e / 2] = lo16[part] | (hi16[part] << 16);
     }
+    const int lane = (u & 3) * 16 + (c & 15);
+#pragma unroll
+    for (int part = 0; part < 3; ++part)
+      cfrag[(((c >> 4) * NKC + (u >> 2)) * 3 + part) * 64 + lane] =
+          make_uint4(pw[part][0], pw[part][1], pw[part][2], pw[part][3]);
+  }
+  __syncthreads();
+  float nl[NCB][4];
+#pragma unroll
+  for (int cbk = 0; cbk < NCB; ++cbk)
+#pragma unroll
+    for (int vv = 0; vv < 4; ++vv) nl[cbk][vv] = lnrm[16 * cbk + 4 * g + vv];
+  const uint16_t* vb = v + b * sB + h * sH;
+  const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  for (int it = 0; it < NIT; ++it) {
+    const int t0 = base + (it * 8 + w) * 16 * TBW;
+    if (t0 >= S) break;
+    uint4 xw[TBW][NKC];
+#pragma unroll
+    for (int tb = 0; tb < TBW; ++tb) {
+      const uint16_t* row = vb + (int64_t)min(t0 + 16 * tb + lr, S - 1) * sS;  // rows past S: discarded
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) xw[tb][kc] = *(const uint4*)(row + 32 * kc + 8 * g);
+    }
+    v4f acc[NCB][TBW];
+#pragma unroll
+    for (int cbk = 0; cbk < NCB; ++cbk)
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+        for (int part = 0; part < 3; ++part) {
+          const v8bf af = __builtin_bit_cast(v8bf, cfrag[((cbk * NKC + kc) * 3 + part) * 64 + l]);
+#pragma unroll
+          for (int tb = 0; tb < TBW; ++tb)
+            acc[cbk][tb] = mfma_bf16(af, __builtin_bit_cast(v8bf, xw[tb][kc]),
+                                     (kc == 0 && part == 0) ? zero4 : acc[cbk][tb]);
+        }
+    int lab[TBW];
+    u32 mlane = 0;  // max |x| bits over the lane's TBW tokens
+#pragma unroll
+    for (int tb = 0; tb < TBW; ++tb) {
+      // |x|_inf (exact: packed 16-bit maxima of the magnitude bits) and |x|^2
+      typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+      u16x2 mm = {0, 0};
+      float x2 = 0.f;
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        const u32 wd[4] = {xw[tb][kc].x, xw[tb][kc].y, xw[tb][kc].z, xw[tb][kc].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          mm = __builtin_elementwise_max(mm, __builtin_bit_cast(u16x2, wd[q] & 0x7fff7fffu));
+          x2 = __builtin_fmaf(bf16_lo(wd[q]), bf16_lo(wd[q]), x2);
+          x2 = __builtin_fmaf(bf16_hi(wd[q]), bf16_hi(wd[q]), x2);
+        }
+      }
+      u32 m = max((u32)mm[0], (u32)mm[1]);
+      m = over_groups(m, [](u32 a, u32 c) { return max(a, c); });
+      mlane = max(mlane, m);
+      x2 = __uint_as_float(over_groups(__float_as_uint(x2), [](u32 x, u32 y) {
+        return __float_as_uint(__uint_as_float(x) + __uint_as_float(y));
+      }));
+      const float xn = __builtin_sqrtf(x2) * (1.0f + 0x1p-10f);  // >= |x| (a sum of squares, a sqrt)
+      float a[NCB][4], lo[NCB][4];
+      float hmin = INFINITY;
+#pragma unroll
+      for (int cbk = 0; cbk < NCB; ++cbk) {
+        const float4 bc = *(const float4*)&lbc[16 * cbk + 4 * g];
+        const float bcv[4] = {bc.x, bc.y, bc.z, bc.w};
+#pragma unroll
+        for (int vv = 0; vv < 4; ++vv) {
+          a[cbk][vv] = __builtin_fmaf(-2.0f, acc[cbk][tb][vv], nl[cbk][vv]);
+          const float beta = __builtin_fmaf(fabsf(a[cbk][vv]), 0x1p-22f, __builtin_fmaf(xn, bcv[vv], 0x1p-96f));
+          lo[cbk][vv] = a[cbk][vv] - beta;  // NaN for padded centroids: never a candidate
+          hmin = fminf(hmin, a[cbk][vv] + beta);
+        }
+      }
+      hmin = __uint_as_float(over_groups(__float_as_uint(hmin), [](u32 x, u32 y) {
+        return __float_as_uint(fminf(__uint_as_float(x), __uint_as_float(y)));
+      }));
+      // candidate set as bits c = 16 cb + 4 g + v, word c / 32
+      u32 cm[NW];
+#pragma unroll
+      for (int q = 0; q < NW; ++q) cm[q] = 0u;
+#pragma unroll
+      for (int cbk = 0; cbk < NCB; ++cbk)
+#pragma unroll
+        for (int vv = 0; vv < 4; ++vv)
+          if (lo[cbk][vv] <= hmin) cm[cbk / 2] |= 1u << ((16 * cbk + 4 * g + vv) & 31);
+      int cnt = 0;
+#pragma unroll
+      for (int q = 0; q < NW; ++q) {
+        cm[q] = over_groups(cm[q], [](u32 x, u32 y) { return x | y; });
+        cnt += __builtin_popcount(cm[q]);
+      }
+      int idx = -1;
+#pragma unroll
+      for (int q = NW - 1; q >= 0; --q)
+        if (cm[q]) idx = 32 * q + __builtin_ctz(cm[q]);
+      const int tok = t0 + 16 * tb + lr;
+      const bool decided = cnt == 1 && idx < k;
+      lab[tb] = (tok < S && decided) ? idx : -1;
+      if (tok < S && g == 0) {
+        if (decided) {
+          labels[bh * S + tok] = idx;
+          atomicAdd(&lcnt[idx], 1);
+        } else {
+          const unsigned slot = atomicAdd(&lmisc[1], 1u);
+          otok[slot] = (unsigned short)(tok - base);
+#pragma unroll
+          for (int q = 0; q < NW; ++q) omask[slot * NW + q] = cm[q];
+        }
+      }
+    }
+    // member sums of the decided tokens: the lane's 32 channels of each.
+    // The lane's TBW tokens (16 apart) usually share a cluster: then each
+    // channel's TBW fixed-point values are added in registers first (int32 is
+    // exact for |x| < 32: |fx24| < 2^29, TBW <= 4) and go out as one atomic.
+    bool same = lab[0] >= 0;
+#pragma unroll
+    for (int tb = 1; tb < TBW; ++tb) same = same && lab[tb] == lab[0];
+    if (same && bf16_to_f32((uint16_t)mlane) < 32.0f) {
+      unsigned long long* ls = lsum + lab[0] * LD + 8 * g;
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          int s0 = 0, s1 = 0;
+#pragma unroll
+          for (int tb = 0; tb < TBW; ++tb) {
+            const u32 wd = q == 0 ? xw[tb][kc].x : q == 1 ? xw[tb][kc].y : q == 2 ? xw[tb][kc].z : xw[tb][kc].w;
+            s0 += (int)fx24_small(wd & 0xffffu);
+            s1 += (int)fx24_small(wd >> 16);
+          }
+          atomicAdd(&ls[32 * kc + 2 * q], (unsigned long long)(long long)s0);
+          atomicAdd(&ls[32 * kc + 2 * q + 1], (unsigned long long)(long long)s1);
+        }
+      }
+    } else if (bf16_to_f32((uint16_t)mlane) < 128.0f) {
+#pragma unroll
+      for (int tb = 0; tb < TBW; ++tb) {
+        if (lab[tb] < 0) continue;
+        unsigned long long* ls = lsum + lab[tb] * LD + 8 * g;
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+          const u32 wd[4] = {xw[tb][kc].x, xw[tb][kc].y, xw[tb][kc].z, xw[tb][kc].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            atomicAdd(&ls[32 * kc + 2 * q], (unsigned long long)fx24_small(wd[q] & 0xffffu));
+            atomicAdd(&ls[32 * kc + 2 * q + 1], (unsigned long long)fx24_small(wd[q] >> 16));
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int tb = 0; tb < TBW; ++tb) {
+        if (lab[tb] < 0) continue;
+        unsigned long long* ls = lsum + lab[tb] * LD + 8 * g;
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+          const u32 wd[4] = {xw[tb][kc].x, xw[tb][kc].y, xw[tb][kc].z, xw[tb][kc].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            atomicAdd(&ls[32 * kc + 2 * q], (unsigned long long)fx24(bf16_lo(wd[q])));
+            atomicAdd(&ls[32 * kc + 2 * q + 1], (unsigned long long)fx24(bf16_hi(wd[q])));
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // the open tokens: the exact rule over each one's candidates, in increasing
+  // cluster index so that ties still go to the lowest
+  const int nopen = (int)lmisc[1];
+  const float* __restrict__ nb = ws.norms + bh * k;
+  for (int i = t; i < nopen; i += 512) {
+    const int tok = base + otok[i];
+    float x[D];
+    load_row_f32<D>(vb + (int64_t)tok * sS, x);
+    int best = -1;
+    float bd = 0.0f;
+    for (int q = 0; q < NW; ++q) {
+      u32 mk = omask[i * NW + q];
+      while (mk) {
+        const int c = 32 * q + __builtin_ctz(mk);
+        mk &= mk - 1;
+        if (c >= k) break;
+        float d0 = 0.f;
+#pragma unroll
+        for (int d = 0; d < D; ++d) d0 = __builtin_fmaf(x[d], cb[c * D + d], d0);
+        const float e0 = __builtin_fmaf(-2.0f, d0, nb[c]);
+        if (best < 0 || e0 < bd) {
+          bd = e0;
+          best = c;
+        }
+      }
+    }
+    if (best < 0) best = exact_label<D>(x, cb, nb, k);  // an empty set cannot happen; stay exact regardless
     labels[bh * S + tok] = best;
     atomicAdd(&lcnt[best], 1);
-    unsigned long long* ls = lsum + best * D;
+    unsigned long long* ls = lsum + best * LD;
 #pragma unroll
     for (int d = 0; d < D; ++d) atomicAdd(&ls[d], (unsigned long long)fx24(x[d]));
   }
   __syncthreads();
   unsigned long long* gs = (unsigned long long*)ws.sums + bh * k * D;
-  for (int e = t; e < k * D; e += 256)
-    if (lcnt[e / D] > 0) atomicAdd(&gs[e], lsum[e]);
-  for (int e = t; e < k; e += 256)
+  for (int e = t; e < k * D; e += 512)
+    if (lcnt[e / D] > 0) atomicAdd(&gs[e], lsum[(e / D) * LD + e % D]);
+  for (int e = t; e < k; e += 512)
     if (lcnt[e] > 0) atomicAdd((unsigned long long*)&ws.counts[bh * k + e], (unsigned long long)lcnt[e]);
 }
 
@@ -514,8 +800,11 @@ hipError_t launch_group_t(const vc_shape& sh, Bshd k, Bshd v, const vc_group_par
     group_init<D><<<dim3(H, B), 256, 0, st>>>(v.p, v.sB, v.sS, v.sH, S, H, kc, p.seed,
                                               (p.flags & VC_GROUP_WARM_START) ? 1 : 0, cent, ws);
     const dim3 ga((S + kAssignTokens - 1) / kAssignTokens, H, B);
+    const int ncb = kc <= 16 ? 1 : kc <= 32 ? 2 : kc <= 64 ? 4 : 8;  // k <= 8192 / D
+    auto assign = ncb == 1 ? kmeans_assign_mx<D, 1> : ncb == 2 ? kmeans_assign_mx<D, 2>
+                  : ncb == 4 ? kmeans_assign_mx<D, 4> : kmeans_assign_mx<D, (D == 64 ? 8 : 4)>;
     for (int it = 0; it < p.iters; ++it) {
-      kmeans_assign<D><<<ga, 256, 0, st>>>(v.p, v.sB, v.sS, v.sH, S, H, kc, cent, labels, ws);
+      assign<<<ga, 512, 0, st>>>(v.p, v.sB, v.sS, v.sH, S, H, kc, cent, labels, ws);
       kmeans_update<D><<<BH, 256, 0, st>>>(kc, cent, ws);
     }
     label_hist<<<dim3(nchunk, H, B), 256, 0, st>>>(labels, S, H, kc, nchunk, ws);

@@ -221,6 +221,32 @@ def test_smooth_group_video_bitexact(vc):
     _group_case(vc, k, v, 64, 4, 1002)
 
 
+@pytest.mark.parametrize("D,kc", [(128, 8), (64, 16), (128, 64), (64, 128)])
+def test_smooth_group_ties_bitexact(vc, D, kc):
+    # six distinct value rows per head, each repeated: the Forgy draw takes
+    # duplicate centroids, so most tokens are equally far from two or more
+    # clusters and the lowest index must win (the open-token path)
+    print(f"case group ties D={D} k={kc}", flush=True)
+    S, H = 1500, 2
+    q, k, v = vcsynth.random_qkv(1, S, H, D, seed=31)
+    g = torch.Generator().manual_seed(5)
+    base = torch.randn((6, H, D), generator=g)
+    pick = torch.randint(0, 6, (S,), generator=g)
+    v = base[pick].unsqueeze(0).to(torch.bfloat16)
+    _group_case(vc, k, v, kc, 3, 17)
+
+
+def test_smooth_group_large_values_bitexact(vc):
+    # a quarter of the tokens scaled x400 (|v| in the thousands): the slow
+    # fixed-point conversion and a wide candidate margin
+    print("case group large values", flush=True)
+    q, k, v = vcsynth.random_qkv(1, 2000, 2, 128, seed=41, v_kind="t3")
+    g = torch.Generator().manual_seed(6)
+    scale = torch.where(torch.rand((1, 2000, 2, 1), generator=g) < 0.25, 400.0, 1.0)
+    v = (v.float() * scale).to(torch.bfloat16)
+    _group_case(vc, k, v, 64, 3, 23)
+
+
 def _next_step(x, seed, sigma=0.05):
     """bf16 activations of a following denoising step: x plus small noise."""
     g = torch.Generator().manual_seed(seed)
