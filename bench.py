@@ -35,16 +35,20 @@ sys.path.insert(0, ROOT)
 FP8_PEAK_TFLOPS = 5000.0   # MI355X published dense FP8 matrix-core peak
 BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense BF16 matrix-core peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fp8_wan_traffic.json")
-ATTN_SRC = os.path.join(ROOT, "bit_fp8_attention_amd", "csrc", "vc_attn_fp8.hip")
+# the attention kernel's sources: its file and the header of shared device helpers
+ATTN_SRC = [os.path.join(ROOT, "bit_fp8_attention_amd", "csrc", f) for f in ("vc_attn_fp8.hip", "vc_common.hpp")]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def _sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def _sha(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def traffic_from_profile():

@@ -230,6 +230,7 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
   // feeds to the mean product
   float rb[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
   v4f Sc[2][8];                               // S^T of the current tile
+  float pm[2];                                // max of its key blocks 0..5 (steady-state tiles)
   float ksv = ksb[tile_at(0)];                // key scale of the current tile
   v8i P[2];                                   // codes of the previous tile
 
@@ -243,9 +244,13 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
   // k - NM; each is read from LDS two MFMA pairs ahead of its use, so the LDS
   // latency hides behind matrix-core work.  PV / QK are std::true_type or
   // std::false_type, so every index is a compile-time constant. ----
-  auto mphase = [&](int j, const uint8_t* Kt, const uint8_t* Vt, auto pv_tag, auto qk_tag) {
+  auto mphase = [&](int j, const uint8_t* Kt, const uint8_t* Vt, auto pv_tag, auto qk_tag, auto pm_tag) {
     constexpr bool PV = decltype(pv_tag)::value;
     constexpr bool QK = decltype(qk_tag)::value;
+    // PM: a tile with no masked keys; the running-max tree over its key
+    // blocks 0..5 is built here, two MFMA pairs behind their products, on
+    // VALU issue slots the matrix-core chain leaves free
+    constexpr bool PM = QK && decltype(pm_tag)::value;
     constexpr int K0 = PV ? 0 : NM;
     constexpr int K1 = QK ? NM + 8 : NM;
     constexpr int KD = D == 128 ? 2 : 1;  // LDS reads of one K fragment
@@ -275,6 +280,19 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
       } else {
         Sc[0][k - NM] = mfma_fp8(f, qf[0], zero4);
         Sc[1][k - NM] = mfma_fp8(f, qf[1], zero4);
+        if constexpr (PM && k - NM >= 2) {
+          constexpr int t8 = k - NM - 2;
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            float m = __builtin_fmaxf(__builtin_fmaxf(t8 == 0 ? Sc[s][0][0] : pm[s], Sc[s][t8][t8 == 0 ? 1 : 0]),
+                                      Sc[s][t8][t8 == 0 ? 2 : 1]);
+            if (t8 == 0) {
+              pm[s] = __builtin_fmaxf(m, Sc[s][0][3]);
+            } else {
+              pm[s] = __builtin_fmaxf(__builtin_fmaxf(m, Sc[s][t8][2]), Sc[s][t8][3]);
+            }
+          }
+        }
       }
     });
     // issue order: the first two fragments' reads, the row sums, then per
@@ -338,7 +356,8 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
 
   // ---- V phase: running max, rescale, codes of tile j; half B then issues
   // the copies of K_{j+3} and V_{j+2} into the stages M(j) last read ----
-  auto vphase = [&](int j, uint8_t* Kdst, uint8_t* Vdst, bool tail) {
+  auto vphase = [&](int j, uint8_t* Kdst, uint8_t* Vdst, bool tail, auto pm_tag) {
+    constexpr bool PM = decltype(pm_tag)::value;
     const int t = tile_at(j);
     if (tail) {
       const int lim = S - t * kBlk;  // valid keys in this tile
@@ -360,6 +379,13 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
     float mx[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
+      if constexpr (PM) {  // blocks 0..5 came from the M phase
+        const float m = __builtin_fmaxf(__builtin_fmaxf(pm[s], Sc[s][6][0]), Sc[s][6][1]);
+        const float m2 = __builtin_fmaxf(__builtin_fmaxf(m, Sc[s][6][2]), Sc[s][6][3]);
+        const float m3 = __builtin_fmaxf(__builtin_fmaxf(m2, Sc[s][7][0]), Sc[s][7][1]);
+        mx[s] = __builtin_fmaxf(__builtin_fmaxf(m3, Sc[s][7][2]), Sc[s][7][3]);
+        continue;
+      }
       auto x = [&](int e) { return Sc[s][e >> 2][e & 3]; };
       float u[11];
 #pragma unroll
@@ -432,34 +458,34 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
   }
 
   // j = 0 (may be the ragged tile; no P.V yet)
-  mphase(0, kst0, vst2, std::false_type{}, std::true_type{});
+  mphase(0, kst0, vst2, std::false_type{}, std::true_type{}, std::false_type{});
   mwait(0);
   phase_sync();
-  vphase(0, kst0, vst2, tail_first);
+  vphase(0, kst0, vst2, tail_first, std::false_type{});
   phase_sync();
 
   // steady state, j = 1 .. n - 2: stages fixed per unrolled copy (j mod 3)
   int j = 1;
   while (true) {
     if (j >= n - 1) break;
-    mphase(j, kst1, vst0, std::true_type{}, std::true_type{});
+    mphase(j, kst1, vst0, std::true_type{}, std::true_type{}, std::true_type{});
     mwait(j);
     phase_sync();
-    vphase(j, kst1, vst0, false);
+    vphase(j, kst1, vst0, false, std::true_type{});
     phase_sync();
     ++j;
     if (j >= n - 1) break;
-    mphase(j, kst2, vst1, std::true_type{}, std::true_type{});
+    mphase(j, kst2, vst1, std::true_type{}, std::true_type{}, std::true_type{});
     mwait(j);
     phase_sync();
-    vphase(j, kst2, vst1, false);
+    vphase(j, kst2, vst1, false, std::true_type{});
     phase_sync();
     ++j;
     if (j >= n - 1) break;
-    mphase(j, kst0, vst2, std::true_type{}, std::true_type{});
+    mphase(j, kst0, vst2, std::true_type{}, std::true_type{}, std::true_type{});
     mwait(j);
     phase_sync();
-    vphase(j, kst0, vst2, false);
+    vphase(j, kst0, vst2, false, std::true_type{});
     phase_sync();
     ++j;
   }
@@ -469,14 +495,14 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
   uint8_t* const Vp = cl == 0 ? vst2 : (cl == 1 ? vst0 : vst1);  // V_{n-2}
   uint8_t* const Vl = cl == 0 ? vst0 : (cl == 1 ? vst1 : vst2);  // V_{n-1}
   if (n >= 2) {
-    mphase(n - 1, Kl, Vp, std::true_type{}, std::true_type{});
+    mphase(n - 1, Kl, Vp, std::true_type{}, std::true_type{}, std::false_type{});
     mwait(n - 1);
     phase_sync();
-    vphase(n - 1, Kl, Vp, tail_last);
+    vphase(n - 1, Kl, Vp, tail_last, std::false_type{});
     phase_sync();
   }
   // M(n): the last P.V
-  mphase(n, nullptr, Vl, std::true_type{}, std::false_type{});
+  mphase(n, nullptr, Vl, std::true_type{}, std::false_type{}, std::false_type{});
   if (!hb) phase_sync();  // half A's extra barrier, matching half B's first
   if (hb) wait_vm();      // no copy may outlive the workgroup's LDS
 
