@@ -78,14 +78,14 @@ def traffic_job(w):
     import bit_fp8_attention_amd as vc
     import vcsynth
     q, k, v = vcsynth.make_qkv(w.name, device="cuda")
-    qz = vc.vc_quantize(q)
+    qz = vc.vc_quantize(q, sm_scale=w.sm_scale)
     g = vc.vc_smooth_group(k, v, w.clusters, w.iters, w.seed)
     o = torch.empty_like(q)
     a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
     torch.cuda.synchronize()
     vc.vc_attn_fwd(qz["q8"], qz["q_scale"], g["k8"], g["k_scale"], g["r8"], g["r_scale"], g["mu_split"], S=w.S,
-                   out=o, sm_scale=w.sm_scale)
+                   out=o)
     b.copy_(a)
     torch.cuda.synchronize()
     log("traffic job done")
@@ -165,7 +165,7 @@ def cpu_baseline(w, q, k, v, target_s=12.0):
     while True:
         rows = np.sort(rng.choice(w.S, n, replace=False))
         t0 = time.perf_counter()
-        oracle.attn_emulate_rows(prep["q_codes"], prep["q_scale"], kc, ks, vc_, vs, mu, w.S, w.sm_scale, rows)
+        oracle.attn_emulate_rows(prep["q_codes"], prep["q_scale"], kc, ks, vc_, vs, mu, w.S, 0.125, rows)
         elapsed = time.perf_counter() - t0
         if elapsed >= target_s / 4 or n >= w.S:
             break
@@ -222,7 +222,7 @@ def main():
 
     vs_on = w.vsmooth
     clusters, iters = (w.clusters, w.iters) if vs_on else (0, 0)
-    qz = vc.vc_quantize(q) if vs_on else vc.vc_quantize(q, k, v)
+    qz = vc.vc_quantize(q, sm_scale=w.sm_scale) if vs_on else vc.vc_quantize(q, k, v, sm_scale=w.sm_scale)
     if vs_on:
         ws = torch.empty(vc.vc_smooth_group_workspace_size(w.B, w.H, w.S, w.D, clusters), dtype=torch.uint8,
                          device=dev)
@@ -235,18 +235,18 @@ def main():
         e = [E() for _ in range(4)] if ev is not None else None
         if e: e[0].record()
         if vs_on:
-            vc.vc_quantize(q, out=qz)
+            vc.vc_quantize(q, sm_scale=w.sm_scale, out=qz)
             if e: e[1].record()
             vc.vc_smooth_group(k, v, clusters, iters, w.seed, workspace=ws, out=g)
             if e: e[2].record()
             vc.vc_attn_fwd(qz["q8"], qz["q_scale"], g["k8"], g["k_scale"], g["r8"], g["r_scale"], g["mu_split"],
-                           S=w.S, out=o, sm_scale=w.sm_scale)
+                           S=w.S, out=o)
         else:
-            vc.vc_quantize(q, k, v, out=qz)
+            vc.vc_quantize(q, k, v, sm_scale=w.sm_scale, out=qz)
             if e: e[1].record()
             if e: e[2].record()
             vc.vc_attn_fwd(qz["q8"], qz["q_scale"], qz["k8"], qz["k_scale"], qz["v8"], qz["v_scale"], None, S=w.S,
-                           out=o, sm_scale=w.sm_scale)
+                           out=o)
         if e:
             e[3].record()
             ev.append(e)

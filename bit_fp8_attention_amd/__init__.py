@@ -28,7 +28,7 @@ VC_OK = 0
 VC_ATTN_SEQUENTIAL = 1
 VC_GROUP_WARM_START = 1
 VC_GROUP_REUSE_PERM = 2
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class VcError(RuntimeError):
@@ -66,11 +66,11 @@ def lib():
             raise RuntimeError(f"{LIB_PATH} is missing: build the HIP library first "
                                "(python -c 'import __graft_entry__ as g; g.build()')")
         L = ctypes.CDLL(LIB_PATH)
-        P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        P, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
         L.vc_abi_version.restype = i32
         L.vc_status_str.argtypes = [i32]
         L.vc_status_str.restype = ctypes.c_char_p
-        L.vc_quantize.argtypes = [P] * 11
+        L.vc_quantize.argtypes = [P, f32] + [P] * 10
         L.vc_quantize.restype = i32
         L.vc_smooth_group_workspace_size.argtypes = [P, i32]
         L.vc_smooth_group_workspace_size.restype = sz
@@ -134,8 +134,9 @@ def nblk_of(S: int) -> int:
 # vc_quantize
 # --------------------------------------------------------------------------- #
 
-def vc_quantize(q=None, k=None, v=None, *, out=None):
-    """FP8 operands.  q, k, v: bf16 [B,S,H,D] (any may be None).
+def vc_quantize(q=None, k=None, v=None, *, sm_scale: float = 0.0, out=None):
+    """FP8 operands.  q, k, v: bf16 [B,S,H,D] (any may be None); sm_scale is
+    the softmax scale the attention will use (0: 1/sqrt(D)), folded into q8.
     Returns dict with q8, q_scale, k8, k_scale, v8, v_scale (see vc_attn.h)."""
     ref = next(x for x in (q, k, v) if x is not None)
     sh = _shape_of(ref)
@@ -153,7 +154,7 @@ def vc_quantize(q=None, k=None, v=None, *, out=None):
         o.setdefault("v8", torch.empty((B, H, D, nb * 128), dtype=torch.uint8, device=dev))
         o.setdefault("v_scale", torch.empty((B, H, D), dtype=torch.float32, device=dev))
     qd, kd, vd = _bshd(q), _bshd(k), _bshd(v)
-    st = lib().vc_quantize(ctypes.byref(sh), ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd),
+    st = lib().vc_quantize(ctypes.byref(sh), float(sm_scale), ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd),
                            _ptr(o.get("q8")), _ptr(o.get("q_scale")), _ptr(o.get("k8")), _ptr(o.get("k_scale")),
                            _ptr(o.get("v8")), _ptr(o.get("v_scale")), _stream())
     _check(st, "vc_quantize")
@@ -244,16 +245,17 @@ def vsmooth_schedule(n_steps: int, step: int, reuse: int = 4) -> str:
 # vc_attn_fwd
 # --------------------------------------------------------------------------- #
 
-def vc_attn_fwd(q8, q_scale, k8, k_scale, v8, v_scale, mu_split=None, *, S: int, out=None, sm_scale: float = 0.0,
-                window: int = 2, sequential: bool = False):
+def vc_attn_fwd(q8, q_scale, k8, k_scale, v8, v_scale, mu_split=None, *, S: int, out=None, window: int = 2,
+                sequential: bool = False):
     """FP8 ExpCast attention.  Codes and scales as produced by vc_quantize /
-    vc_smooth_group; S is the token count.  Returns bf16 [B,S,H,D]."""
+    vc_smooth_group (the softmax scale rides in q8: pass it to vc_quantize);
+    S is the token count.  Returns bf16 [B,S,H,D]."""
     B, H, S_pad, D = q8.shape
     assert S_pad == nblk_of(S) * 128
     sh = vc_shape(B, H, S, D)
     if out is None:
         out = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=q8.device)
-    p = vc_attn_params(sm_scale, window, VC_ATTN_SEQUENTIAL if sequential else 0)
+    p = vc_attn_params(0.0, window, VC_ATTN_SEQUENTIAL if sequential else 0)
     od = _bshd_out(out)
     st = lib().vc_attn_fwd(ctypes.byref(sh), ctypes.byref(p), _ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale),
                            _ptr(v8), _ptr(v_scale), _ptr(mu_split), ctypes.byref(od), _stream())

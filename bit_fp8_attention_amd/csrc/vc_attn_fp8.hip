@@ -5,12 +5,18 @@
 //  - online softmax recurrence m', alpha, A <- alpha A + P V, l <- alpha l + P1
 //    ([VC] §3.1 Eq. 1), running maximum on the true (dequantised) score and
 //    every increase applied ([OVC] "Scheduling around ExpCast");
-//  - each probability is an E4M3 code from one fused multiply-add into which
-//    softmax scale, Q/K dequant scales, log2 e, the factor 8 and the running
-//    maximum are folded: c = Round(8 g acc + 119.65 - 8 M') ([VC] §3.3 Eq. 7,
-//    beta = -0.35), rounded half-even and clamped at 0 by one integer
-//    conversion (v_cvt_pk_u8_f32) that also drops the byte into its slot of
-//    the matrix-core operand register -- no exponential, no FP8 cast;
+//  - each probability is the E4M3 code c = Round(8 g acc + 119.65 - 8 M')
+//    ([VC] §3.3 Eq. 7, beta = -0.35).  [OVC] "Scheduling around ExpCast"
+//    folds softmax scale, Q/K dequant scales, log2 e, the factor 8 and the
+//    running maximum into one multiply-add per score; here they are folded
+//    one step earlier, into the score product itself: Q's codes carry
+//    8 sm_scale log2 e (vc_quantize), the power-of-two Q/K block scales enter
+//    the matrix core as its E8M0 operands, and the accumulator starts at
+//    119.65 - 8 M, so the product emits 8 g acc + 119.65 - 8 M directly and a
+//    code is one integer conversion (v_cvt_pk_u8_f32: round half-even, clamp
+//    at 0, byte into its slot of the operand register) -- no exponential, no
+//    FP8 cast, no multiply-add.  Only a tile whose max rises adds the shift
+//    8 (M - M') to its scores;
 //  - the row sum is taken over the same bytes ([OVC] "A consistent
 //    denominator") by a matrix-core product against a tile of ones;
 //  - V-Smooth's block mean is restored in the same accumulator,
@@ -115,7 +121,7 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ q_scale, const uint8_t* __restrict__ k8,
     const float* __restrict__ k_scale, const uint8_t* __restrict__ v8, const float* __restrict__ v_scale,
     const u32* __restrict__ mu, uint16_t* __restrict__ o, int64_t oB, int64_t oS, int64_t oH, int S, int H,
-    int nblk, int npair, float c1, int window, int sequential) {
+    int nblk, int npair, int window, int sequential) {
   constexpr int NM = D / 16;             // channel blocks of the output
   constexpr int TB = kBlk * D;           // bytes of one K or V tile
   constexpr int NI = TB / 1024 / 4;      // 1 KB copies per issuing wave per tile
@@ -149,7 +155,8 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
   const uint8_t* kb = k8 + (int64_t)bh * S_pad * D;
   const uint8_t* vb = v8 + (int64_t)bh * D * S_pad;  // packed: tile t at + t * 128 * D
   const float* ksb = k_scale + (int64_t)bh * nblk;
-  const float c2 = c1 * q_scale[(int64_t)bh * nblk + qt];
+  // E8M0 block scale of the query tile (Q's codes carry 8 sm_scale log2 e)
+  const int sq = __builtin_amdgcn_readfirstlane(e8m0_of_pow2(q_scale[(int64_t)bh * nblk + qt]));
 
   // mid-window order of the pair: start a few tiles past the pair's diagonal
   const int start = __builtin_amdgcn_readfirstlane(sequential ? 0 : min(2 * pr + 1 + window, nblk - 1));
@@ -219,7 +226,10 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
   const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                     0x38383838, 0x38383838, 0x38383838, 0x38383838};  // E4M3 1.0
   const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
-  float M[2] = {-INFINITY, -INFINITY};  // running max of query lr of each sub-tile (log2 units)
+  // code offset 119.65 - 8 M of query lr of each sub-tile, M its running max
+  // (log2 units), and the S^T accumulator start holding it; 0 before the
+  // first tile, which sets it from that tile's max
+  float Bo[2] = {0.f, 0.f};
   float Lq[2] = {0.f, 0.f};             // running denominator of query lr
   v4f O[2][NM];
 #pragma unroll
@@ -231,7 +241,8 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
   float rb[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
   v4f Sc[2][8];                               // S^T of the current tile
   float pm[2];                                // max of its key blocks 0..5 (steady-state tiles)
-  float ksv = ksb[tile_at(0)];                // key scale of the current tile
+  int skv = e8m0_of_pow2(ksb[tile_at(0)]);    // E8M0 key scale of the current tile
+  v4f cinit[2] = {zero4, zero4};
   v8i P[2];                                   // codes of the previous tile
 
   // ---- M phase: row sums of P_{j-1}, A^T += V_{j-1}^T P_{j-1}^T, then
@@ -278,8 +289,8 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
         O[0][k] = mfma_fp8(f, P[0], O[0][k]);
         O[1][k] = mfma_fp8(f, P[1], O[1][k]);
       } else {
-        Sc[0][k - NM] = mfma_fp8(f, qf[0], zero4);
-        Sc[1][k - NM] = mfma_fp8(f, qf[1], zero4);
+        Sc[0][k - NM] = mfma_fp8_scaled(f, qf[0], cinit[0], skv, sq);
+        Sc[1][k - NM] = mfma_fp8_scaled(f, qf[1], cinit[1], skv, sq);
         if constexpr (PM && k - NM >= 2) {
           constexpr int t8 = k - NM - 2;
 #pragma unroll
@@ -306,6 +317,13 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       });
     }
+    // keep the score products in this block, ahead of the mean-restoration
+    // branch: the block-scaled products were otherwise moved below it, out
+    // of the interleaving above
+    if constexpr (QK)
+      asm volatile("" ::"v"(Sc[0][0]), "v"(Sc[0][1]), "v"(Sc[0][2]), "v"(Sc[0][3]), "v"(Sc[0][4]), "v"(Sc[0][5]),
+                   "v"(Sc[0][6]), "v"(Sc[0][7]), "v"(Sc[1][0]), "v"(Sc[1][1]), "v"(Sc[1][2]), "v"(Sc[1][3]),
+                   "v"(Sc[1][4]), "v"(Sc[1][5]), "v"(Sc[1][6]), "v"(Sc[1][7]));
     if constexpr (PV) {
       const int i = j - 1;
       const int slot = i & 7;
@@ -370,8 +388,6 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
             Sc[1][t8][v] = -INFINITY;
           }
     }
-    const float gk = c2 * ksv;
-    const float a8 = 8.0f * gk;
     // the lane's 32 scores of each sub-tile: a max tree of depth 4 (one
     // v_max3_f32 per two scores, as a chain would take, but 4 dependent
     // steps instead of 16), both sub-tiles before either rescale, so the
@@ -401,34 +417,41 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
     for (int s = 0; s < 2; ++s) mx[s] = max_over_groups(mx[s]);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const float Mn = __builtin_fmaxf(M[s], gk * mx[s]);
-      if (__any(Mn > M[s])) {
-        const float alpha = exp2f(M[s] - Mn);
-        Lq[s] *= alpha;
-        if (VS) {
-          rb[s][0] *= alpha;
-          rb[s][1] *= alpha;
-        }
-        // whole-vector multiplies (lane-wise: alpha is the lane's own query);
-        // per-element updates led the register allocator to keep two copies
-        // of the accumulators and spill
+      // Sc holds 8 g acc + Bo = 8 (score - M) + 119.65: the max rose iff the
+      // tile's largest exceeds 119.65; the first tile always sets the offset
+      const bool rise = j == 0 || mx[s] > 119.65f;
+      if (__any(rise)) {
+        const float delta = rise ? 119.65f - mx[s] : 0.0f;  // 8 (M - M'), 0 where the max held
+        if (j != 0) {
+          const float alpha = exp2f(delta * 0.125f);
+          Lq[s] *= alpha;
+          if (VS) {
+            rb[s][0] *= alpha;
+            rb[s][1] *= alpha;
+          }
+          // whole-vector multiplies (lane-wise: alpha is the lane's own query);
+          // per-element updates led the register allocator to keep two copies
+          // of the accumulators and spill
 #pragma unroll
-        for (int m = 0; m < NM; ++m) O[s][m] = O[s][m] * alpha;
-        M[s] = Mn;
+          for (int m = 0; m < NM; ++m) O[s][m] = O[s][m] * alpha;
+        }
+        Bo[s] += delta;
+        cinit[s] = v4f{Bo[s], Bo[s], Bo[s], Bo[s]};
+#pragma unroll
+        for (int t8 = 0; t8 < 8; ++t8) Sc[s][t8] = Sc[s][t8] + delta;
       }
-      const float bb = 119.65f - 8.0f * M[s];
 #pragma unroll
       for (int t8 = 0; t8 < 8; ++t8) {
         u32 wd = 0;
-        wd = VC_EXPCAST_BYTE(wd, a8, Sc[s][t8][0], bb, 0);
-        wd = VC_EXPCAST_BYTE(wd, a8, Sc[s][t8][1], bb, 1);
-        wd = VC_EXPCAST_BYTE(wd, a8, Sc[s][t8][2], bb, 2);
-        wd = VC_EXPCAST_BYTE(wd, a8, Sc[s][t8][3], bb, 3);
+        wd = __builtin_amdgcn_cvt_pk_u8_f32(Sc[s][t8][0], 0, wd);
+        wd = __builtin_amdgcn_cvt_pk_u8_f32(Sc[s][t8][1], 1, wd);
+        wd = __builtin_amdgcn_cvt_pk_u8_f32(Sc[s][t8][2], 2, wd);
+        wd = __builtin_amdgcn_cvt_pk_u8_f32(Sc[s][t8][3], 3, wd);
         P[s][t8] = (int)wd;
       }
     }
     // the next tile's key scale, a whole phase before it is needed
-    if (j + 1 < n) ksv = ksb[tile_at(j + 1)];
+    if (j + 1 < n) skv = e8m0_of_pow2(ksb[tile_at(j + 1)]);
     if (hb) {
       if (j + 2 < n) issue_mu(j + 2);
       if (j + 3 < n) issue_k(Kdst, j + 3);
@@ -464,30 +487,20 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
   vphase(0, kst0, vst2, tail_first, std::false_type{});
   phase_sync();
 
-  // steady state, j = 1 .. n - 2: stages fixed per unrolled copy (j mod 3)
-  int j = 1;
-  while (true) {
-    if (j >= n - 1) break;
-    mphase(j, kst1, vst0, std::true_type{}, std::true_type{}, std::true_type{});
-    mwait(j);
-    phase_sync();
-    vphase(j, kst1, vst0, false, std::true_type{});
-    phase_sync();
-    ++j;
-    if (j >= n - 1) break;
-    mphase(j, kst2, vst1, std::true_type{}, std::true_type{}, std::true_type{});
-    mwait(j);
-    phase_sync();
-    vphase(j, kst2, vst1, false, std::true_type{});
-    phase_sync();
-    ++j;
-    if (j >= n - 1) break;
-    mphase(j, kst0, vst2, std::true_type{}, std::true_type{}, std::true_type{});
-    mwait(j);
-    phase_sync();
-    vphase(j, kst0, vst2, false, std::true_type{});
-    phase_sync();
-    ++j;
+  // steady state, rolled: stages picked at run time (j mod 3)
+  {
+    int ck = 1, cv = 0;
+    for (int j = 1; j < n - 1; ++j) {
+      uint8_t* const Kc = ck == 0 ? kst0 : (ck == 1 ? kst1 : kst2);
+      uint8_t* const Vc = cv == 0 ? vst0 : (cv == 1 ? vst1 : vst2);
+      mphase(j, Kc, Vc, std::true_type{}, std::true_type{}, std::true_type{});
+      mwait(j);
+      phase_sync();
+      vphase(j, Kc, Vc, false, std::true_type{});
+      phase_sync();
+      ck = ck == 2 ? 0 : ck + 1;
+      cv = cv == 2 ? 0 : cv + 1;
+    }
   }
   // j = n - 1 (may be the ragged tile); stages chosen at run time
   const int cl = (n - 1) % 3;
@@ -529,30 +542,29 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
 }
 
 template <int D, bool VS>
-hipError_t launch_t(const vc_shape& sh, float c1, int window, int seq, const uint8_t* q8, const float* qs,
+hipError_t launch_t(const vc_shape& sh, int window, int seq, const uint8_t* q8, const float* qs,
                     const uint8_t* k8, const float* ks, const uint8_t* v8, const float* vs, const u32* mu,
                     BshdOut o, hipStream_t st) {
   const int nblk = (sh.S + kBlk - 1) / kBlk;
   const int npair = (nblk + 1) / 2;
   const int64_t n = (int64_t)npair * sh.H * sh.B;
   attn_fp8_kernel<D, VS><<<(unsigned)n, 512, 0, st>>>(q8, qs, k8, ks, v8, vs, mu, o.p, o.sB, o.sS, o.sH, sh.S,
-                                                          sh.H, nblk, npair, c1, window, seq);
+                                                          sh.H, nblk, npair, window, seq);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attn_fp8(const vc_shape& sh, float sm_scale, int window, uint32_t flags, const uint8_t* q8,
-                           const float* q_scale, const uint8_t* k8, const float* k_scale, const uint8_t* v8,
-                           const float* v_scale, const u32* mu_split, BshdOut o, hipStream_t st) {
-  const float c1 = sm_scale * 1.44269504088896340736f;  // fl32(sm_scale * fl32(log2 e))
+hipError_t launch_attn_fp8(const vc_shape& sh, int window, uint32_t flags, const uint8_t* q8, const float* q_scale,
+                           const uint8_t* k8, const float* k_scale, const uint8_t* v8, const float* v_scale,
+                           const u32* mu_split, BshdOut o, hipStream_t st) {
   const int seq = (flags & VC_ATTN_SEQUENTIAL) ? 1 : 0;
   if (sh.D == 128) {
-    if (mu_split) return launch_t<128, true>(sh, c1, window, seq, q8, q_scale, k8, k_scale, v8, v_scale, mu_split, o, st);
-    return launch_t<128, false>(sh, c1, window, seq, q8, q_scale, k8, k_scale, v8, v_scale, nullptr, o, st);
+    if (mu_split) return launch_t<128, true>(sh, window, seq, q8, q_scale, k8, k_scale, v8, v_scale, mu_split, o, st);
+    return launch_t<128, false>(sh, window, seq, q8, q_scale, k8, k_scale, v8, v_scale, nullptr, o, st);
   }
-  if (mu_split) return launch_t<64, true>(sh, c1, window, seq, q8, q_scale, k8, k_scale, v8, v_scale, mu_split, o, st);
-  return launch_t<64, false>(sh, c1, window, seq, q8, q_scale, k8, k_scale, v8, v_scale, nullptr, o, st);
+  if (mu_split) return launch_t<64, true>(sh, window, seq, q8, q_scale, k8, k_scale, v8, v_scale, mu_split, o, st);
+  return launch_t<64, false>(sh, window, seq, q8, q_scale, k8, k_scale, v8, v_scale, nullptr, o, st);
 }
 
 }  // namespace vc

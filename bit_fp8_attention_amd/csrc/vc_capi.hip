@@ -60,12 +60,13 @@ __attribute__((visibility("default"))) const char* vc_status_str(int32_t s) {
   }
 }
 
-__attribute__((visibility("default"))) int32_t vc_quantize(const vc_shape* sh, const vc_bshd* q, const vc_bshd* k,
-                                                            const vc_bshd* v, uint8_t* q8, float* q_scale,
-                                                            uint8_t* k8, float* k_scale, uint8_t* v8,
-                                                            float* v_scale, void* stream) {
+__attribute__((visibility("default"))) int32_t vc_quantize(const vc_shape* sh, float sm_scale, const vc_bshd* q,
+                                                            const vc_bshd* k, const vc_bshd* v, uint8_t* q8,
+                                                            float* q_scale, uint8_t* k8, float* k_scale,
+                                                            uint8_t* v8, float* v_scale, void* stream) {
   int32_t e = check_shape(sh);
   if (e) return e;
+  if (!(sm_scale >= 0.0f) || isinf(sm_scale)) return VC_ERR_UNSUPPORTED;
   const bool dq = q && q->ptr, dk = k && k->ptr, dv = v && v->ptr;
   if (dq) {
     if ((e = check_bshd(q))) return e;
@@ -83,8 +84,10 @@ __attribute__((visibility("default"))) int32_t vc_quantize(const vc_shape* sh, c
     if (!aligned16(v8) || ((uintptr_t)v_scale & 3u)) return VC_ERR_ALIGN;
   }
   hipStream_t st = (hipStream_t)stream;
-  if (dq && (e = hip_status(vc::launch_qk_quant(*sh, as_bshd(q), q8, q_scale, false, st)))) return e;
-  if (dk && (e = hip_status(vc::launch_qk_quant(*sh, as_bshd(k), k8, k_scale, true, st)))) return e;
+  const float sm = sm_scale == 0.0f ? 1.0f / sqrtf((float)sh->D) : sm_scale;
+  const float G = 8.0f * (sm * 1.44269504088896340736f);  // 8 fl(sm_scale * fl(log2 e)), exact times 8
+  if (dq && (e = hip_status(vc::launch_qk_quant(*sh, as_bshd(q), G, q8, q_scale, false, st)))) return e;
+  if (dk && (e = hip_status(vc::launch_qk_quant(*sh, as_bshd(k), 1.0f, k8, k_scale, true, st)))) return e;
   if (dv && (e = hip_status(vc::launch_v_quant(*sh, as_bshd(v), v8, v_scale, st)))) return e;
   return VC_OK;
 }
@@ -135,9 +138,8 @@ __attribute__((visibility("default"))) int32_t vc_attn_fwd(const vc_shape* sh, c
   if (((uintptr_t)q_scale | (uintptr_t)k_scale | (uintptr_t)v_scale | (uintptr_t)mu_split) & 3u) return VC_ERR_ALIGN;
   if (p->window < 0 || (p->flags & ~VC_ATTN_SEQUENTIAL)) return VC_ERR_UNSUPPORTED;
   if (!(p->sm_scale >= 0.0f) || isinf(p->sm_scale)) return VC_ERR_UNSUPPORTED;
-  const float sm = p->sm_scale == 0.0f ? 1.0f / sqrtf((float)sh->D) : p->sm_scale;
   BshdOut ob{(uint16_t*)o->ptr, o->sB, o->sS, o->sH};
-  return hip_status(vc::launch_attn_fp8(*sh, sm, p->window, p->flags, q8, q_scale, k8, k_scale, v8, v_scale,
+  return hip_status(vc::launch_attn_fp8(*sh, p->window, p->flags, q8, q_scale, k8, k_scale, v8, v_scale,
                                         mu_split, ob, (hipStream_t)stream));
 }
 

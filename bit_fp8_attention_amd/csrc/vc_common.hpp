@@ -47,6 +47,20 @@ VC_DEV u32 cvt4_fp8(float x0, float x1, float x2, float x3) {
 // clamped below at 0 by the integer conversion (v_cvt_pk_u8_f32).
 #define VC_EXPCAST_BYTE(word, a, x, b, sel) __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf((a), (x), (b)), (sel), (word))
 
+// Q/K block scale: the smallest power of two 2^e (e >= -127) with
+// amax <= 448 * 2^e, 2^0 for a block of zeros -- a scale the block-scaled
+// matrix-core product applies exactly, as its E8M0 operand e + 127.
+VC_DEV int pow2_block_exp(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  int e = __builtin_amdgcn_frexp_expf(amax) - 10;  // amax in [2^(e+9), 2^(e+10)): one step low
+  if (e < -127) e = -127;
+  while (amax > ldexpf(448.0f, e)) ++e;
+  return e;
+}
+// The E8M0 byte of a power-of-two scale 2^e, e in [-127, 127]: the fp32
+// exponent field (2^-127, the one subnormal, has field 0 = E8M0 2^-127).
+VC_DEV int e8m0_of_pow2(float s) { return (__float_as_int(s) >> 23) & 0xff; }
+
 // Packed FP8 operand layouts (see vc_attn.h): each 128-key tile of K and of
 // V is one contiguous block, and inside it every 16-byte chunk sits at
 // chunk index (logical ^ swizzle(row)).  The attention kernel's fragment
@@ -96,6 +110,13 @@ VC_DEV v4f mfma_fp8(v8i a, v8i b, v4f c) {
 }
 
 VC_DEV v4f mfma_bf16(v8bf a, v8bf b, v4f c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
+
+// The same FP8 product with E8M0 block scales 2^(sa - 127) on A and
+// 2^(sb - 127) on B (one scale for the whole operand here: every lane passes
+// the same byte), fp32 accumulate onto c.
+VC_DEV v4f mfma_fp8_scaled(v8i a, v8i b, v4f c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
 
 // Asynchronous 16-byte global -> LDS copy: lane i lands at lds_base + 16 i.
 VC_DEV void lds_dma16(const void* g, void* lds_base) {

@@ -655,12 +655,10 @@ __global__ __launch_bounds__(256) void group_apply1(const uint16_t* __restrict__
     if ((t & 63) == 0) red[t >> 6] = m;
     __syncthreads();
     m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    float s = 1.0f, inv = 1.0f;
-    if (m > 0.0f) {
-      s = m / 448.0f;
-      inv = 448.0f / m;
-    }
-    if (t == 0) k_scale[bh * nblk + j] = s;
+    // power-of-two block scale, as for vc_quantize's K
+    const int e = pow2_block_exp(m);
+    const float inv = ldexpf(1.0f, -e);
+    if (t == 0) k_scale[bh * nblk + j] = ldexpf(1.0f, e);
     uint8_t* kd = k8 + (bh * nblk * kBlk + (int64_t)j * kBlk) * D;
 #pragma unroll
     for (int r = 0; r < Mp::RPT; ++r) {

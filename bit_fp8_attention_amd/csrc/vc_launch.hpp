@@ -20,7 +20,9 @@ struct BshdOut {
 };
 
 // vc_quantize.hip
-hipError_t launch_qk_quant(const vc_shape& sh, Bshd x, uint8_t* codes, float* scale, bool pack, hipStream_t st);
+// pre: fp32 factor applied before quantising (Q: G = 8 fl(sm_scale log2 e), K: 1)
+hipError_t launch_qk_quant(const vc_shape& sh, Bshd x, float pre, uint8_t* codes, float* scale, bool pack,
+                           hipStream_t st);
 hipError_t launch_v_quant(const vc_shape& sh, Bshd v, uint8_t* v8, float* v_scale, hipStream_t st);
 hipError_t launch_pack_v_bf16(const vc_shape& sh, Bshd v, uint16_t* vt, hipStream_t st);
 hipError_t launch_expcast_codes(const float* x, const float* a, const float* b, int64_t n, int32_t row_len,
@@ -33,9 +35,10 @@ hipError_t launch_smooth_group(const vc_shape& sh, Bshd k, Bshd v, const vc_grou
                                float* r_scale, uint16_t* mu_bf16, uint32_t* mu_split, void* ws, hipStream_t st);
 
 // vc_attn_fp8.hip
-hipError_t launch_attn_fp8(const vc_shape& sh, float sm_scale, int window, uint32_t flags, const uint8_t* q8,
-                           const float* q_scale, const uint8_t* k8, const float* k_scale, const uint8_t* v8,
-                           const float* v_scale, const uint32_t* mu_split, BshdOut o, hipStream_t st);
+// q8 / q_scale carry the softmax factor G (vc_quantize); Q/K scales are powers of two
+hipError_t launch_attn_fp8(const vc_shape& sh, int window, uint32_t flags, const uint8_t* q8, const float* q_scale,
+                           const uint8_t* k8, const float* k_scale, const uint8_t* v8, const float* v_scale,
+                           const uint32_t* mu_split, BshdOut o, hipStream_t st);
 
 // vc_attn_bf16.hip
 hipError_t launch_attn_bf16(const vc_shape& sh, float sm_scale, int window, uint32_t flags, Bshd q, Bshd k,

@@ -2,7 +2,10 @@
 //
 // [OVC] "Scheduling around ExpCast" / "Fused input preparation": Q and K are
 // quantised to E4M3 with one scale per 128-token block, V with one scale per
-// head, V written transposed with keys contiguous ("Packed V").  Three
+// head, V written transposed with keys contiguous ("Packed V").  The Q/K
+// block scales are powers of two, and Q is multiplied by G = 8 fl(sm_scale
+// log2 e) first: the factors the blog folds into the code's multiply-add go
+// into the FP8 operands and the matrix core's E8M0 block scales instead.  Three
 // stream-ordered passes as on the blog: Q/K per block; V per-head maximum;
 // V convert into the packed layout.  [VC] §3.1 gives X_q = s_X * Xhat.
 //
@@ -37,6 +40,17 @@ VC_DEV uint2 codes8(uint4 w, float inv) {
   return r;
 }
 
+// 8 bf16 -> E4M3(fl(x * pre) * 2^-e): the product rounds once to fp32, the
+// power-of-two scaling is exact (only values far below E4M3's range could
+// round in it, and those encode as 0 either way)
+VC_DEV uint2 codes8_pow2(uint4 w, float pre, float p2) {
+  auto f = [&](float x) { return (x * pre) * p2; };
+  uint2 r;
+  r.x = cvt4_fp8(f(bf16_lo(w.x)), f(bf16_hi(w.x)), f(bf16_lo(w.y)), f(bf16_hi(w.y)));
+  r.y = cvt4_fp8(f(bf16_lo(w.z)), f(bf16_hi(w.z)), f(bf16_lo(w.w)), f(bf16_hi(w.w)));
+  return r;
+}
+
 VC_DEV float block_max256(float m, float* red) {
   m = wave_max(m);
   int w = threadIdx.x >> 6;
@@ -58,9 +72,12 @@ VC_DEV void scale_pair(float amax, float& s, float& inv) {
 
 // Q or K: one workgroup per (block j, head h, batch b).  PACK writes the
 // packed K layout (chunk-swizzled rows), otherwise plain row-major codes.
+// Each element is multiplied by pre first (Q: G = 8 fl(sm_scale log2 e),
+// K: 1); the block scale is the power of two pow2_block_exp picks for the
+// products' amax (fl(max |x| * pre), the max of the rounded products).
 template <int D, bool PACK>
 __global__ __launch_bounds__(256) void qk_block_quant(const uint16_t* __restrict__ x, int64_t sB, int64_t sS,
-                                                      int64_t sH, int S, int H, int nblk,
+                                                      int64_t sH, int S, int H, int nblk, float pre,
                                                       uint8_t* __restrict__ codes, float* __restrict__ scale) {
   constexpr int CPR = D / 8;             // 16-byte chunks per row
   constexpr int NCH = kBlk * CPR / 256;  // chunks per thread
@@ -76,16 +93,16 @@ __global__ __launch_bounds__(256) void qk_block_quant(const uint16_t* __restrict
     m = amax8(v[i], m);
   }
   m = block_max256(m, red);
-  float s, inv;
-  scale_pair(m, s, inv);
+  const int e = pow2_block_exp(m * pre);
+  const float p2 = ldexpf(1.0f, -e);
   const int64_t bh = (int64_t)b * H + h;
-  if (t == 0) scale[bh * nblk + j] = s;
+  if (t == 0) scale[bh * nblk + j] = ldexpf(1.0f, e);
   uint8_t* cb = codes + (bh * nblk * kBlk + (int64_t)j * kBlk) * D;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     int c = t + 256 * i, row = c / CPR, ch = c % CPR;
     const int off = PACK ? kpack_off<D>(row, ch >> 1) + (ch & 1) * 8 : row * D + ch * 8;
-    *(uint2*)(cb + off) = codes8(v[i], inv);
+    *(uint2*)(cb + off) = codes8_pow2(v[i], pre, p2);
   }
 }
 
@@ -214,19 +231,20 @@ __global__ void expcast_codes_kernel(const float* __restrict__ x, const float* _
 
 }  // namespace
 
-hipError_t launch_qk_quant(const vc_shape& sh, Bshd x, uint8_t* codes, float* scale, bool pack, hipStream_t st) {
+hipError_t launch_qk_quant(const vc_shape& sh, Bshd x, float pre, uint8_t* codes, float* scale, bool pack,
+                           hipStream_t st) {
   int nblk = (sh.S + kBlk - 1) / kBlk;
   dim3 grid(nblk, sh.H, sh.B);
   if (sh.D == 128) {
     if (pack)
-      qk_block_quant<128, true><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nblk, codes, scale);
+      qk_block_quant<128, true><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nblk, pre, codes, scale);
     else
-      qk_block_quant<128, false><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nblk, codes, scale);
+      qk_block_quant<128, false><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nblk, pre, codes, scale);
   } else {
     if (pack)
-      qk_block_quant<64, true><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nblk, codes, scale);
+      qk_block_quant<64, true><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nblk, pre, codes, scale);
     else
-      qk_block_quant<64, false><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nblk, codes, scale);
+      qk_block_quant<64, false><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nblk, pre, codes, scale);
   }
   return hipGetLastError();
 }

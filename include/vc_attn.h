@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define VC_ABI_VERSION 2
+#define VC_ABI_VERSION 3
 
 typedef enum vc_status {
   VC_OK = 0,
@@ -93,22 +93,30 @@ const char* vc_status_str(int32_t status);
  * [OVC] "Scheduling around ExpCast" and "Fused input preparation": Q and K
  * take one E4M3 scale per 128-token block, V one scale per head; the packed
  * V is stored transposed with the key dimension contiguous ("Packed V").
- * [VC] §3.1: X_q = s_X * Xhat.
+ * [VC] §3.1: X_q = s_X * Xhat.  The blog folds softmax scale, log2 e and
+ * ExpCast's factor 8 into the code's multiply-add; here they go into Q's
+ * codes, and the Q/K block scales are powers of two, which the attention
+ * kernel's block-scaled matrix product applies exactly.
  *
- * For each (b, h) and 128-token block j of Q (and of K):
- *   amax = max |x| over the block's valid rows; s = amax / 448 (fp32);
- *   code = E4M3_rne(x * (448 / amax)) (fp32 product, round-half-even);
- *   a block of zeros takes s = 1.  Rows >= S are written as code 0.
+ * sm_scale: the softmax scale (0 selects 1/sqrt(D)); must be finite, >= 0.
+ * G = 8 * fl(sm_scale * fl(log2 e)) (fp32; the factor 8 is exact).
+ * For each (b, h) and 128-token block j of Q (pre = G) and of K (pre = 1):
+ *   y = fl(x * pre); amax = max |y| over the block's valid rows;
+ *   e = the smallest integer >= -127 with amax <= 448 * 2^e (e = 0 for a
+ *   block of zeros); scale = 2^e; code = E4M3_rne(y * 2^-e).
+ *   Rows >= S are written as code 0.  So Q * G ~= q8 * q_scale and
+ *   K ~= k8 * k_scale.
  *   q8:           uint8 [B][H][S_pad][D] row-major
  *   k8:           packed K (B*H*S_pad*D bytes)
- *   q_scale, k_scale: fp32 [B][H][nblk]
- * For V: one amax per (b, h) over all S x D elements, same rule;
+ *   q_scale, k_scale: fp32 [B][H][nblk] (powers of two)
+ * For V: one amax per (b, h) over all S x D elements; s = amax / 448 (fp32),
+ * code = E4M3_rne(x * (448 / amax)), s = 1 for zeros;
  *   v8:      packed V (B*H*S_pad*D bytes; keys >= S are code 0)
  *   v_scale: fp32 [B][H][D]          (the head's scale repeated over d)
  * Any of q, k, v may have ptr == NULL to skip that operand (its outputs are
  * then ignored and may be NULL).  q8/k8/v8 must be 16-byte aligned.
  */
-int32_t vc_quantize(const vc_shape* shape, const vc_bshd* q, const vc_bshd* k, const vc_bshd* v,
+int32_t vc_quantize(const vc_shape* shape, float sm_scale, const vc_bshd* q, const vc_bshd* k, const vc_bshd* v,
                     uint8_t* q8, float* q_scale, uint8_t* k8, float* k_scale, uint8_t* v8, float* v_scale,
                     void* stream);
 
@@ -158,7 +166,8 @@ size_t vc_smooth_group_workspace_size(const vc_shape* shape, int32_t clusters);
  *     (448 / amax_d) in fp32 is stored as a bf16 pair mu_split[j][d] =
  *     hi | lo << 16, hi = bf16_rne(m), lo = bf16_rne(m - hi) (m - hi is
  *     exact), the form the attention kernel's mean product reads.  K' is
- *     quantised per 128-row block as in vc_quantize.
+ *     quantised per 128-row block as K in vc_quantize (power-of-two
+ *     scales).
  * With VC_GROUP_WARM_START, step 1 starts from the given centroids; with
  * VC_GROUP_REUSE_PERM, steps 1 and 2 are skipped and perm is an input.  The
  * two flags exclude each other (VC_ERR_UNSUPPORTED).
@@ -180,7 +189,8 @@ int32_t vc_smooth_group(const vc_shape* shape, const vc_bshd* k, const vc_bshd* 
 #define VC_ATTN_SEQUENTIAL 1u /* visit key blocks 0..nblk-1 instead of mid-window */
 
 typedef struct vc_attn_params {
-  float sm_scale;  /* softmax scale; 0 selects 1/sqrt(D) */
+  float sm_scale;  /* softmax scale; 0 selects 1/sqrt(D) (vc_attn_fwd_bf16; the FP8
+                      path takes it from q8, see vc_quantize; validated only) */
   int32_t window;  /* mid-window offset W >= 0 (default 2) */
   uint32_t flags;  /* VC_ATTN_SEQUENTIAL or 0 */
 } vc_attn_params;
@@ -191,8 +201,8 @@ typedef struct vc_attn_params {
  * [VC] §3.1 Eq. 1 (online softmax), §3.2 Eq. 6 (A <- aA + P_q R_q + r mu^T),
  * §3.3 Eq. 7 (c = clip_[0,120](Round(8(u+8)+56+beta)), beta = -0.35);
  * [OVC] "Scheduling around ExpCast" (true-score running max, scales folded
- * into one FMA, 4 codes per register), "A consistent denominator",
- * "Mid-window key traversal".
+ * into the code arithmetic, 4 codes per register), "A consistent
+ * denominator", "Mid-window key traversal".
  *
  * For each query row i (tile qt = i / 128) and key block t in the order
  *   start = min((qt | 1) + window, nblk - 1): start, start-1, ..., 0,
@@ -200,12 +210,15 @@ typedef struct vc_attn_params {
  * (query tiles 2p and 2p+1 are processed together and share one pass over
  * K/V -- [OVC] "A warp-specialized pipeline" -- so the start lies `window`
  * blocks past the pair's second diagonal block),
- * acc = FP8 dot products (matrix cores, fp32 accumulate);
- * g = fl(fl(sm_scale * log2 e) * q_scale[qt]) * k_scale[t];
- * M' = max(M, g * max acc); when M' > M the numerator and denominator are
- * rescaled by 2^(M - M');
- * code = Round(fma(8g, acc, 119.65 - 8M')) clipped below at 0 (an integer
- * conversion, no exponential, no FP8 cast); keys >= S get code 0;
+ * y = q_scale[qt] * k_scale[t] * (Q8 . K8) + (119.65 - 8 M) (matrix cores:
+ * E8M0 block scales, fp32 accumulate starting at the offset), where
+ * q_scale * k_scale * (Q8 . K8) / 8 is the log2-domain score because q8
+ * carries G (vc_quantize) -- so sm_scale does not enter here;
+ * M' = max(M, M + (max y - 119.65) / 8) (the first tile sets M from its
+ * max); when M' > M the numerator and denominator are rescaled by
+ * 2^(M - M') and y gains 8 (M - M');
+ * code = Round(y) clipped below at 0 (an integer conversion, no
+ * exponential, no FP8 cast); keys >= S get code 0;
  * A += P_code . V8 (matrix cores); r = sum of the decoded codes (the same
  * bytes, through the matrix cores against a tile of ones); l += r;
  * with V-Smooth A += r * (hi + lo) of mu_split[t], as the three bf16
@@ -215,7 +228,8 @@ typedef struct vc_attn_params {
  * rows in the original query order.
  * Inputs are those of vc_quantize (plain path: q8 .. v_scale from it) or, for
  * V-Smooth, q8/q_scale from vc_quantize and k8/k_scale, v8 = r8,
- * v_scale = r_scale, mu_split from vc_smooth_group.
+ * v_scale = r_scale, mu_split from vc_smooth_group.  q_scale and k_scale
+ * must be powers of two in [2^-127, 2^127] (as those calls write them).
  * Requires |scores| well below 2^17 in log2 units so the code never exceeds
  * 120 (the upper clip is then implicit).
  */

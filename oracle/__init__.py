@@ -63,6 +63,7 @@ def lib():
         L.vco_expcast_code_u.argtypes = [ctypes.c_double, ctypes.c_double]
         L.vco_expcast_code_u.restype = ctypes.c_int
         L.vco_quantize_blocks.argtypes = [P, i64, i32, i32, P, P]
+        L.vco_quantize_blocks_pow2.argtypes = [P, i64, i32, i32, f32, P, P]
         L.vco_quantize_v_head.argtypes = [P, i64, i32, i32, P]
         L.vco_quantize_v_head.restype = f32
         L.vco_splitmix64_stream.argtypes = [u64, i32, P]
@@ -131,8 +132,15 @@ def _head(x: np.ndarray, b: int, h: int) -> np.ndarray:
     return np.ascontiguousarray(x[b, :, h, :])
 
 
-def quantize_qk(x: np.ndarray):
-    """Per-128-token-block E4M3.  x: uint16 [B,S,H,D].
+def q_prefactor(sm_scale: float) -> float:
+    """G = 8 fl32(sm_scale * fl32(log2 e)), the factor Q carries into its codes."""
+    c1 = np.float32(np.float32(sm_scale) * np.float32(1.4426950408889634))
+    return float(np.float32(8.0) * c1)
+
+
+def quantize_qk(x: np.ndarray, pre: float = 1.0):
+    """Per-128-token-block E4M3 with power-of-two scales, after an fp32
+    multiply by `pre` (G for Q, 1 for K).  x: uint16 [B,S,H,D].
     Returns codes uint8 [B,H,S_pad,D], scales fp32 [B,H,nblk]."""
     B, S, H, D = x.shape
     nblk = (S + 127) // 128
@@ -144,7 +152,7 @@ def quantize_qk(x: np.ndarray):
             xh = _head(x, b, h)
             c = np.zeros((nblk * 128, D), np.uint8)
             s = np.zeros(nblk, np.float32)
-            L.vco_quantize_blocks(_p(xh), D, S, D, _p(c), _p(s))
+            L.vco_quantize_blocks_pow2(_p(xh), D, S, D, float(pre), _p(c), _p(s))
             codes[b, h], scales[b, h] = c, s
     return codes, scales
 
@@ -245,10 +253,12 @@ def tile_order(qt: int, nblk: int, window: int = 2, sequential: bool = False) ->
     return out
 
 
-def attn_emulate_rows(q_codes, q_scale, k_codes, k_scale, v_codes_t, v_scale, mu_scaled, S, sm_scale,
+def attn_emulate_rows(q_codes, q_scale, k_codes, k_scale, v_codes_t, v_scale, mu_scaled, S, c1,
                       rows, window=2, flags=0):
     """One head.  q_codes/k_codes [S_pad,D], v_codes_t [D,S_pad], scales as
-    produced by the quantisers, mu_scaled [nblk,D] or None.
+    produced by the quantisers, mu_scaled [nblk,D] or None.  c1 is the
+    log2-domain score per unit of q_scale * k_scale * (Qhat . Khat): 1/8 when
+    Q carries G (quantize_qk(q, q_prefactor(sm_scale))).
     Returns (out_f32 [n,D], out_bf16 bits [n,D], stats [n,2])."""
     q_codes = np.ascontiguousarray(q_codes, np.uint8)
     k_codes = np.ascontiguousarray(k_codes, np.uint8)
@@ -267,7 +277,7 @@ def attn_emulate_rows(q_codes, q_scale, k_codes, k_scale, v_codes_t, v_scale, mu
         mu_scaled = np.ascontiguousarray(mu_scaled, np.float32)
         mu_p = _p(mu_scaled)
     lib().vco_attn_emulate_rows(_p(q_codes), _p(q_scale), _p(k_codes), _p(k_scale), _p(v_codes_t),
-                                _p(v_scale), mu_p, S, D, float(sm_scale), window, flags, _p(rows), n,
+                                _p(v_scale), mu_p, S, D, float(c1), window, flags, _p(rows), n,
                                 _p(of), _p(ob), _p(st))
     return of, ob, st
 
@@ -283,7 +293,7 @@ def pipeline_head(q, k, v, b, h, *, vsmooth, nclust=64, iters=4, seed=0, sm_scal
     nblk = (S + 127) // 128
     qc = np.zeros((nblk * 128, D), np.uint8)
     qs = np.zeros(nblk, np.float32)
-    lib().vco_quantize_blocks(_p(qh), D, S, D, _p(qc), _p(qs))
+    lib().vco_quantize_blocks_pow2(_p(qh), D, S, D, q_prefactor(sm_scale), _p(qc), _p(qs))
     out = dict(q_codes=qc, q_scale=qs)
     if vsmooth:
         labels, cent = kmeans_head(_head(v, b, h), nclust, iters, seed, b, h, H)
@@ -295,12 +305,12 @@ def pipeline_head(q, k, v, b, h, *, vsmooth, nclust=64, iters=4, seed=0, sm_scal
         kh = _head(k, b, h)
         kc = np.zeros((nblk * 128, D), np.uint8)
         ks = np.zeros(nblk, np.float32)
-        lib().vco_quantize_blocks(_p(kh), D, S, D, _p(kc), _p(ks))
+        lib().vco_quantize_blocks_pow2(_p(kh), D, S, D, 1.0, _p(kc), _p(ks))
         vc = np.zeros((D, nblk * 128), np.uint8)
         s = lib().vco_quantize_v_head(_p(_head(v, b, h)), D, S, D, _p(vc))
         vs = np.full(D, s, np.float32)
         mu = None
         out.update(k_codes=kc, k_scale=ks, v_codes=vc, v_scale=vs)
-    of, ob, st = attn_emulate_rows(qc, qs, kc, ks, vc, vs, mu, S, sm_scale, rows, window, flags)
+    of, ob, st = attn_emulate_rows(qc, qs, kc, ks, vc, vs, mu, S, 0.125, rows, window, flags)
     out.update(out_f32=of, out_bf16=ob, stats=st, rows=rows)
     return out

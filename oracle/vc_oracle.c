@@ -143,8 +143,15 @@ EXPORT int vco_expcast_code_u(double u, double beta) {
 /* ------------------------------------------------------------------------ */
 /* Quantizers, [OVC] "Scheduling around ExpCast": Q and K take one scale per */
 /* 128-token block, V one scale per head; X_q = s_X * Xhat ([VC] §3.1).      */
-/* Reading: s = amax/448 and the codes are E4M3(x * (448/amax)) with both    */
-/* quotients rounded to fp32; a block of zeros takes s = 1.                  */
+/* The pages leave the value of a scale open.  Readings:                     */
+/*  - V (per head) and the V-Smooth residual (per channel): s = amax/448,    */
+/*    codes E4M3(x * (448/amax)), both quotients rounded to fp32;            */
+/*  - Q and K blocks: s = 2^e, the smallest power of two (e >= -127) with    */
+/*    amax <= 448 * 2^e, codes E4M3(x * 2^-e) -- a scale a block-scaled      */
+/*    matrix product applies exactly.  Q is first multiplied (fp32) by       */
+/*    G = 8 fl(sm_scale * log2 e), the factor [OVC] folds into the code's     */
+/*    multiply-add, so 8 * (log2-domain score) = s_Q s_K (Qhat . Khat).      */
+/* A block of zeros takes s = 1.                                             */
 /* ------------------------------------------------------------------------ */
 
 static void scale_pair(float amax, float* s, float* inv) {
@@ -157,8 +164,40 @@ static void scale_pair(float amax, float* s, float* inv) {
   }
 }
 
+/* The power-of-two block exponent: smallest e >= -127 with amax <= 448*2^e. */
+static int pow2_block_exp(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  int e = ilogbf(amax) - 9; /* 448 * 2^(E-9) < 2^E <= amax: one step too low */
+  if (e < -127) e = -127;
+  while (amax > ldexpf(448.0f, e)) ++e;
+  return e;
+}
+
 /*
- * One head.  x: bf16 rows, row r at x + r*ld (D contiguous).
+ * One head, Q or K.  x: bf16 rows, row r at x + r*ld (D contiguous); pre is
+ * the fp32 factor applied first (G for Q, 1 for K).
+ * Out: codes [nblk*128][D] (rows >= S are zero), scale [nblk] = 2^e.
+ */
+EXPORT void vco_quantize_blocks_pow2(const uint16_t* x, int64_t ld, int32_t S, int32_t D, float pre,
+                                     uint8_t* codes, float* scale) {
+  int32_t nblk = (S + 127) / 128;
+  for (int32_t j = 0; j < nblk; ++j) {
+    int32_t r0 = j * 128, r1 = r0 + 128 < S ? r0 + 128 : S;
+    float amax = 0.0f;
+    for (int32_t r = r0; r < r1; ++r)
+      for (int32_t d = 0; d < D; ++d) amax = fmaxf(amax, fabsf(bf16_to_f32(x[r * ld + d]) * pre));
+    int e = pow2_block_exp(amax);
+    scale[j] = ldexpf(1.0f, e);
+    for (int32_t r = r0; r < j * 128 + 128; ++r)
+      for (int32_t d = 0; d < D; ++d)
+        codes[(int64_t)r * D + d] =
+            (r < S) ? vco_e4m3_encode(ldexpf(bf16_to_f32(x[r * ld + d]) * pre, -e)) : 0;
+  }
+}
+
+/*
+ * One head, amax/448 rule (kept for reference comparisons).  x: bf16 rows,
+ * row r at x + r*ld (D contiguous).
  * Out: codes [nblk*128][D] (rows >= S are zero), scale [nblk].
  */
 EXPORT void vco_quantize_blocks(const uint16_t* x, int64_t ld, int32_t S, int32_t D, uint8_t* codes,
@@ -369,7 +408,7 @@ EXPORT void vco_smooth_apply(const uint16_t* k, int64_t ldk, const uint16_t* v, 
   uint16_t* kp = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)S * D);
   for (int32_t r = 0; r < S; ++r)
     for (int32_t d = 0; d < D; ++d) kp[(int64_t)r * D + d] = k[(int64_t)perm[r] * ldk + d];
-  vco_quantize_blocks(kp, D, S, D, k_codes, k_scale);
+  vco_quantize_blocks_pow2(kp, D, S, D, 1.0f, k_codes, k_scale);
   free(kp);
   free(R);
   free(amax);
@@ -413,16 +452,17 @@ EXPORT void vco_tile_order(int32_t qt, int32_t nblk, int32_t window, int32_t seq
  * q_codes [S_pad][D] with q_scale [nblk] (query rows in token order),
  * k_codes [S_pad][D] with k_scale [nblk], v_codes_t [D][S_pad] with
  * v_scale [D], mu_scaled [nblk][D] or NULL for the plain path.
+ * c1: the log2-domain score per unit of q_scale * k_scale * (Qhat.Khat):
+ * fl(sm_scale * log2 e) for codes of the raw Q, 1/8 for Q carrying G.
  * rows: n query indices.  Out: out_f32 [n][D] (pre-rounding output, fp32)
  * and out_bf16 [n][D]; stats (may be NULL) [n][2] = {rescales, final max M}.
  */
 EXPORT void vco_attn_emulate_rows(const uint8_t* q_codes, const float* q_scale, const uint8_t* k_codes,
                                   const float* k_scale, const uint8_t* v_codes_t, const float* v_scale,
-                                  const float* mu_scaled, int32_t S, int32_t D, float sm_scale,
+                                  const float* mu_scaled, int32_t S, int32_t D, float c1,
                                   int32_t window, int32_t flags, const int32_t* rows, int32_t n,
                                   float* out_f32, uint16_t* out_bf16, double* stats) {
   int32_t nblk = (S + 127) / 128, S_pad = nblk * 128;
-  const float log2e = 1.44269504088896340736f;
   double dq[256];
   e4m3_table_init();
 #pragma omp parallel for schedule(dynamic, 1) private(dq)
@@ -436,7 +476,7 @@ EXPORT void vco_attn_emulate_rows(const uint8_t* q_codes, const float* q_scale, 
     double l = 0.0;
     float M = -INFINITY;
     int32_t rescales = 0;
-    float c2 = (sm_scale * log2e) * q_scale[qt];
+    float c2 = c1 * q_scale[qt];
     for (int32_t d = 0; d < D; ++d) dq[d] = DEC(q_codes[(int64_t)i * D + d]);
     for (int32_t oi = 0; oi < nblk; ++oi) {
       int32_t t = order[oi];

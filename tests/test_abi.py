@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(vc):
 
 
 def test_abi_version_and_status_strings(vc):
-    assert vc.vc_abi_version() == vc.ABI_VERSION == 2
+    assert vc.vc_abi_version() == vc.ABI_VERSION == 3
     assert vc.vc_status_str(0) == "VC_OK"
     for s in range(1, 7):
         assert vc.vc_status_str(s).startswith("VC_ERR_")
@@ -65,27 +65,31 @@ def test_quantize_validation(vc):
     none = m.vc_bshd(None, 0, 0, 0)
     st = ctypes.c_void_p(0)
     P = ctypes.c_void_p
-    assert L.vc_quantize(None, None, None, None, None, None, None, None, None, None, st) == 1
+    assert L.vc_quantize(None, 0.0, None, None, None, None, None, None, None, None, None, st) == 1
     bad_d = m.vc_shape(1, 2, 256, 96)
-    assert L.vc_quantize(ctypes.byref(bad_d), ctypes.byref(ok), ctypes.byref(none), ctypes.byref(none),
+    assert L.vc_quantize(ctypes.byref(bad_d), 0.0, ctypes.byref(ok), ctypes.byref(none), ctypes.byref(none),
                          P(FAKE), P(FAKE), None, None, None, None, st) == 2
     bad_s = m.vc_shape(1, 2, 0, 128)
-    assert L.vc_quantize(ctypes.byref(bad_s), ctypes.byref(ok), ctypes.byref(none), ctypes.byref(none),
+    assert L.vc_quantize(ctypes.byref(bad_s), 0.0, ctypes.byref(ok), ctypes.byref(none), ctypes.byref(none),
                          P(FAKE), P(FAKE), None, None, None, None, st) == 2
     sh = _shape()
     # q given without its outputs
-    assert L.vc_quantize(ctypes.byref(sh), ctypes.byref(ok), ctypes.byref(none), ctypes.byref(none),
+    assert L.vc_quantize(ctypes.byref(sh), 0.0, ctypes.byref(ok), ctypes.byref(none), ctypes.byref(none),
                          None, None, None, None, None, None, st) == 1
     # misaligned input pointer and stride
     mis = m.vc_bshd(FAKE + 2, 256 * 2 * 128, 2 * 128, 128)
-    assert L.vc_quantize(ctypes.byref(sh), ctypes.byref(mis), ctypes.byref(none), ctypes.byref(none),
+    assert L.vc_quantize(ctypes.byref(sh), 0.0, ctypes.byref(mis), ctypes.byref(none), ctypes.byref(none),
                          P(FAKE), P(FAKE), None, None, None, None, st) == 3
     mis2 = m.vc_bshd(FAKE, 256 * 2 * 128, 2 * 128 + 4, 128)
-    assert L.vc_quantize(ctypes.byref(sh), ctypes.byref(mis2), ctypes.byref(none), ctypes.byref(none),
+    assert L.vc_quantize(ctypes.byref(sh), 0.0, ctypes.byref(mis2), ctypes.byref(none), ctypes.byref(none),
                          P(FAKE), P(FAKE), None, None, None, None, st) == 3
     # misaligned output codes
-    assert L.vc_quantize(ctypes.byref(sh), ctypes.byref(ok), ctypes.byref(none), ctypes.byref(none),
+    assert L.vc_quantize(ctypes.byref(sh), 0.0, ctypes.byref(ok), ctypes.byref(none), ctypes.byref(none),
                          P(FAKE + 8), P(FAKE), None, None, None, None, st) == 3
+    # softmax scale negative, infinite or NaN
+    for bad in (-1.0, float("inf"), float("nan")):
+        assert L.vc_quantize(ctypes.byref(sh), bad, ctypes.byref(ok), ctypes.byref(none), ctypes.byref(none),
+                             P(FAKE), P(FAKE), None, None, None, None, st) == 4
 
 
 def test_smooth_group_validation(vc):

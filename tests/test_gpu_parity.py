@@ -101,10 +101,12 @@ def test_quantize_bitexact(vc, B, S, H, D, kind):
         q, k, v = vcsynth.make_qkv("plain", S=S, H=H)
     else:
         q, k, v = vcsynth.random_qkv(B, S, H, D, seed=S + H, v_kind="t3" if kind == "t3" else "normal")
-    out = vc.vc_quantize(q.cuda(), k.cuda(), v.cuda())
+    # Q's codes carry G = 8 fl(sm log2 e); a non-default scale on some cases
+    sm = float(np.float32(0.3 if kind == "t3" else 1 / np.sqrt(D)))
+    out = vc.vc_quantize(q.cuda(), k.cuda(), v.cuda(), sm_scale=sm)
     torch.cuda.synchronize()
     qb, kb, vb = (vcsynth.bf16_bits(x) for x in (q, k, v))
-    codes, sc = oracle.quantize_qk(qb)
+    codes, sc = oracle.quantize_qk(qb, oracle.q_prefactor(sm))
     assert (_np(out["q8"]) == codes).all()
     assert (_np(out["q_scale"]) == sc).all()
     codes, sc = oracle.quantize_qk(kb)
@@ -122,9 +124,10 @@ def test_quantize_strided_views(vc):
     fused = torch.randn((B, S, 3, H, D), generator=g).to(torch.bfloat16)
     fd = fused.cuda()
     q, k, v = fd[:, :, 0], fd[:, :, 1], fd[:, :, 2]
-    out = vc.vc_quantize(q, k, v)
+    sm = float(np.float32(1 / np.sqrt(D)))
+    out = vc.vc_quantize(q, k, v, sm_scale=sm)
     torch.cuda.synchronize()
-    codes, sc = oracle.quantize_qk(vcsynth.bf16_bits(fused[:, :, 0]))
+    codes, sc = oracle.quantize_qk(vcsynth.bf16_bits(fused[:, :, 0]), oracle.q_prefactor(sm))
     assert (_np(out["q8"]) == codes).all() and (_np(out["q_scale"]) == sc).all()
     codes, sc = oracle.quantize_qk(vcsynth.bf16_bits(fused[:, :, 1]))
     assert (unpack_k(_np(out["k8"]), D) == codes).all() and (_np(out["k_scale"]) == sc).all()
@@ -138,9 +141,9 @@ def test_quantize_strided_views(vc):
 
 def _plain_case(vc, q, k, v, sm_scale, window=2, sequential=False, rows_per_head=None, seed=0):
     B, S, H, D = q.shape
-    qz = vc.vc_quantize(q.cuda(), k.cuda(), v.cuda())
+    qz = vc.vc_quantize(q.cuda(), k.cuda(), v.cuda(), sm_scale=sm_scale)
     o = vc.vc_attn_fwd(qz["q8"], qz["q_scale"], qz["k8"], qz["k_scale"], qz["v8"], qz["v_scale"], None, S=S,
-                       sm_scale=sm_scale, window=window, sequential=sequential)
+                       window=window, sequential=sequential)
     torch.cuda.synchronize()
     og = _bf16_f32(o)
     qb, kb, vb = (vcsynth.bf16_bits(x) for x in (q, k, v))
@@ -321,10 +324,10 @@ def test_smooth_group_reuse_perm_bitexact(vc, S, H, D):
 
 def _vsmooth_case(vc, q, k, v, clusters, iters, seed, sm, rows_per_head=None, window=2):
     B, S, H, D = q.shape
-    qz = vc.vc_quantize(q.cuda())
+    qz = vc.vc_quantize(q.cuda(), sm_scale=sm)
     g = vc.vc_smooth_group(k.cuda(), v.cuda(), clusters, iters, seed)
     o = vc.vc_attn_fwd(qz["q8"], qz["q_scale"], g["k8"], g["k_scale"], g["r8"], g["r_scale"], g["mu_split"], S=S,
-                       sm_scale=sm, window=window)
+                       window=window)
     torch.cuda.synchronize()
     og = _bf16_f32(o)
     qb, kb, vb = (vcsynth.bf16_bits(x) for x in (q, k, v))
@@ -372,7 +375,8 @@ def test_attn_vsmooth_video_envelope(vc):
     ref = exact.attention_rows(qf, kf, vf, sm, rows)
     # dequantised operands: scores and values the FP8 path actually sees
     blk = np.arange(S) // 128
-    qd = oracle.e4m3_decode(res["q_codes"][:S]) * res["q_scale"][blk][:, None]
+    # Q's codes carry G = 8 fl(sm log2 e): divide it back out
+    qd = oracle.e4m3_decode(res["q_codes"][:S]) * res["q_scale"][blk][:, None] / oracle.q_prefactor(sm)
     perm = res["perm"]
     kd_p = oracle.e4m3_decode(res["k_codes"][:S]) * res["k_scale"][blk][:, None]
     vd_p = (oracle.e4m3_decode(res["r_codes"][:, :S]).T + res["mu_scaled"][blk]) * res["r_scale"][None, :]

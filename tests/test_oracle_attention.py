@@ -143,14 +143,14 @@ def test_emulation_integer_scores_plain(S, D, order):
     q, k = _integer_qk(S, D, seed=S + D)
     v = np.random.default_rng(5).standard_normal((S, D)).astype(np.float32) * 3
     qb, kb, vb = _bits(q), _bits(k), _bits(v)
-    sm = _unit_fold_scale()
     qc, qs = oracle.quantize_qk(qb[None, :, None, :])
     kc, ks = oracle.quantize_qk(kb[None, :, None, :])
     vc, vs = oracle.quantize_v(vb[None, :, None, :])
     assert (qs == 1).all() and (ks == 1).all()
     rows = np.arange(S)
+    # c1 = 1: the log2-domain score is the integer dot product itself
     of, _, st = oracle.attn_emulate_rows(qc[0, 0], qs[0, 0], kc[0, 0], ks[0, 0], vc[0, 0], vs[0, 0], None,
-                                         S, sm, rows, window=2,
+                                         S, 1.0, rows, window=2,
                                          flags=oracle.SEQUENTIAL if order == "seq" else 0)
     # exact attention with base-2 weights on the dequantised values
     v_deq = oracle.e4m3_decode(vc[0, 0, :, :S]).T * vs[0, 0][None, :]
@@ -168,9 +168,11 @@ def test_emulation_integer_scores_vsmooth():
     vb = vcsynth.bf16_bits(vt)[0, :S, 0, :D].copy()
     qb, kb = _bits(q), _bits(k)
     sm = _unit_fold_scale()
+    assert oracle.q_prefactor(sm) == 8.0
     res = oracle.pipeline_head(qb[None, :, None], kb[None, :, None], vb[None, :, None], 0, 0, vsmooth=True,
                                nclust=8, iters=3, seed=1000, sm_scale=sm)
-    assert (res["q_scale"] == 1).all() and (res["k_scale"] == 1).all()
+    # Q carries G = 8: amax 8 * 448 = 448 * 2^3, so the same codes under scale 8
+    assert (res["q_scale"] == 8).all() and (res["k_scale"] == 1).all()
     perm = res["perm"]
     # dequantised permuted values: s_R * (R_hat + mu_scaled of the row's block)
     blk = np.arange(S) // 128
@@ -214,7 +216,8 @@ def test_emulation_within_eq15_envelope():
     qb, kb, vb = (vcsynth.bf16_bits(x) for x in (q, k, v))
     res = oracle.pipeline_head(qb, kb, vb, 0, 0, vsmooth=False, sm_scale=sm)
     blk = np.arange(S) // 128
-    qd = oracle.e4m3_decode(res["q_codes"][:S]) * res["q_scale"][blk][:, None]
+    # Q's codes carry G = 8 fl(sm log2 e): divide it back out
+    qd = oracle.e4m3_decode(res["q_codes"][:S]) * res["q_scale"][blk][:, None] / oracle.q_prefactor(sm)
     kd = oracle.e4m3_decode(res["k_codes"][:S]) * res["k_scale"][blk][:, None]
     vd = oracle.e4m3_decode(res["v_codes"][:, :S]).T * res["v_scale"][None, :]
     ref = exact.attention_rows(qd, kd, vd, sm)
