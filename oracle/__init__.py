@@ -33,6 +33,11 @@ _lib = None
 SEQUENTIAL = 1
 EXACT_EXP = 2
 
+# preprocessing flags (vco_prep_rows)
+PREP_ROPE = 1
+PREP_HADAMARD = 2
+PREP_CENTER = 4
+
 
 def build(force: bool = True) -> str:
     """Compile the C oracle with gcc (IEEE fp32, no contraction)."""
@@ -64,6 +69,8 @@ def lib():
         L.vco_expcast_code_u.restype = ctypes.c_int
         L.vco_quantize_blocks.argtypes = [P, i64, i32, i32, P, P]
         L.vco_quantize_blocks_pow2.argtypes = [P, i64, i32, i32, f32, P, P]
+        L.vco_prep_rows.argtypes = [P, i64, i32, i32, i32, P, P, P, P]
+        L.vco_quantize_f32_blocks_pow2.argtypes = [P, i32, i32, f32, P, P]
         L.vco_quantize_v_head.argtypes = [P, i64, i32, i32, P]
         L.vco_quantize_v_head.restype = f32
         L.vco_splitmix64_stream.argtypes = [u64, i32, P]
@@ -155,6 +162,43 @@ def quantize_qk(x: np.ndarray, pre: float = 1.0):
             L.vco_quantize_blocks_pow2(_p(xh), D, S, D, float(pre), _p(c), _p(s))
             codes[b, h], scales[b, h] = c, s
     return codes, scales
+
+
+def prep_rows(x_head: np.ndarray, flags: int, rope_cos=None, rope_sin=None):
+    """One head's rows x_head uint16 (bf16 bits) [S,D], token position = row:
+    RoPE (PREP_ROPE, tables fp32 [S, D/2]), centring (PREP_CENTER), then the
+    unnormalised Hadamard rotation (PREP_HADAMARD).  Returns (y fp32 [S,D],
+    channel mean fp32 [D] or None)."""
+    x_head = np.ascontiguousarray(x_head, np.uint16)
+    S, D = x_head.shape
+    y = np.zeros((S, D), np.float32)
+    mean = np.zeros(D, np.float32)
+    cp = sp = None
+    if flags & PREP_ROPE:
+        rope_cos = np.ascontiguousarray(rope_cos, np.float32)
+        rope_sin = np.ascontiguousarray(rope_sin, np.float32)
+        assert rope_cos.shape == (S, D // 2) and rope_sin.shape == (S, D // 2)
+        cp, sp = _p(rope_cos), _p(rope_sin)
+    lib().vco_prep_rows(_p(x_head), D, S, D, int(flags), cp, sp, _p(y), _p(mean))
+    return y, (mean if flags & PREP_CENTER else None)
+
+
+def quantize_f32_pow2(y: np.ndarray, pre: float = 1.0):
+    """Power-of-two block quantiser of one head's fp32 rows y [S,D] (after an
+    fp32 multiply by pre).  Returns codes uint8 [S_pad,D], scales fp32 [nblk]."""
+    y = np.ascontiguousarray(y, np.float32)
+    S, D = y.shape
+    nblk = (S + 127) // 128
+    c = np.zeros((nblk * 128, D), np.uint8)
+    sc = np.zeros(nblk, np.float32)
+    lib().vco_quantize_f32_blocks_pow2(_p(y), S, D, float(pre), _p(c), _p(sc))
+    return c, sc
+
+
+def q_prefactor_prep(sm_scale: float, D: int, flags: int) -> float:
+    """Q's pre-factor: G, divided by D (exactly) when the rotation is on."""
+    G = q_prefactor(sm_scale)
+    return float(np.float32(G) / np.float32(D)) if flags & PREP_HADAMARD else G
 
 
 def quantize_v(x: np.ndarray):
@@ -283,7 +327,7 @@ def attn_emulate_rows(q_codes, q_scale, k_codes, k_scale, v_codes_t, v_scale, mu
 
 
 def pipeline_head(q, k, v, b, h, *, vsmooth, nclust=64, iters=4, seed=0, sm_scale=None, rows=None,
-                  window=2, flags=0):
+                  window=2, flags=0, prep=0, rope_cos=None, rope_sin=None):
     """Full oracle pipeline for one head from bf16 inputs [B,S,H,D]:
     quantise, (group,) emulate the listed query rows.  Returns a dict."""
     B, S, H, D = q.shape
@@ -291,21 +335,32 @@ def pipeline_head(q, k, v, b, h, *, vsmooth, nclust=64, iters=4, seed=0, sm_scal
     rows = np.arange(S) if rows is None else np.asarray(rows)
     qh = _head(q, b, h)
     nblk = (S + 127) // 128
-    qc = np.zeros((nblk * 128, D), np.uint8)
-    qs = np.zeros(nblk, np.float32)
-    lib().vco_quantize_blocks_pow2(_p(qh), D, S, D, q_prefactor(sm_scale), _p(qc), _p(qs))
+    if prep:
+        # Q: RoPE and rotation (no centring); K: all three, before the gather
+        yq, _ = prep_rows(qh, prep & ~PREP_CENTER, rope_cos, rope_sin)
+        qc, qs = quantize_f32_pow2(yq, q_prefactor_prep(sm_scale, D, prep))
+        yk, kmean = prep_rows(_head(k, b, h), prep, rope_cos, rope_sin)
+    else:
+        qc = np.zeros((nblk * 128, D), np.uint8)
+        qs = np.zeros(nblk, np.float32)
+        lib().vco_quantize_blocks_pow2(_p(qh), D, S, D, q_prefactor(sm_scale), _p(qc), _p(qs))
     out = dict(q_codes=qc, q_scale=qs)
     if vsmooth:
         labels, cent = kmeans_head(_head(v, b, h), nclust, iters, seed, b, h, H)
         perm = argsort_labels(labels, nclust)
         g = smooth_apply_head(_head(k, b, h), _head(v, b, h), perm)
+        if prep:  # K' = prepared K gathered by pi
+            g["k_codes"], g["k_scale"] = quantize_f32_pow2(yk[perm])
         out.update(g, labels=labels, centroids=cent, perm=perm)
         kc, ks, vc, vs, mu = g["k_codes"], g["k_scale"], g["r_codes"], g["r_scale"], g["mu_scaled"]
     else:
         kh = _head(k, b, h)
-        kc = np.zeros((nblk * 128, D), np.uint8)
-        ks = np.zeros(nblk, np.float32)
-        lib().vco_quantize_blocks_pow2(_p(kh), D, S, D, 1.0, _p(kc), _p(ks))
+        if prep:
+            kc, ks = quantize_f32_pow2(yk)
+        else:
+            kc = np.zeros((nblk * 128, D), np.uint8)
+            ks = np.zeros(nblk, np.float32)
+            lib().vco_quantize_blocks_pow2(_p(kh), D, S, D, 1.0, _p(kc), _p(ks))
         vc = np.zeros((D, nblk * 128), np.uint8)
         s = lib().vco_quantize_v_head(_p(_head(v, b, h)), D, S, D, _p(vc))
         vs = np.full(D, s, np.float32)

@@ -195,6 +195,91 @@ EXPORT void vco_quantize_blocks_pow2(const uint16_t* x, int64_t ld, int32_t S, i
   }
 }
 
+/* ------------------------------------------------------------------------ */
+/* Preprocessing of Q and K ahead of the quantiser, [VC] §3.4 and App. B:   */
+/* rotary embedding, the key channel mean (centring) and the QK Hadamard    */
+/* rotation.  The pages leave their exact forms open.  Readings:            */
+/*  - RoPE rotates the pairs (2i, 2i+1) of a row by the caller's angle for   */
+/*    the token's position p: (a, b) -> (a c - b s, a s + b c), c, s =       */
+/*    cos/sin[p][i], each product and difference rounded to fp32;            */
+/*  - centring subtracts from every key the channel mean over the head's S   */
+/*    keys (after RoPE): sums in 64-bit fixed point with 24 fraction bits    */
+/*    (order independent), mean = fl32(sum / (S 2^24)) in fp64.  Any vector  */
+/*    subtracted from all keys leaves each softmax row unchanged;            */
+/*  - the rotation is the unnormalised Walsh-Hadamard transform over D       */
+/*    (H H^T = D I, so scores grow by exactly D, which Q's pre-factor takes  */
+/*    back), computed as radix-2 butterflies (a, b) -> (a + b, a - b) over    */
+/*    strides 1, 2, ..., D/2 in that order, in fp32.                         */
+/* ------------------------------------------------------------------------ */
+
+static int64_t fx24(float v);  /* 64-bit fixed point, 24 fraction bits (k-means section) */
+
+#define VCO_PREP_ROPE 1
+#define VCO_PREP_HADAMARD 2
+#define VCO_PREP_CENTER 4
+
+static void rope_row(float* v, int32_t D, const float* c, const float* s) {
+  for (int32_t i = 0; i < D / 2; ++i) {
+    float a = v[2 * i], b = v[2 * i + 1];
+    float ac = a * c[i], bs = b * s[i], as = a * s[i], bc = b * c[i];
+    v[2 * i] = ac - bs;
+    v[2 * i + 1] = as + bc;
+  }
+}
+
+static void fwht_row(float* v, int32_t D) {
+  for (int32_t h = 1; h < D; h <<= 1)
+    for (int32_t i = 0; i < D; ++i)
+      if (!(i & h)) {
+        float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+}
+
+/*
+ * One head: x bf16 rows (row r at x + r*ld, token position r), flags as
+ * above, cos/sin fp32 [S][D/2] (used with VCO_PREP_ROPE).  Out y fp32 [S][D]
+ * in the order RoPE, centring, rotation; mean (if not NULL) gets the channel
+ * mean used for centring.
+ */
+EXPORT void vco_prep_rows(const uint16_t* x, int64_t ld, int32_t S, int32_t D, int32_t flags, const float* cosb,
+                          const float* sinb, float* y, float* mean) {
+  for (int32_t r = 0; r < S; ++r) {
+    float* v = y + (int64_t)r * D;
+    for (int32_t d = 0; d < D; ++d) v[d] = bf16_to_f32(x[r * ld + d]);
+    if (flags & VCO_PREP_ROPE) rope_row(v, D, cosb + (int64_t)r * (D / 2), sinb + (int64_t)r * (D / 2));
+  }
+  if (flags & VCO_PREP_CENTER) {
+    for (int32_t d = 0; d < D; ++d) {
+      int64_t sum = 0;
+      for (int32_t r = 0; r < S; ++r) sum += fx24(y[(int64_t)r * D + d]);
+      float c = (float)((double)sum / ((double)S * 16777216.0));
+      if (mean) mean[d] = c;
+      for (int32_t r = 0; r < S; ++r) y[(int64_t)r * D + d] -= c;
+    }
+  }
+  if (flags & VCO_PREP_HADAMARD)
+    for (int32_t r = 0; r < S; ++r) fwht_row(y + (int64_t)r * D, D);
+}
+
+/* Power-of-two block quantiser of fp32 rows y [S][D] (as vco_quantize_blocks_pow2, after pre). */
+EXPORT void vco_quantize_f32_blocks_pow2(const float* y, int32_t S, int32_t D, float pre, uint8_t* codes,
+                                         float* scale) {
+  int32_t nblk = (S + 127) / 128;
+  for (int32_t j = 0; j < nblk; ++j) {
+    int32_t r0 = j * 128, r1 = r0 + 128 < S ? r0 + 128 : S;
+    float amax = 0.0f;
+    for (int32_t r = r0; r < r1; ++r)
+      for (int32_t d = 0; d < D; ++d) amax = fmaxf(amax, fabsf(y[(int64_t)r * D + d] * pre));
+    int e = pow2_block_exp(amax);
+    scale[j] = ldexpf(1.0f, e);
+    for (int32_t r = r0; r < j * 128 + 128; ++r)
+      for (int32_t d = 0; d < D; ++d)
+        codes[(int64_t)r * D + d] = (r < S) ? vco_e4m3_encode(ldexpf(y[(int64_t)r * D + d] * pre, -e)) : 0;
+  }
+}
+
 /*
  * One head, amax/448 rule (kept for reference comparisons).  x: bf16 rows,
  * row r at x + r*ld (D contiguous).
