@@ -28,7 +28,7 @@ VC_OK = 0
 VC_ATTN_SEQUENTIAL = 1
 VC_GROUP_WARM_START = 1
 VC_GROUP_REUSE_PERM = 2
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class VcError(RuntimeError):
@@ -54,6 +54,16 @@ class vc_group_params(ctypes.Structure):
                 ("flags", ctypes.c_uint32)]
 
 
+VC_PREP_ROPE = 1
+VC_PREP_HADAMARD = 2
+VC_PREP_K_CENTER = 4
+
+
+class vc_prep_params(ctypes.Structure):
+    _fields_ = [("flags", ctypes.c_uint32), ("rope_cos", ctypes.c_void_p), ("rope_sin", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
 class vc_attn_params(ctypes.Structure):
     _fields_ = [("sm_scale", ctypes.c_float), ("window", ctypes.c_int32), ("flags", ctypes.c_uint32)]
 
@@ -70,11 +80,13 @@ def lib():
         L.vc_abi_version.restype = i32
         L.vc_status_str.argtypes = [i32]
         L.vc_status_str.restype = ctypes.c_char_p
-        L.vc_quantize.argtypes = [P, f32] + [P] * 10
+        L.vc_quantize.argtypes = [P, f32] + [P] * 11
+        L.vc_prep_workspace_size.argtypes = [P]
+        L.vc_prep_workspace_size.restype = sz
         L.vc_quantize.restype = i32
         L.vc_smooth_group_workspace_size.argtypes = [P, i32]
         L.vc_smooth_group_workspace_size.restype = sz
-        L.vc_smooth_group.argtypes = [P] * 14 + [sz, P]
+        L.vc_smooth_group.argtypes = [P] * 15 + [sz, P]
         L.vc_smooth_group.restype = i32
         L.vc_attn_fwd.argtypes = [P] * 11
         L.vc_attn_fwd.restype = i32
@@ -134,9 +146,31 @@ def nblk_of(S: int) -> int:
 # vc_quantize
 # --------------------------------------------------------------------------- #
 
-def vc_quantize(q=None, k=None, v=None, *, sm_scale: float = 0.0, out=None):
+def _prep(prep, ref, with_k: bool):
+    """A vc_prep_params for prep = None, or a dict with keys flags, and with
+    VC_PREP_ROPE rope_cos / rope_sin (fp32 [S, D/2] device tensors); the
+    centring workspace is allocated here when needed (or taken from
+    prep["workspace"])."""
+    if not prep or not prep.get("flags"):
+        return None, None
+    flags = int(prep["flags"])
+    cs, sn = prep.get("rope_cos"), prep.get("rope_sin")
+    for t in (cs, sn):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError("rope tables must be contiguous fp32 [S, D/2]")
+    ws = prep.get("workspace")
+    if with_k and (flags & VC_PREP_K_CENTER) and ws is None:
+        sh = _shape_of(ref)
+        ws = torch.empty(max(int(lib().vc_prep_workspace_size(ctypes.byref(sh))), 8), dtype=torch.uint8,
+                         device=ref.device)
+    pp = vc_prep_params(flags, _ptr(cs), _ptr(sn), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size())
+    return pp, ws
+
+
+def vc_quantize(q=None, k=None, v=None, *, sm_scale: float = 0.0, prep=None, out=None):
     """FP8 operands.  q, k, v: bf16 [B,S,H,D] (any may be None); sm_scale is
-    the softmax scale the attention will use (0: 1/sqrt(D)), folded into q8.
+    the softmax scale the attention will use (0: 1/sqrt(D)), folded into q8;
+    prep: None or {"flags": VC_PREP_*, "rope_cos": ..., "rope_sin": ...}.
     Returns dict with q8, q_scale, k8, k_scale, v8, v_scale (see vc_attn.h)."""
     ref = next(x for x in (q, k, v) if x is not None)
     sh = _shape_of(ref)
@@ -154,7 +188,9 @@ def vc_quantize(q=None, k=None, v=None, *, sm_scale: float = 0.0, out=None):
         o.setdefault("v8", torch.empty((B, H, D, nb * 128), dtype=torch.uint8, device=dev))
         o.setdefault("v_scale", torch.empty((B, H, D), dtype=torch.float32, device=dev))
     qd, kd, vd = _bshd(q), _bshd(k), _bshd(v)
-    st = lib().vc_quantize(ctypes.byref(sh), float(sm_scale), ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd),
+    pp, _ws = _prep(prep, ref, k is not None)
+    st = lib().vc_quantize(ctypes.byref(sh), float(sm_scale), ctypes.byref(pp) if pp is not None else None,
+                           ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd),
                            _ptr(o.get("q8")), _ptr(o.get("q_scale")), _ptr(o.get("k8")), _ptr(o.get("k_scale")),
                            _ptr(o.get("v8")), _ptr(o.get("v_scale")), _stream())
     _check(st, "vc_quantize")
@@ -171,7 +207,7 @@ def vc_smooth_group_workspace_size(B: int, H: int, S: int, D: int, clusters: int
 
 
 def vc_smooth_group(k, v, clusters: int, iters: int, seed: int, *, workspace=None, out=None, warm_start=None,
-                    reuse_perm=None):
+                    reuse_perm=None, prep=None):
     """V-Smooth grouping.  k, v: bf16 [B,S,H,D].  Returns dict with centroids,
     labels, perm, k8, k_scale, r8, r_scale, mu_bf16, mu_split (int32 storage
     of the uint32 pairs bf16(m) | bf16(m - bf16(m)) << 16 of each scaled block
@@ -218,7 +254,9 @@ def vc_smooth_group(k, v, clusters: int, iters: int, seed: int, *, workspace=Non
         workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
     p = vc_group_params(clusters, iters, seed, flags)
     kd, vd = _bshd(k), _bshd(v)
+    pp, _ws = _prep(prep, k, True)
     st = lib().vc_smooth_group(ctypes.byref(sh), ctypes.byref(kd), ctypes.byref(vd), ctypes.byref(p),
+                               ctypes.byref(pp) if pp is not None else None,
                                _ptr(o.get("centroids")), _ptr(o.get("labels")), _ptr(o["perm"]), _ptr(o["k8"]),
                                _ptr(o["k_scale"]), _ptr(o["r8"]), _ptr(o["r_scale"]), _ptr(o["mu_bf16"]),
                                _ptr(o["mu_split"]), _ptr(workspace), workspace.numel() * workspace.element_size(),

@@ -60,13 +60,40 @@ __attribute__((visibility("default"))) const char* vc_status_str(int32_t s) {
   }
 }
 
-__attribute__((visibility("default"))) int32_t vc_quantize(const vc_shape* sh, float sm_scale, const vc_bshd* q,
+// Validates a vc_prep_params (NULL = none) into PrepArgs; with_k: K is
+// prepared in this call (the centring workspace is then needed).
+static int32_t check_prep(const vc_shape* sh, const vc_prep_params* pp, bool with_k, vc::PrepArgs* out) {
+  *out = vc::PrepArgs{0u, nullptr, nullptr, nullptr};
+  if (!pp || !pp->flags) return VC_OK;
+  if (pp->flags & ~(VC_PREP_ROPE | VC_PREP_HADAMARD | VC_PREP_K_CENTER)) return VC_ERR_UNSUPPORTED;
+  if (pp->flags & VC_PREP_ROPE) {
+    if (!pp->rope_cos || !pp->rope_sin) return VC_ERR_NULL;
+    if (((uintptr_t)pp->rope_cos | (uintptr_t)pp->rope_sin) & 15u) return VC_ERR_ALIGN;
+  }
+  if (with_k && (pp->flags & VC_PREP_K_CENTER)) {
+    if (!pp->workspace) return VC_ERR_NULL;
+    if ((uintptr_t)pp->workspace & 7u) return VC_ERR_ALIGN;
+    if (pp->workspace_bytes < (size_t)sh->B * sh->H * sh->D * 8) return VC_ERR_WORKSPACE;
+  }
+  *out = vc::PrepArgs{pp->flags, pp->rope_cos, pp->rope_sin, (const long long*)pp->workspace};
+  return VC_OK;
+}
+
+__attribute__((visibility("default"))) size_t vc_prep_workspace_size(const vc_shape* sh) {
+  if (check_shape(sh)) return 0;
+  return (size_t)sh->B * sh->H * sh->D * 8;
+}
+
+__attribute__((visibility("default"))) int32_t vc_quantize(const vc_shape* sh, float sm_scale,
+                                                            const vc_prep_params* prep, const vc_bshd* q,
                                                             const vc_bshd* k, const vc_bshd* v, uint8_t* q8,
                                                             float* q_scale, uint8_t* k8, float* k_scale,
                                                             uint8_t* v8, float* v_scale, void* stream) {
   int32_t e = check_shape(sh);
   if (e) return e;
   if (!(sm_scale >= 0.0f) || isinf(sm_scale)) return VC_ERR_UNSUPPORTED;
+  vc::PrepArgs pa;
+  if ((e = check_prep(sh, prep, k && k->ptr, &pa))) return e;
   const bool dq = q && q->ptr, dk = k && k->ptr, dv = v && v->ptr;
   if (dq) {
     if ((e = check_bshd(q))) return e;
@@ -85,9 +112,15 @@ __attribute__((visibility("default"))) int32_t vc_quantize(const vc_shape* sh, f
   }
   hipStream_t st = (hipStream_t)stream;
   const float sm = sm_scale == 0.0f ? 1.0f / sqrtf((float)sh->D) : sm_scale;
-  const float G = 8.0f * (sm * 1.44269504088896340736f);  // 8 fl(sm_scale * fl(log2 e)), exact times 8
-  if (dq && (e = hip_status(vc::launch_qk_quant(*sh, as_bshd(q), G, q8, q_scale, false, st)))) return e;
-  if (dk && (e = hip_status(vc::launch_qk_quant(*sh, as_bshd(k), 1.0f, k8, k_scale, true, st)))) return e;
+  float G = 8.0f * (sm * 1.44269504088896340736f);  // 8 fl(sm_scale * fl(log2 e)), exact times 8
+  if (pa.flags & VC_PREP_HADAMARD) G /= (float)sh->D;  // exact: D is a power of two
+  vc::PrepArgs pq = pa;
+  pq.flags &= ~VC_PREP_K_CENTER;  // Q is not centred
+  if (dq && (e = hip_status(vc::launch_qk_quant(*sh, as_bshd(q), G, pq, q8, q_scale, false, st)))) return e;
+  if (dk && (pa.flags & VC_PREP_K_CENTER) &&
+      (e = hip_status(vc::launch_k_center_sums(*sh, as_bshd(k), pa, (unsigned long long*)prep->workspace, st))))
+    return e;
+  if (dk && (e = hip_status(vc::launch_qk_quant(*sh, as_bshd(k), 1.0f, pa, k8, k_scale, true, st)))) return e;
   if (dv && (e = hip_status(vc::launch_v_quant(*sh, as_bshd(v), v8, v_scale, st)))) return e;
   return VC_OK;
 }
@@ -98,9 +131,9 @@ __attribute__((visibility("default"))) size_t vc_smooth_group_workspace_size(con
 }
 
 __attribute__((visibility("default"))) int32_t vc_smooth_group(
-    const vc_shape* sh, const vc_bshd* k, const vc_bshd* v, const vc_group_params* p, float* centroids,
-    int32_t* labels, int32_t* perm, uint8_t* k8, float* k_scale, uint8_t* r8, float* r_scale, uint16_t* mu_bf16,
-    uint32_t* mu_split, void* workspace, size_t workspace_bytes, void* stream) {
+    const vc_shape* sh, const vc_bshd* k, const vc_bshd* v, const vc_group_params* p, const vc_prep_params* prep,
+    float* centroids, int32_t* labels, int32_t* perm, uint8_t* k8, float* k_scale, uint8_t* r8, float* r_scale,
+    uint16_t* mu_bf16, uint32_t* mu_split, void* workspace, size_t workspace_bytes, void* stream) {
   int32_t e = check_shape(sh);
   if (e) return e;
   if ((e = check_bshd(k)) || (e = check_bshd(v))) return e;
@@ -120,8 +153,14 @@ __attribute__((visibility("default"))) int32_t vc_smooth_group(
     return VC_ERR_ALIGN;
   if (((uintptr_t)mu_bf16) & 1u) return VC_ERR_ALIGN;
   if (workspace_bytes < vc::group_workspace_bytes(*sh, p->clusters)) return VC_ERR_WORKSPACE;
+  vc::PrepArgs pa;
+  if ((e = check_prep(sh, prep, true, &pa))) return e;
+  hipStream_t st = (hipStream_t)stream;
+  if ((pa.flags & VC_PREP_K_CENTER) &&
+      (e = hip_status(vc::launch_k_center_sums(*sh, as_bshd(k), pa, (unsigned long long*)prep->workspace, st))))
+    return e;
   return hip_status(vc::launch_smooth_group(*sh, as_bshd(k), as_bshd(v), *p, centroids, labels, perm, k8, k_scale,
-                                            r8, r_scale, mu_bf16, mu_split, workspace, (hipStream_t)stream));
+                                            r8, r_scale, mu_bf16, mu_split, workspace, pa, st));
 }
 
 __attribute__((visibility("default"))) int32_t vc_attn_fwd(const vc_shape* sh, const vc_attn_params* p,

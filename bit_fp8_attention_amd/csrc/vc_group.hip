@@ -24,6 +24,7 @@
 #include <algorithm>
 
 #include "vc_common.hpp"
+#include "vc_prep.hpp"
 #include "vc_launch.hpp"
 
 namespace vc {
@@ -618,7 +619,7 @@ __global__ __launch_bounds__(256) void group_apply1(const uint16_t* __restrict__
                                                     int64_t vS, int64_t vH, int S, int H, int nblk,
                                                     const int32_t* __restrict__ perm, uint8_t* __restrict__ k8,
                                                     float* __restrict__ k_scale, uint16_t* __restrict__ mu_bf16,
-                                                    GroupWs ws) {
+                                                    GroupWs ws, PrepArgs pp) {
   using Mp = ApplyMap<D>;
   __shared__ long long psum[Mp::RG][D];
   __shared__ float pmax[Mp::RG][D];
@@ -635,21 +636,34 @@ __global__ __launch_bounds__(256) void group_apply1(const uint16_t* __restrict__
     tok[r] = row < nvalid ? perm[bh * S + j * kBlk + row] : -1;
   }
   // ---- K' = K[pi], per-block E4M3 ----
+  // With preprocessing ([VC] App. B: centring statistics, RoPE, gather,
+  // Hadamard, mean subtraction), each gathered key is rotated at its original
+  // position, centred by the head's channel mean and transformed, as in
+  // vc_quantize's K path, before the block scale is taken.
   {
     const uint16_t* kb = kx + b * kB + h * kH;
-    uint4 kv[Mp::RPT];
+    float kv[Mp::RPT][8];
+    float cm[8];
+    if (pp.flags & kPrepCenter) {
+#pragma unroll
+      for (int e2 = 0; e2 < 8; ++e2) cm[e2] = fx24_mean_of(pp.ksum[bh * D + ch * 8 + e2], S);
+    }
     float m = 0.0f;
 #pragma unroll
     for (int r = 0; r < Mp::RPT; ++r) {
-      kv[r] = tok[r] >= 0 ? *(const uint4*)(kb + (int64_t)tok[r] * kS + ch * 8) : make_uint4(0, 0, 0, 0);
-      m = fmaxf(m, fabsf(bf16_lo(kv[r].x)));
-      m = fmaxf(m, fabsf(bf16_hi(kv[r].x)));
-      m = fmaxf(m, fabsf(bf16_lo(kv[r].y)));
-      m = fmaxf(m, fabsf(bf16_hi(kv[r].y)));
-      m = fmaxf(m, fabsf(bf16_lo(kv[r].z)));
-      m = fmaxf(m, fabsf(bf16_hi(kv[r].z)));
-      m = fmaxf(m, fabsf(bf16_lo(kv[r].w)));
-      m = fmaxf(m, fabsf(bf16_hi(kv[r].w)));
+      unpack8(tok[r] >= 0 ? *(const uint4*)(kb + (int64_t)tok[r] * kS + ch * 8) : make_uint4(0, 0, 0, 0), kv[r]);
+      if (pp.flags) {
+        if (tok[r] >= 0) {
+          if (pp.flags & kPrepRope)
+            rope8(kv[r], pp.cs + (int64_t)tok[r] * (D / 2) + ch * 4, pp.sn + (int64_t)tok[r] * (D / 2) + ch * 4);
+          if (pp.flags & kPrepCenter)
+#pragma unroll
+            for (int e2 = 0; e2 < 8; ++e2) kv[r][e2] -= cm[e2];
+        }
+        if (pp.flags & kPrepHadamard) fwht_row8<Mp::CPR>(kv[r], ch);  // every lane of the row takes part
+      }
+#pragma unroll
+      for (int e2 = 0; e2 < 8; ++e2) m = fmaxf(m, fabsf(kv[r][e2]));
     }
     m = wave_max(m);
     if ((t & 63) == 0) red[t >> 6] = m;
@@ -662,10 +676,9 @@ __global__ __launch_bounds__(256) void group_apply1(const uint16_t* __restrict__
     uint8_t* kd = k8 + (bh * nblk * kBlk + (int64_t)j * kBlk) * D;
 #pragma unroll
     for (int r = 0; r < Mp::RPT; ++r) {
-      uint4 w = kv[r];
       uint2 c;
-      c.x = cvt4_fp8(bf16_lo(w.x) * inv, bf16_hi(w.x) * inv, bf16_lo(w.y) * inv, bf16_hi(w.y) * inv);
-      c.y = cvt4_fp8(bf16_lo(w.z) * inv, bf16_hi(w.z) * inv, bf16_lo(w.w) * inv, bf16_hi(w.w) * inv);
+      c.x = cvt4_fp8(kv[r][0] * inv, kv[r][1] * inv, kv[r][2] * inv, kv[r][3] * inv);
+      c.y = cvt4_fp8(kv[r][4] * inv, kv[r][5] * inv, kv[r][6] * inv, kv[r][7] * inv);
       *(uint2*)(kd + kpack_off<D>(rg * Mp::RPT + r, ch >> 1) + (ch & 1) * 8) = c;
     }
   }
@@ -787,7 +800,7 @@ __global__ __launch_bounds__(256) void group_apply2(const uint16_t* __restrict__
 template <int D>
 hipError_t launch_group_t(const vc_shape& sh, Bshd k, Bshd v, const vc_group_params& p, float* cent, int32_t* labels,
                           int32_t* perm, uint8_t* k8, float* k_scale, uint8_t* r8, float* r_scale,
-                          uint16_t* mu_bf16, u32* mu_split, GroupWs ws, hipStream_t st) {
+                          uint16_t* mu_bf16, u32* mu_split, GroupWs ws, PrepArgs pp, hipStream_t st) {
   const int S = sh.S, H = sh.H, B = sh.B, kc = p.clusters;
   const int nblk = (S + kBlk - 1) / kBlk, nchunk = (S + kChunk - 1) / kChunk;
   const int BH = B * H;
@@ -810,7 +823,7 @@ hipError_t launch_group_t(const vc_shape& sh, Bshd k, Bshd v, const vc_group_par
     label_scatter<<<dim3(nchunk, H, B), 256, 0, st>>>(labels, S, H, kc, nchunk, ws, perm);
   }
   group_apply1<D><<<dim3(nblk, H, B), 256, 0, st>>>(k.p, k.sB, k.sS, k.sH, v.p, v.sB, v.sS, v.sH, S, H, nblk, perm,
-                                                    k8, k_scale, mu_bf16, ws);
+                                                    k8, k_scale, mu_bf16, ws, pp);
   group_apply2<D><<<dim3(nblk, H, B), 256, 0, st>>>(v.p, v.sB, v.sS, v.sH, S, H, nblk, perm, mu_bf16, ws, r8,
                                                     r_scale, mu_split);
   return hipGetLastError();
@@ -826,12 +839,14 @@ size_t group_workspace_bytes(const vc_shape& sh, int clusters) {
 
 hipError_t launch_smooth_group(const vc_shape& sh, Bshd k, Bshd v, const vc_group_params& p, float* centroids,
                                int32_t* labels, int32_t* perm, uint8_t* k8, float* k_scale, uint8_t* r8,
-                               float* r_scale, uint16_t* mu_bf16, uint32_t* mu_split, void* ws, hipStream_t st) {
+                               float* r_scale, uint16_t* mu_bf16, uint32_t* mu_split, void* ws, PrepArgs pp,
+                               hipStream_t st) {
   GroupWs g = carve(ws, sh, p.clusters, nullptr);
   if (sh.D == 128)
     return launch_group_t<128>(sh, k, v, p, centroids, labels, perm, k8, k_scale, r8, r_scale, mu_bf16, mu_split, g,
-                               st);
-  return launch_group_t<64>(sh, k, v, p, centroids, labels, perm, k8, k_scale, r8, r_scale, mu_bf16, mu_split, g, st);
+                               pp, st);
+  return launch_group_t<64>(sh, k, v, p, centroids, labels, perm, k8, k_scale, r8, r_scale, mu_bf16, mu_split, g, pp,
+                            st);
 }
 
 }  // namespace vc

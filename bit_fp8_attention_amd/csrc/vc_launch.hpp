@@ -20,9 +20,19 @@ struct BshdOut {
 };
 
 // vc_quantize.hip
-// pre: fp32 factor applied before quantising (Q: G = 8 fl(sm_scale log2 e), K: 1)
-hipError_t launch_qk_quant(const vc_shape& sh, Bshd x, float pre, uint8_t* codes, float* scale, bool pack,
-                           hipStream_t st);
+// Q/K preprocessing ahead of the quantiser (VC_PREP_* flags of vc_attn.h)
+constexpr uint32_t kPrepRope = 1u, kPrepHadamard = 2u, kPrepCenter = 4u;
+struct PrepArgs {
+  uint32_t flags;         // 0: none
+  const float* cs;        // RoPE tables fp32 [S][D/2] by token position
+  const float* sn;
+  const long long* ksum;  // K centring: fixed-point channel sums [B][H][D]
+};
+// pre: fp32 factor applied before quantising (Q: G = 8 fl(sm_scale log2 e), over D with the rotation; K: 1)
+hipError_t launch_qk_quant(const vc_shape& sh, Bshd x, float pre, PrepArgs pp, uint8_t* codes, float* scale,
+                           bool pack, hipStream_t st);
+// K centring statistics into ksum (zeroed here first): sums over all keys after RoPE
+hipError_t launch_k_center_sums(const vc_shape& sh, Bshd x, PrepArgs pp, unsigned long long* ksum, hipStream_t st);
 hipError_t launch_v_quant(const vc_shape& sh, Bshd v, uint8_t* v8, float* v_scale, hipStream_t st);
 hipError_t launch_pack_v_bf16(const vc_shape& sh, Bshd v, uint16_t* vt, hipStream_t st);
 hipError_t launch_expcast_codes(const float* x, const float* a, const float* b, int64_t n, int32_t row_len,
@@ -32,7 +42,8 @@ hipError_t launch_expcast_codes(const float* x, const float* a, const float* b, 
 size_t group_workspace_bytes(const vc_shape& sh, int clusters);
 hipError_t launch_smooth_group(const vc_shape& sh, Bshd k, Bshd v, const vc_group_params& p, float* centroids,
                                int32_t* labels, int32_t* perm, uint8_t* k8, float* k_scale, uint8_t* r8,
-                               float* r_scale, uint16_t* mu_bf16, uint32_t* mu_split, void* ws, hipStream_t st);
+                               float* r_scale, uint16_t* mu_bf16, uint32_t* mu_split, void* ws, PrepArgs pp,
+                               hipStream_t st);
 
 // vc_attn_fp8.hip
 // q8 / q_scale carry the softmax factor G (vc_quantize); Q/K scales are powers of two

@@ -13,6 +13,7 @@
 // loads (each row is D contiguous bf16), amax through a wave then LDS
 // reduction, E4M3 conversion with the hardware round-half-even convert.
 #include "vc_common.hpp"
+#include "vc_prep.hpp"
 #include "vc_launch.hpp"
 
 namespace vc {
@@ -40,17 +41,6 @@ VC_DEV uint2 codes8(uint4 w, float inv) {
   return r;
 }
 
-// 8 bf16 -> E4M3(fl(x * pre) * 2^-e): the product rounds once to fp32, the
-// power-of-two scaling is exact (only values far below E4M3's range could
-// round in it, and those encode as 0 either way)
-VC_DEV uint2 codes8_pow2(uint4 w, float pre, float p2) {
-  auto f = [&](float x) { return (x * pre) * p2; };
-  uint2 r;
-  r.x = cvt4_fp8(f(bf16_lo(w.x)), f(bf16_hi(w.x)), f(bf16_lo(w.y)), f(bf16_hi(w.y)));
-  r.y = cvt4_fp8(f(bf16_lo(w.z)), f(bf16_hi(w.z)), f(bf16_lo(w.w)), f(bf16_hi(w.w)));
-  return r;
-}
-
 VC_DEV float block_max256(float m, float* red) {
   m = wave_max(m);
   int w = threadIdx.x >> 6;
@@ -72,38 +62,111 @@ VC_DEV void scale_pair(float amax, float& s, float& inv) {
 
 // Q or K: one workgroup per (block j, head h, batch b).  PACK writes the
 // packed K layout (chunk-swizzled rows), otherwise plain row-major codes.
-// Each element is multiplied by pre first (Q: G = 8 fl(sm_scale log2 e),
-// K: 1); the block scale is the power of two pow2_block_exp picks for the
-// products' amax (fl(max |x| * pre), the max of the rounded products).
+// With preprocessing ([VC] §3.4, App. B), each valid row is first rotated
+// (RoPE at its position), centred (K: minus the head's channel mean, from the
+// fixed-point sums of k_center_sums) and transformed by the unnormalised
+// Walsh-Hadamard matrix, all in fp32.  Each element is then multiplied by
+// pre (Q: G = 8 fl(sm_scale log2 e), over D with the rotation; K: 1); the
+// block scale is the power of two pow2_block_exp picks for the products'
+// amax (the max of the rounded products).
 template <int D, bool PACK>
 __global__ __launch_bounds__(256) void qk_block_quant(const uint16_t* __restrict__ x, int64_t sB, int64_t sS,
-                                                      int64_t sH, int S, int H, int nblk, float pre,
+                                                      int64_t sH, int S, int H, int nblk, float pre, PrepArgs pp,
                                                       uint8_t* __restrict__ codes, float* __restrict__ scale) {
   constexpr int CPR = D / 8;             // 16-byte chunks per row
   constexpr int NCH = kBlk * CPR / 256;  // chunks per thread
   __shared__ float red[4];
   const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const int64_t bh = (int64_t)b * H + h;
   const uint16_t* xb = x + b * sB + h * sH;
-  uint4 v[NCH];
-  float m = 0.0f;
+  const int ch = t % CPR;  // the same chunk for every row of this thread
+  float xv[NCH][8];
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    int c = t + 256 * i, row = c / CPR, ch = c % CPR, tok = j * kBlk + row;
-    v[i] = tok < S ? *(const uint4*)(xb + (int64_t)tok * sS + ch * 8) : make_uint4(0, 0, 0, 0);
-    m = amax8(v[i], m);
+    const int row = (t + 256 * i) / CPR, tok = j * kBlk + row;
+    unpack8(tok < S ? *(const uint4*)(xb + (int64_t)tok * sS + ch * 8) : make_uint4(0, 0, 0, 0), xv[i]);
   }
+  if (pp.flags) {
+    float cm[8];
+    if (pp.flags & kPrepCenter) {
+#pragma unroll
+      for (int e2 = 0; e2 < 8; ++e2) cm[e2] = fx24_mean_of(pp.ksum[bh * D + ch * 8 + e2], S);
+    }
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int row = (t + 256 * i) / CPR, tok = j * kBlk + row;
+      if (tok < S) {
+        if (pp.flags & kPrepRope) rope8(xv[i], pp.cs + (int64_t)tok * (D / 2) + ch * 4, pp.sn + (int64_t)tok * (D / 2) + ch * 4);
+        if (pp.flags & kPrepCenter)
+#pragma unroll
+          for (int e2 = 0; e2 < 8; ++e2) xv[i][e2] -= cm[e2];
+      }
+      if (pp.flags & kPrepHadamard) fwht_row8<CPR>(xv[i], ch);  // every lane of the row takes part
+    }
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i)
+#pragma unroll
+    for (int e2 = 0; e2 < 8; ++e2) m = fmaxf(m, fabsf(xv[i][e2] * pre));
   m = block_max256(m, red);
-  const int e = pow2_block_exp(m * pre);
+  const int e = pow2_block_exp(m);
   const float p2 = ldexpf(1.0f, -e);
-  const int64_t bh = (int64_t)b * H + h;
   if (t == 0) scale[bh * nblk + j] = ldexpf(1.0f, e);
   uint8_t* cb = codes + (bh * nblk * kBlk + (int64_t)j * kBlk) * D;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    int c = t + 256 * i, row = c / CPR, ch = c % CPR;
+    const int row = (t + 256 * i) / CPR;
     const int off = PACK ? kpack_off<D>(row, ch >> 1) + (ch & 1) * 8 : row * D + ch * 8;
-    *(uint2*)(cb + off) = codes8_pow2(v[i], pre, p2);
+    auto f = [&](int e2) { return (xv[i][e2] * pre) * p2; };
+    uint2 r;
+    r.x = cvt4_fp8(f(0), f(1), f(2), f(3));
+    r.y = cvt4_fp8(f(4), f(5), f(6), f(7));
+    *(uint2*)(cb + off) = r;
   }
+}
+
+// K centring statistics: per (b, h), the fixed-point sums over all S keys of
+// each channel after RoPE, added into ksum [B][H][D] (zeroed first).  One
+// workgroup per (128-key block, head, batch), the same row/chunk map as
+// qk_block_quant; the sums of a workgroup are combined in LDS first.
+template <int D>
+__global__ __launch_bounds__(256) void k_center_sums(const uint16_t* __restrict__ x, int64_t sB, int64_t sS,
+                                                     int64_t sH, int S, int H, PrepArgs pp,
+                                                     unsigned long long* __restrict__ ksum) {
+  constexpr int CPR = D / 8;
+  constexpr int NCH = kBlk * CPR / 256;
+  constexpr int RG = 256 / CPR;
+  __shared__ long long ps[RG][D];
+  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const int64_t bh = (int64_t)b * H + h;
+  const uint16_t* xb = x + b * sB + h * sH;
+  const int ch = t % CPR, rg = t / CPR;
+  long long acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int row = (t + 256 * i) / CPR, tok = j * kBlk + row;
+    if (tok < S) {
+      float xv[8];
+      unpack8(*(const uint4*)(xb + (int64_t)tok * sS + ch * 8), xv);
+      if (pp.flags & kPrepRope) rope8(xv, pp.cs + (int64_t)tok * (D / 2) + ch * 4, pp.sn + (int64_t)tok * (D / 2) + ch * 4);
+#pragma unroll
+      for (int e2 = 0; e2 < 8; ++e2) acc[e2] += fx24_ll(xv[e2]);
+    }
+  }
+#pragma unroll
+  for (int e2 = 0; e2 < 8; ++e2) ps[rg][ch * 8 + e2] = acc[e2];
+  __syncthreads();
+  for (int d = t; d < D; d += 256) {
+    long long sum = 0;
+    for (int r = 0; r < RG; ++r) sum += ps[r][d];
+    atomicAdd(ksum + bh * D + d, (unsigned long long)sum);  // two's complement: signed sums add exactly
+  }
+}
+
+__global__ void zero_u64(unsigned long long* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0ull;
 }
 
 // V pass 1: per-(b,h) amax as ordered uint bits, accumulated into
@@ -231,20 +294,32 @@ __global__ void expcast_codes_kernel(const float* __restrict__ x, const float* _
 
 }  // namespace
 
-hipError_t launch_qk_quant(const vc_shape& sh, Bshd x, float pre, uint8_t* codes, float* scale, bool pack,
-                           hipStream_t st) {
+hipError_t launch_k_center_sums(const vc_shape& sh, Bshd x, PrepArgs pp, unsigned long long* ksum, hipStream_t st) {
+  const int nblk = (sh.S + kBlk - 1) / kBlk;
+  const int64_t n = (int64_t)sh.B * sh.H * sh.D;
+  zero_u64<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(ksum, n);
+  dim3 grid(nblk, sh.H, sh.B);
+  if (sh.D == 128)
+    k_center_sums<128><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, pp, ksum);
+  else
+    k_center_sums<64><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, pp, ksum);
+  return hipGetLastError();
+}
+
+hipError_t launch_qk_quant(const vc_shape& sh, Bshd x, float pre, PrepArgs pp, uint8_t* codes, float* scale,
+                           bool pack, hipStream_t st) {
   int nblk = (sh.S + kBlk - 1) / kBlk;
   dim3 grid(nblk, sh.H, sh.B);
   if (sh.D == 128) {
     if (pack)
-      qk_block_quant<128, true><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nblk, pre, codes, scale);
+      qk_block_quant<128, true><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nblk, pre, pp, codes, scale);
     else
-      qk_block_quant<128, false><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nblk, pre, codes, scale);
+      qk_block_quant<128, false><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nblk, pre, pp, codes, scale);
   } else {
     if (pack)
-      qk_block_quant<64, true><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nblk, pre, codes, scale);
+      qk_block_quant<64, true><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nblk, pre, pp, codes, scale);
     else
-      qk_block_quant<64, false><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nblk, pre, codes, scale);
+      qk_block_quant<64, false><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nblk, pre, pp, codes, scale);
   }
   return hipGetLastError();
 }

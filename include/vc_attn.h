@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define VC_ABI_VERSION 3
+#define VC_ABI_VERSION 4
 
 typedef enum vc_status {
   VC_OK = 0,
@@ -88,6 +88,48 @@ int32_t vc_abi_version(void);
 /* Static, human-readable name of a status code. */
 const char* vc_status_str(int32_t status);
 
+/* ----------------------------------------------------------------------- */
+
+/*
+ * Q/K preprocessing ahead of the quantisers ([VC] §3.4 "Fused Kernel and
+ * Amortized Grouping" and Appendix B: rotary embedding, the key channel mean,
+ * the QK Hadamard rotation, fused into the quantisers).  Applied per row in
+ * this order, in fp32, before the pre-factor and the block scale:
+ *   VC_PREP_ROPE:     pairs (2i, 2i+1) of a row at token position p become
+ *                     (a c - b s, a s + b c), c = rope_cos[p][i],
+ *                     s = rope_sin[p][i] (fp32 [S][D/2] device tables; for
+ *                     V-Smooth's K' the position is the key's own, before the
+ *                     gather);
+ *   VC_PREP_K_CENTER: K only: minus the channel mean of the head's S keys
+ *                     after RoPE (sums in 64-bit fixed point with 24 fraction
+ *                     bits, mean = fl(sum / (S 2^24)) in fp64).  Softmax rows
+ *                     do not change;
+ *   VC_PREP_HADAMARD: the unnormalised Walsh-Hadamard transform over D,
+ *                     radix-2 butterflies (a, b) -> (a + b, a - b) over strides
+ *                     1, 2, ..., D/2; Q's pre-factor becomes G / D (exact), so
+ *                     the scores do not change.
+ * Q and K must be prepared alike (the same RoPE tables, the rotation on both)
+ * for the attention to be the intended one: with V-Smooth, pass the same
+ * vc_prep_params to vc_quantize (Q) and vc_smooth_group (K).
+ * workspace: device, 8-byte aligned, >= vc_prep_workspace_size(shape) bytes,
+ * needed with VC_PREP_K_CENTER when K is given (else may be NULL); its
+ * contents on entry do not matter.
+ */
+#define VC_PREP_ROPE 1u
+#define VC_PREP_HADAMARD 2u
+#define VC_PREP_K_CENTER 4u
+
+typedef struct vc_prep_params {
+  uint32_t flags;        /* OR of VC_PREP_* (0: none) */
+  const float* rope_cos; /* fp32 [S][D/2], with VC_PREP_ROPE */
+  const float* rope_sin; /* fp32 [S][D/2], with VC_PREP_ROPE */
+  void* workspace;
+  size_t workspace_bytes;
+} vc_prep_params;
+
+/* Bytes of device workspace VC_PREP_K_CENTER needs: B*H*D*8. */
+size_t vc_prep_workspace_size(const vc_shape* shape);
+
 /*
  * vc_quantize -- FP8 operands for the attention kernel.
  * [OVC] "Scheduling around ExpCast" and "Fused input preparation": Q and K
@@ -99,8 +141,11 @@ const char* vc_status_str(int32_t status);
  * kernel's block-scaled matrix product applies exactly.
  *
  * sm_scale: the softmax scale (0 selects 1/sqrt(D)); must be finite, >= 0.
- * G = 8 * fl(sm_scale * fl(log2 e)) (fp32; the factor 8 is exact).
- * For each (b, h) and 128-token block j of Q (pre = G) and of K (pre = 1):
+ * G = 8 * fl(sm_scale * fl(log2 e)) (fp32; the factor 8 is exact), divided
+ * by D with VC_PREP_HADAMARD.
+ * prep: preprocessing (above), or NULL for none.
+ * For each (b, h) and 128-token block j of Q (pre = G) and of K (pre = 1),
+ * x the row after preprocessing:
  *   y = fl(x * pre); amax = max |y| over the block's valid rows;
  *   e = the smallest integer >= -127 with amax <= 448 * 2^e (e = 0 for a
  *   block of zeros); scale = 2^e; code = E4M3_rne(y * 2^-e).
@@ -116,9 +161,9 @@ const char* vc_status_str(int32_t status);
  * Any of q, k, v may have ptr == NULL to skip that operand (its outputs are
  * then ignored and may be NULL).  q8/k8/v8 must be 16-byte aligned.
  */
-int32_t vc_quantize(const vc_shape* shape, float sm_scale, const vc_bshd* q, const vc_bshd* k, const vc_bshd* v,
-                    uint8_t* q8, float* q_scale, uint8_t* k8, float* k_scale, uint8_t* v8, float* v_scale,
-                    void* stream);
+int32_t vc_quantize(const vc_shape* shape, float sm_scale, const vc_prep_params* prep, const vc_bshd* q,
+                    const vc_bshd* k, const vc_bshd* v, uint8_t* q8, float* q_scale, uint8_t* k8, float* k_scale,
+                    uint8_t* v8, float* v_scale, void* stream);
 
 /* ----------------------------------------------------------------------- */
 
@@ -168,6 +213,8 @@ size_t vc_smooth_group_workspace_size(const vc_shape* shape, int32_t clusters);
  *     exact), the form the attention kernel's mean product reads.  K' is
  *     quantised per 128-row block as K in vc_quantize (power-of-two
  *     scales).
+ * prep: K's preprocessing (vc_quantize), applied to each key of K' before
+ * its block scale, or NULL for none.
  * With VC_GROUP_WARM_START, step 1 starts from the given centroids; with
  * VC_GROUP_REUSE_PERM, steps 1 and 2 are skipped and perm is an input.  The
  * two flags exclude each other (VC_ERR_UNSUPPORTED).
@@ -180,9 +227,9 @@ size_t vc_smooth_group_workspace_size(const vc_shape* shape, int32_t clusters);
  * 256-byte aligned; its contents on entry do not matter.
  */
 int32_t vc_smooth_group(const vc_shape* shape, const vc_bshd* k, const vc_bshd* v, const vc_group_params* p,
-                        float* centroids, int32_t* labels, int32_t* perm, uint8_t* k8, float* k_scale,
-                        uint8_t* r8, float* r_scale, uint16_t* mu_bf16, uint32_t* mu_split, void* workspace,
-                        size_t workspace_bytes, void* stream);
+                        const vc_prep_params* prep, float* centroids, int32_t* labels, int32_t* perm, uint8_t* k8,
+                        float* k_scale, uint8_t* r8, float* r_scale, uint16_t* mu_bf16, uint32_t* mu_split,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* ----------------------------------------------------------------------- */
 
