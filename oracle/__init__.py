@@ -79,7 +79,10 @@ def lib():
         L.vco_argsort_labels.argtypes = [P, i32, i32, P]
         L.vco_smooth_apply.argtypes = [P, i64, P, i64, i32, i32, P, P, P, P, P, P, P]
         L.vco_tile_order.argtypes = [i32, i32, i32, i32, P]
-        L.vco_attn_emulate_rows.argtypes = [P, P, P, P, P, P, P, i32, i32, f32, i32, i32, P, i32, P, P, P]
+        L.vco_attn_emulate_rows.argtypes = [P, P, P, P, P, P, P, i32, i32, f32, i32, i32, P, i32, P, P, P, i32,
+                                            P, P, P]
+        L.vco_repair_select.argtypes = [P, i64, i32, i32, i32, P, P]
+        L.vco_repair_rows.argtypes = [P, i64, i32, i32, P, i32, P]
         _lib = L
     return _lib
 
@@ -297,12 +300,41 @@ def tile_order(qt: int, nblk: int, window: int = 2, sequential: bool = False) ->
     return out
 
 
+def repair_count(S: int, rho: float) -> int:
+    """Number of repair rows for rho (the fraction of tokens): ceil(rho S)."""
+    return 0 if rho <= 0 else min(S, int(np.ceil(rho * S - 1e-9)))
+
+
+def repair_select(v_head: np.ndarray, R: int):
+    """One head's V (uint16 bf16 bits [S,D]): residual energies (fp64 [S]) and
+    the R selected token indices (int32, ascending)."""
+    v_head = np.ascontiguousarray(v_head, np.uint16)
+    S, D = v_head.shape
+    idx = np.zeros(max(R, 1), np.int32)
+    e = np.zeros(S, np.float64)
+    lib().vco_repair_select(_p(v_head), D, S, D, int(R), _p(idx), _p(e))
+    return idx[:R], e
+
+
+def repair_rows(v_head: np.ndarray, idx: np.ndarray):
+    """Residual codes of the selected tokens, key-contiguous uint8 [D, R_pad]."""
+    v_head = np.ascontiguousarray(v_head, np.uint16)
+    S, D = v_head.shape
+    idx = np.ascontiguousarray(idx, np.int32)
+    R = idx.size
+    out = np.zeros((D, (R + 127) // 128 * 128), np.uint8)
+    lib().vco_repair_rows(_p(v_head), D, S, D, _p(idx), R, _p(out))
+    return out
+
+
 def attn_emulate_rows(q_codes, q_scale, k_codes, k_scale, v_codes_t, v_scale, mu_scaled, S, c1,
-                      rows, window=2, flags=0):
+                      rows, window=2, flags=0, repair=None):
     """One head.  q_codes/k_codes [S_pad,D], v_codes_t [D,S_pad], scales as
     produced by the quantisers, mu_scaled [nblk,D] or None.  c1 is the
     log2-domain score per unit of q_scale * k_scale * (Qhat . Khat): 1/8 when
     Q carries G (quantize_qk(q, q_prefactor(sm_scale))).
+    repair: None or dict(rk_codes [R_pad,D], rk_scale [nrb], rv_codes_t [D,R_pad], R),
+    tiles of repair rows visited after all others, numerator only.
     Returns (out_f32 [n,D], out_bf16 bits [n,D], stats [n,2])."""
     q_codes = np.ascontiguousarray(q_codes, np.uint8)
     k_codes = np.ascontiguousarray(k_codes, np.uint8)
@@ -320,14 +352,22 @@ def attn_emulate_rows(q_codes, q_scale, k_codes, k_scale, v_codes_t, v_scale, mu
     if mu_scaled is not None:
         mu_scaled = np.ascontiguousarray(mu_scaled, np.float32)
         mu_p = _p(mu_scaled)
+    rk = rks = rv = None
+    R = 0
+    if repair is not None and repair["R"] > 0:
+        rk = np.ascontiguousarray(repair["rk_codes"], np.uint8)
+        rks = np.ascontiguousarray(repair["rk_scale"], np.float32)
+        rv = np.ascontiguousarray(repair["rv_codes_t"], np.uint8)
+        R = int(repair["R"])
     lib().vco_attn_emulate_rows(_p(q_codes), _p(q_scale), _p(k_codes), _p(k_scale), _p(v_codes_t),
                                 _p(v_scale), mu_p, S, D, float(c1), window, flags, _p(rows), n,
-                                _p(of), _p(ob), _p(st))
+                                None if rk is None else _p(rk), None if rks is None else _p(rks),
+                                None if rv is None else _p(rv), R, _p(of), _p(ob), _p(st))
     return of, ob, st
 
 
 def pipeline_head(q, k, v, b, h, *, vsmooth, nclust=64, iters=4, seed=0, sm_scale=None, rows=None,
-                  window=2, flags=0, prep=0, rope_cos=None, rope_sin=None):
+                  window=2, flags=0, prep=0, rope_cos=None, rope_sin=None, repair_rho=0.0):
     """Full oracle pipeline for one head from bf16 inputs [B,S,H,D]:
     quantise, (group,) emulate the listed query rows.  Returns a dict."""
     B, S, H, D = q.shape
@@ -366,6 +406,18 @@ def pipeline_head(q, k, v, b, h, *, vsmooth, nclust=64, iters=4, seed=0, sm_scal
         vs = np.full(D, s, np.float32)
         mu = None
         out.update(k_codes=kc, k_scale=ks, v_codes=vc, v_scale=vs)
-    of, ob, st = attn_emulate_rows(qc, qs, kc, ks, vc, vs, mu, S, 0.125, rows, window, flags)
+    repair = None
+    R = 0 if vsmooth else repair_count(S, repair_rho)
+    if R > 0:
+        # [OVC] "Why V residual repair": the top R tokens by residual energy;
+        # their keys (prepared alike) quantised as blocks of their own
+        idx, energy = repair_select(_head(v, b, h), R)
+        yk_all = yk if prep else bf16_bits_to_f32(_head(k, b, h)).astype(np.float32)
+        rk, rks = quantize_f32_pow2(np.ascontiguousarray(yk_all[idx]))
+        rv = repair_rows(_head(v, b, h), idx)
+        repair = dict(rk_codes=rk, rk_scale=rks, rv_codes_t=rv, R=R)
+        out.update(repair_idx=idx, repair_energy=energy, repair_k_codes=rk, repair_k_scale=rks,
+                   repair_v_codes=rv)
+    of, ob, st = attn_emulate_rows(qc, qs, kc, ks, vc, vs, mu, S, 0.125, rows, window, flags, repair)
     out.update(out_f32=of, out_bf16=ob, stats=st, rows=rows)
     return out

@@ -321,6 +321,83 @@ EXPORT float vco_quantize_v_head(const uint16_t* x, int64_t ld, int32_t S, int32
 }
 
 /* ------------------------------------------------------------------------ */
+/* V residual repair, [OVC] "Why V residual repair": with one V scale per    */
+/* head, token j leaves the residual r_j = V_j - s_V Vhat_j; the top rho*S  */
+/* tokens by energy sum_c r_jc^2 become extra value rows (their residuals)  */
+/* paired with copies of their keys, visited last, numerator only.          */
+/* Readings: r = fl32(v - fl32(s_V dec(code))); the energy is summed in fp64 */
+/* over c = 0 .. D-1 in order; ties in energy go to the lower index; the    */
+/* selected indices are returned in ascending order; a residual row is      */
+/* quantised in the head's own V scale, code = E4M3(fl32(r * 448/amax)), so */
+/* the kernel's single epilogue multiply covers it too.                     */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  double e;
+  int32_t j;
+} vco_energy_t;
+static int cmp_energy_desc(const void* a, const void* b) {
+  const vco_energy_t* x = (const vco_energy_t*)a;
+  const vco_energy_t* y = (const vco_energy_t*)b;
+  if (x->e > y->e) return -1;
+  if (x->e < y->e) return 1;
+  return (x->j > y->j) - (x->j < y->j);
+}
+static int cmp_i32(const void* a, const void* b) {
+  int32_t i = *(const int32_t*)a, j = *(const int32_t*)b;
+  return (i > j) - (i < j);
+}
+
+/* One head's residual energies (energy [S]) and the R selected indices (idx [R], ascending). */
+EXPORT void vco_repair_select(const uint16_t* x, int64_t ld, int32_t S, int32_t D, int32_t R, int32_t* idx,
+                              double* energy) {
+  float amax = 0.0f;
+  for (int32_t r = 0; r < S; ++r)
+    for (int32_t d = 0; d < D; ++d) amax = fmaxf(amax, fabsf(bf16_to_f32(x[r * ld + d])));
+  float s, inv;
+  scale_pair(amax, &s, &inv);
+  vco_energy_t* order = (vco_energy_t*)malloc(sizeof(vco_energy_t) * (size_t)S);
+  for (int32_t j = 0; j < S; ++j) {
+    double e = 0.0;
+    for (int32_t d = 0; d < D; ++d) {
+      float v = bf16_to_f32(x[j * ld + d]);
+      float deq = s * (float)DEC(vco_e4m3_encode(v * inv));
+      float r = v - deq;
+      e += (double)r * (double)r;
+    }
+    energy[j] = e;
+    order[j].e = e;
+    order[j].j = j;
+  }
+  qsort(order, (size_t)S, sizeof(vco_energy_t), cmp_energy_desc);
+  for (int32_t i = 0; i < R; ++i) idx[i] = order[i].j;
+  qsort(idx, (size_t)R, sizeof(int32_t), cmp_i32);
+  free(order);
+}
+
+/* Residual codes of the selected tokens, key-contiguous: r_codes_t [D][Rpad]
+ * (Rpad = R rounded up to 128; pad keys zero). */
+EXPORT void vco_repair_rows(const uint16_t* x, int64_t ld, int32_t S, int32_t D, const int32_t* idx, int32_t R,
+                            uint8_t* r_codes_t) {
+  float amax = 0.0f;
+  for (int32_t r = 0; r < S; ++r)
+    for (int32_t d = 0; d < D; ++d) amax = fmaxf(amax, fabsf(bf16_to_f32(x[r * ld + d])));
+  float s, inv;
+  scale_pair(amax, &s, &inv);
+  int32_t Rpad = (R + 127) / 128 * 128;
+  for (int32_t d = 0; d < D; ++d)
+    for (int32_t i = 0; i < Rpad; ++i) {
+      uint8_t c = 0;
+      if (i < R) {
+        float v = bf16_to_f32(x[(int64_t)idx[i] * ld + d]);
+        float r = v - s * (float)DEC(vco_e4m3_encode(v * inv));
+        c = vco_e4m3_encode(r * inv);
+      }
+      r_codes_t[(int64_t)d * Rpad + i] = c;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* V-Smooth grouping, [VC] §3.2 "Value-guided permutation" and "Unbalanced   */
 /* clusters cost little": per (b,h) an online k-means over the value tokens  */
 /* gives labels z; pi = argsort(z); K' = K[pi], V' = V[pi].                  */
@@ -546,8 +623,10 @@ EXPORT void vco_attn_emulate_rows(const uint8_t* q_codes, const float* q_scale, 
                                   const float* k_scale, const uint8_t* v_codes_t, const float* v_scale,
                                   const float* mu_scaled, int32_t S, int32_t D, float c1,
                                   int32_t window, int32_t flags, const int32_t* rows, int32_t n,
-                                  float* out_f32, uint16_t* out_bf16, double* stats) {
+                                  const uint8_t* rk_codes, const float* rk_scale, const uint8_t* rv_codes_t,
+                                  int32_t R, float* out_f32, uint16_t* out_bf16, double* stats) {
   int32_t nblk = (S + 127) / 128, S_pad = nblk * 128;
+  int32_t nrb = R > 0 ? (R + 127) / 128 : 0, R_pad = nrb * 128; /* repair tiles, visited last */
   double dq[256];
   e4m3_table_init();
 #pragma omp parallel for schedule(dynamic, 1) private(dq)
@@ -563,17 +642,24 @@ EXPORT void vco_attn_emulate_rows(const uint8_t* q_codes, const float* q_scale, 
     int32_t rescales = 0;
     float c2 = c1 * q_scale[qt];
     for (int32_t d = 0; d < D; ++d) dq[d] = DEC(q_codes[(int64_t)i * D + d]);
-    for (int32_t oi = 0; oi < nblk; ++oi) {
-      int32_t t = order[oi];
-      int32_t k0 = t * 128, k1 = k0 + 128 < S ? k0 + 128 : S;
+    for (int32_t oi = 0; oi < nblk + nrb; ++oi) {
+      /* repair tiles ([OVC] "Why V residual repair"): their keys, residual
+       * rows, scales and row count; numerator only */
+      const int repair = oi >= nblk;
+      int32_t t = repair ? oi - nblk : order[oi];
+      int32_t lim = repair ? R : S;
+      const uint8_t* kc = repair ? rk_codes : k_codes;
+      const uint8_t* vct = repair ? rv_codes_t : v_codes_t;
+      int32_t vld = repair ? R_pad : S_pad;
+      int32_t k0 = t * 128, k1 = k0 + 128 < lim ? k0 + 128 : lim;
       float mxacc = -INFINITY;
       for (int32_t kk = k0; kk < k1; ++kk) {
         double s = 0.0; /* exact: FP8 x FP8 products summed over D <= 256 fit in fp64 */
-        for (int32_t d = 0; d < D; ++d) s += dq[d] * DEC(k_codes[(int64_t)kk * D + d]);
+        for (int32_t d = 0; d < D; ++d) s += dq[d] * DEC(kc[(int64_t)kk * D + d]);
         acc[kk - k0] = (float)s;
         mxacc = fmaxf(mxacc, acc[kk - k0]);
       }
-      float g = c2 * k_scale[t];
+      float g = c2 * (repair ? rk_scale[t] : k_scale[t]);
       float mx = g * mxacc;
       float Mn = fmaxf(M, mx);
       if (Mn > M) {
@@ -597,8 +683,9 @@ EXPORT void vco_attn_emulate_rows(const uint8_t* q_codes, const float* q_scale, 
         }
         if (w == 0.0) continue;
         r += w;
-        for (int32_t d = 0; d < D; ++d) A[d] += w * DEC(v_codes_t[(int64_t)d * S_pad + kk]);
+        for (int32_t d = 0; d < D; ++d) A[d] += w * DEC(vct[(int64_t)d * vld + kk]);
       }
+      if (repair) continue; /* the denominator already counts these keys */
       if (mu_scaled)
         for (int32_t d = 0; d < D; ++d) A[d] += r * (double)mu_scaled[(int64_t)t * D + d];
       l += r;
