@@ -8,9 +8,11 @@ on a non-OK status.  There is no CPU fallback: if the library is missing or
 no GPU is present, calls fail loudly.
 
 Entry points (same names as the C ABI): vc_abi_version, vc_status_str,
-vc_quantize, vc_smooth_group_workspace_size, vc_smooth_group, vc_attn_fwd,
-vc_pack_v_bf16, vc_attn_fwd_bf16, vc_expcast_codes; and vsmooth_schedule, the
-host-side rule for which denoising steps group, reuse or run plain.
+vc_quantize, vc_smooth_group_workspace_size, vc_smooth_group,
+vc_repair_workspace_size, vc_repair_prepare, vc_attn_fwd, vc_pack_v_bf16,
+vc_attn_fwd_bf16, vc_expcast_codes; and vsmooth_schedule, the host-side rule
+for which denoising steps group, reuse or run plain, and repair_count, the
+number of repair rows for a fraction rho of the tokens.
 """
 from __future__ import annotations
 
@@ -28,7 +30,7 @@ VC_OK = 0
 VC_ATTN_SEQUENTIAL = 1
 VC_GROUP_WARM_START = 1
 VC_GROUP_REUSE_PERM = 2
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 class VcError(RuntimeError):
@@ -68,6 +70,11 @@ class vc_attn_params(ctypes.Structure):
     _fields_ = [("sm_scale", ctypes.c_float), ("window", ctypes.c_int32), ("flags", ctypes.c_uint32)]
 
 
+class vc_repair_rows(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int32), ("k8", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+                ("v8", ctypes.c_void_p)]
+
+
 def lib():
     """Load libvcattn.so (built by __graft_entry__.build())."""
     global _lib
@@ -88,7 +95,11 @@ def lib():
         L.vc_smooth_group_workspace_size.restype = sz
         L.vc_smooth_group.argtypes = [P] * 15 + [sz, P]
         L.vc_smooth_group.restype = i32
-        L.vc_attn_fwd.argtypes = [P] * 11
+        L.vc_repair_workspace_size.argtypes = [P]
+        L.vc_repair_workspace_size.restype = sz
+        L.vc_repair_prepare.argtypes = [P, P, P, P, i32, P, P, P, P, P, sz, P]
+        L.vc_repair_prepare.restype = i32
+        L.vc_attn_fwd.argtypes = [P] * 12
         L.vc_attn_fwd.restype = i32
         L.vc_pack_v_bf16.argtypes = [P] * 4
         L.vc_pack_v_bf16.restype = i32
@@ -284,10 +295,11 @@ def vsmooth_schedule(n_steps: int, step: int, reuse: int = 4) -> str:
 # --------------------------------------------------------------------------- #
 
 def vc_attn_fwd(q8, q_scale, k8, k_scale, v8, v_scale, mu_split=None, *, S: int, out=None, window: int = 2,
-                sequential: bool = False):
+                sequential: bool = False, repair=None):
     """FP8 ExpCast attention.  Codes and scales as produced by vc_quantize /
     vc_smooth_group (the softmax scale rides in q8: pass it to vc_quantize);
-    S is the token count.  Returns bf16 [B,S,H,D]."""
+    S is the token count; repair: None or the dict of vc_repair_prepare
+    (plain path only).  Returns bf16 [B,S,H,D]."""
     B, H, S_pad, D = q8.shape
     assert S_pad == nblk_of(S) * 128
     sh = vc_shape(B, H, S, D)
@@ -295,10 +307,60 @@ def vc_attn_fwd(q8, q_scale, k8, k_scale, v8, v_scale, mu_split=None, *, S: int,
         out = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=q8.device)
     p = vc_attn_params(0.0, window, VC_ATTN_SEQUENTIAL if sequential else 0)
     od = _bshd_out(out)
+    rp = None
+    if repair is not None and repair["rows"] > 0:
+        rp = vc_repair_rows(int(repair["rows"]), _ptr(repair["rk8"]), _ptr(repair["rk_scale"]), _ptr(repair["rv8"]))
     st = lib().vc_attn_fwd(ctypes.byref(sh), ctypes.byref(p), _ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale),
-                           _ptr(v8), _ptr(v_scale), _ptr(mu_split), ctypes.byref(od), _stream())
+                           _ptr(v8), _ptr(v_scale), _ptr(mu_split), ctypes.byref(rp) if rp is not None else None,
+                           ctypes.byref(od), _stream())
     _check(st, "vc_attn_fwd")
     return out
+
+
+# --------------------------------------------------------------------------- #
+# vc_repair_prepare
+# --------------------------------------------------------------------------- #
+
+def repair_count(S: int, rho: float) -> int:
+    """Repair rows for a fraction rho of the S tokens: ceil(rho S), at most S
+    ([OVC] "Why V residual repair" uses rho = 0.5%)."""
+    if rho <= 0:
+        return 0
+    return min(S, math.ceil(rho * S - 1e-9))
+
+
+def vc_repair_workspace_size(B: int, H: int, S: int, D: int) -> int:
+    sh = vc_shape(B, H, S, D)
+    return int(lib().vc_repair_workspace_size(ctypes.byref(sh)))
+
+
+def vc_repair_prepare(k, v, rows: int, *, prep=None, workspace=None, out=None):
+    """V residual repair rows.  k, v: bf16 [B,S,H,D]; rows: R in [0, S];
+    prep: K's preprocessing as given to vc_quantize.  Returns dict with rows,
+    idx int32 [B,H,R], rk8 uint8 [B,H,nrb*128,D] (packed K tiles), rk_scale
+    fp32 [B,H,nrb], rv8 uint8 [B,H,nrb,D,128] (packed V tiles)."""
+    sh = _shape_of(v)
+    B, H, S, D = sh.B, sh.H, sh.S, sh.D
+    R = int(rows)
+    nrb = (R + 127) // 128
+    dev = v.device
+    o = dict(out or {})
+    o["rows"] = R
+    o.setdefault("idx", torch.empty((B, H, max(R, 1)), dtype=torch.int32, device=dev))
+    o.setdefault("rk8", torch.empty((B, H, max(nrb, 1) * 128, D), dtype=torch.uint8, device=dev))
+    o.setdefault("rk_scale", torch.empty((B, H, max(nrb, 1)), dtype=torch.float32, device=dev))
+    o.setdefault("rv8", torch.empty((B, H, max(nrb, 1), D, 128), dtype=torch.uint8, device=dev))
+    wsb = vc_repair_workspace_size(B, H, S, D)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    kd, vd = _bshd(k), _bshd(v)
+    pp, _ws = _prep(prep, k, True)
+    st = lib().vc_repair_prepare(ctypes.byref(sh), ctypes.byref(pp) if pp is not None else None, ctypes.byref(kd),
+                                 ctypes.byref(vd), R, _ptr(o["idx"]), _ptr(o["rk8"]), _ptr(o["rk_scale"]),
+                                 _ptr(o["rv8"]), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream())
+    _check(st, "vc_repair_prepare")
+    return o
 
 
 def vc_pack_v_bf16(v, *, out=None):

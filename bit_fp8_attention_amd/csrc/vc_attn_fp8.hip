@@ -120,8 +120,9 @@ template <int D, bool VS>
 __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ q_scale, const uint8_t* __restrict__ k8,
     const float* __restrict__ k_scale, const uint8_t* __restrict__ v8, const float* __restrict__ v_scale,
-    const u32* __restrict__ mu, uint16_t* __restrict__ o, int64_t oB, int64_t oS, int64_t oH, int S, int H,
-    int nblk, int npair, int window, int sequential) {
+    const u32* __restrict__ mu, const uint8_t* __restrict__ rk8, const float* __restrict__ rk_scale,
+    const uint8_t* __restrict__ rv8, int nrb, uint16_t* __restrict__ o, int64_t oB, int64_t oS, int64_t oH, int S,
+    int H, int nblk, int npair, int window, int sequential) {
   constexpr int NM = D / 16;             // channel blocks of the output
   constexpr int TB = kBlk * D;           // bytes of one K or V tile
   constexpr int NI = TB / 1024 / 4;      // 1 KB copies per issuing wave per tile
@@ -145,7 +146,9 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
   const bool hb = w >= 4;                                  // half B
   const int wq = w & 3;                                    // wave within the half
-  const int n = nblk;
+  // visits: the nblk regular key tiles, then (plain path) the nrb repair
+  // tiles ([OVC] "Why V residual repair": visited last, numerator only)
+  const int n = VS ? nblk : nblk + nrb;
   // with an odd number of query tiles, half B of the last pair repeats half
   // A's tile (it must take part in every barrier) and stores nothing
   const bool live = 2 * pr + (hb ? 1 : 0) < nblk;
@@ -155,12 +158,23 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
   const uint8_t* kb = k8 + (int64_t)bh * S_pad * D;
   const uint8_t* vb = v8 + (int64_t)bh * D * S_pad;  // packed: tile t at + t * 128 * D
   const float* ksb = k_scale + (int64_t)bh * nblk;
+  // repair tile r is visit nblk + r, and tile_at(i) = i past the regular
+  // visits, so the repair bases are shifted down by nblk tiles (integer
+  // arithmetic: the shifted address itself is never read) and a visit's
+  // source is base(i) + tile_at(i) * TB either way
+  const uint8_t* rkb = (const uint8_t*)((uintptr_t)(rk8 + (int64_t)bh * nrb * TB) - (uintptr_t)nblk * TB);
+  const uint8_t* rvb = (const uint8_t*)((uintptr_t)(rv8 + (int64_t)bh * nrb * TB) - (uintptr_t)nblk * TB);
+  const float* rksb = (const float*)((uintptr_t)(rk_scale + (int64_t)bh * nrb) - (uintptr_t)nblk * sizeof(float));
   // E8M0 block scale of the query tile (Q's codes carry 8 sm_scale log2 e)
   const int sq = __builtin_amdgcn_readfirstlane(e8m0_of_pow2(q_scale[(int64_t)bh * nblk + qt]));
 
   // mid-window order of the pair: start a few tiles past the pair's diagonal
   const int start = __builtin_amdgcn_readfirstlane(sequential ? 0 : min(2 * pr + 1 + window, nblk - 1));
   auto tile_at = [&](int i) -> int { return sequential ? i : (i <= start ? start - i : i); };
+  auto repair_visit = [&](int i) { return !VS && i >= nblk; };
+  auto ksrc = [&](int i) { return (repair_visit(i) ? rkb : kb) + (int64_t)tile_at(i) * TB; };
+  auto vsrc = [&](int i) { return (repair_visit(i) ? rvb : vb) + (int64_t)tile_at(i) * TB; };
+  auto kscale = [&](int i) { return (repair_visit(i) ? rksb : ksb)[tile_at(i)]; };
 
   const unsigned loff = (unsigned)l * 16u;
   // copies of half B, wave wq: 1 KB blocks 4r + wq of a tile; with V-Smooth
@@ -173,7 +187,7 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
     }
   };
   auto issue_k = [&](uint8_t* dst, int i) {
-    const uint8_t* src = kb + (int64_t)tile_at(i) * TB;
+    const uint8_t* src = ksrc(i);
 #pragma unroll
     for (int r = 0; r < NI; ++r) {
       const int base = (r * 4 + wq) * 1024;
@@ -181,7 +195,7 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
     }
   };
   auto issue_v = [&](uint8_t* dst, int i) {
-    const uint8_t* src = vb + (int64_t)tile_at(i) * TB;
+    const uint8_t* src = vsrc(i);
 #pragma unroll
     for (int r = 0; r < NI; ++r) {
       const int base = (r * 4 + wq) * 1024;
@@ -191,9 +205,9 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
   constexpr int GRP = 2 * NI + (VS ? 1 : 0);  // copies per wave per full group
 
   const FragBase<D> fb(lr, g);
-  const bool ragged = (S % kBlk) != 0;
-  const bool tail_first = ragged && tile_at(0) == n - 1;
-  const bool tail_last = ragged && !tail_first;  // then tile_at(n - 1) == n - 1
+  // visit of the ragged last key tile: first when the order starts there,
+  // else visit nblk - 1 (the last regular one); -1 if S fills its tiles
+  const int tail_visit = (S % kBlk) == 0 ? -1 : (tile_at(0) == nblk - 1 ? 0 : nblk - 1);
 
   if (VS) {  // rows never written must read as finite zeros
     u32* mz = &mring[0][0];
@@ -241,7 +255,7 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
   float rb[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
   v4f Sc[2][8];                               // S^T of the current tile
   float pm[2];                                // max of its key blocks 0..5 (steady-state tiles)
-  int skv = e8m0_of_pow2(ksb[tile_at(0)]);    // E8M0 key scale of the current tile
+  int skv = e8m0_of_pow2(kscale(0));          // E8M0 key scale of the current tile
   v4f cinit[2] = {zero4, zero4};
   v8i P[2];                                   // codes of the previous tile
 
@@ -329,7 +343,7 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
       const int slot = i & 7;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        Lq[s] += rr[s];
+        if (!repair_visit(i)) Lq[s] += rr[s];  // repair rows: numerator only
         if (VS) {
           if (slot == 2 * g) rb[s][0] = rr[s];
           if (slot == 2 * g + 1) rb[s][1] = rr[s];
@@ -451,7 +465,7 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
       }
     }
     // the next tile's key scale, a whole phase before it is needed
-    if (j + 1 < n) skv = e8m0_of_pow2(ksb[tile_at(j + 1)]);
+    if (j + 1 < n) skv = e8m0_of_pow2(kscale(j + 1));
     if (hb) {
       if (j + 2 < n) issue_mu(j + 2);
       if (j + 3 < n) issue_k(Kdst, j + 3);
@@ -484,7 +498,7 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
   mphase(0, kst0, vst2, std::false_type{}, std::true_type{}, std::false_type{});
   mwait(0);
   phase_sync();
-  vphase(0, kst0, vst2, tail_first, std::false_type{});
+  vphase(0, kst0, vst2, tail_visit == 0, std::false_type{});
   phase_sync();
 
   // steady state, rolled: stages picked at run time (j mod 3)
@@ -497,6 +511,20 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
       mwait(j);
       phase_sync();
       vphase(j, Kc, Vc, false, std::true_type{});
+      // plain path with repair tiles: the ragged tile may fall in here.  The
+      // running max above then covered its pad keys, harmless because
+      // vc_quantize makes them copies of the last key; their codes are
+      // cleared here so that the row sum counts only the valid keys
+      if (!VS && j == tail_visit) {
+        const int lim = S - (nblk - 1) * kBlk;
+#pragma unroll
+        for (int t8 = 0; t8 < 8; ++t8) {
+          const int k0 = 16 * t8 + 4 * g;  // key of byte 0 of register t8
+          const u32 keep = k0 + 4 <= lim ? 0xffffffffu : (k0 >= lim ? 0u : (1u << (8 * (lim - k0))) - 1u);
+          P[0][t8] = (int)((u32)P[0][t8] & keep);
+          P[1][t8] = (int)((u32)P[1][t8] & keep);
+        }
+      }
       phase_sync();
       ck = ck == 2 ? 0 : ck + 1;
       cv = cv == 2 ? 0 : cv + 1;
@@ -511,7 +539,7 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
     mphase(n - 1, Kl, Vp, std::true_type{}, std::true_type{}, std::false_type{});
     mwait(n - 1);
     phase_sync();
-    vphase(n - 1, Kl, Vp, tail_last, std::false_type{});
+    vphase(n - 1, Kl, Vp, tail_visit == n - 1, std::false_type{});
     phase_sync();
   }
   // M(n): the last P.V
@@ -544,12 +572,12 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
 template <int D, bool VS>
 hipError_t launch_t(const vc_shape& sh, int window, int seq, const uint8_t* q8, const float* qs,
                     const uint8_t* k8, const float* ks, const uint8_t* v8, const float* vs, const u32* mu,
-                    BshdOut o, hipStream_t st) {
+                    RepairTiles rp, BshdOut o, hipStream_t st) {
   const int nblk = (sh.S + kBlk - 1) / kBlk;
   const int npair = (nblk + 1) / 2;
   const int64_t n = (int64_t)npair * sh.H * sh.B;
-  attn_fp8_kernel<D, VS><<<(unsigned)n, 512, 0, st>>>(q8, qs, k8, ks, v8, vs, mu, o.p, o.sB, o.sS, o.sH, sh.S,
-                                                          sh.H, nblk, npair, window, seq);
+  attn_fp8_kernel<D, VS><<<(unsigned)n, 512, 0, st>>>(q8, qs, k8, ks, v8, vs, mu, rp.k8, rp.k_scale, rp.v8, rp.nrb,
+                                                          o.p, o.sB, o.sS, o.sH, sh.S, sh.H, nblk, npair, window, seq);
   return hipGetLastError();
 }
 
@@ -557,14 +585,16 @@ hipError_t launch_t(const vc_shape& sh, int window, int seq, const uint8_t* q8, 
 
 hipError_t launch_attn_fp8(const vc_shape& sh, int window, uint32_t flags, const uint8_t* q8, const float* q_scale,
                            const uint8_t* k8, const float* k_scale, const uint8_t* v8, const float* v_scale,
-                           const u32* mu_split, BshdOut o, hipStream_t st) {
+                           const u32* mu_split, RepairTiles rp, BshdOut o, hipStream_t st) {
   const int seq = (flags & VC_ATTN_SEQUENTIAL) ? 1 : 0;
+  const RepairTiles none{0, nullptr, nullptr, nullptr};
   if (sh.D == 128) {
-    if (mu_split) return launch_t<128, true>(sh, window, seq, q8, q_scale, k8, k_scale, v8, v_scale, mu_split, o, st);
-    return launch_t<128, false>(sh, window, seq, q8, q_scale, k8, k_scale, v8, v_scale, nullptr, o, st);
+    if (mu_split)
+      return launch_t<128, true>(sh, window, seq, q8, q_scale, k8, k_scale, v8, v_scale, mu_split, none, o, st);
+    return launch_t<128, false>(sh, window, seq, q8, q_scale, k8, k_scale, v8, v_scale, nullptr, rp, o, st);
   }
-  if (mu_split) return launch_t<64, true>(sh, window, seq, q8, q_scale, k8, k_scale, v8, v_scale, mu_split, o, st);
-  return launch_t<64, false>(sh, window, seq, q8, q_scale, k8, k_scale, v8, v_scale, nullptr, o, st);
+  if (mu_split) return launch_t<64, true>(sh, window, seq, q8, q_scale, k8, k_scale, v8, v_scale, mu_split, none, o, st);
+  return launch_t<64, false>(sh, window, seq, q8, q_scale, k8, k_scale, v8, v_scale, nullptr, rp, o, st);
 }
 
 }  // namespace vc

@@ -167,7 +167,8 @@ __attribute__((visibility("default"))) int32_t vc_attn_fwd(const vc_shape* sh, c
                                                             const uint8_t* q8, const float* q_scale,
                                                             const uint8_t* k8, const float* k_scale,
                                                             const uint8_t* v8, const float* v_scale,
-                                                            const uint32_t* mu_split, const vc_bshd_out* o,
+                                                            const uint32_t* mu_split,
+                                                            const vc_repair_rows* repair, const vc_bshd_out* o,
                                                             void* stream) {
   int32_t e = check_shape(sh);
   if (e) return e;
@@ -177,9 +178,46 @@ __attribute__((visibility("default"))) int32_t vc_attn_fwd(const vc_shape* sh, c
   if (((uintptr_t)q_scale | (uintptr_t)k_scale | (uintptr_t)v_scale | (uintptr_t)mu_split) & 3u) return VC_ERR_ALIGN;
   if (p->window < 0 || (p->flags & ~VC_ATTN_SEQUENTIAL)) return VC_ERR_UNSUPPORTED;
   if (!(p->sm_scale >= 0.0f) || isinf(p->sm_scale)) return VC_ERR_UNSUPPORTED;
+  vc::RepairTiles rp{0, nullptr, nullptr, nullptr};
+  if (repair && repair->rows != 0) {
+    if (repair->rows < 0 || repair->rows > sh->S) return VC_ERR_SHAPE;
+    if (mu_split) return VC_ERR_UNSUPPORTED;  // repair rows belong to the plain path
+    if (!repair->k8 || !repair->k_scale || !repair->v8) return VC_ERR_NULL;
+    if (!aligned16(repair->k8) || !aligned16(repair->v8) || ((uintptr_t)repair->k_scale & 3u)) return VC_ERR_ALIGN;
+    rp = vc::RepairTiles{(repair->rows + 127) / 128, repair->k8, repair->k_scale, repair->v8};
+  }
   BshdOut ob{(uint16_t*)o->ptr, o->sB, o->sS, o->sH};
   return hip_status(vc::launch_attn_fp8(*sh, p->window, p->flags, q8, q_scale, k8, k_scale, v8, v_scale,
-                                        mu_split, ob, (hipStream_t)stream));
+                                        mu_split, rp, ob, (hipStream_t)stream));
+}
+
+__attribute__((visibility("default"))) size_t vc_repair_workspace_size(const vc_shape* sh) {
+  if (check_shape(sh)) return 0;
+  return vc::repair_workspace_bytes(*sh);
+}
+
+__attribute__((visibility("default"))) int32_t vc_repair_prepare(const vc_shape* sh, const vc_prep_params* prep,
+                                                                  const vc_bshd* k, const vc_bshd* v, int32_t rows,
+                                                                  int32_t* idx, uint8_t* rk8, float* rk_scale,
+                                                                  uint8_t* rv8, void* workspace,
+                                                                  size_t workspace_bytes, void* stream) {
+  int32_t e = check_shape(sh);
+  if (e) return e;
+  if (rows < 0 || rows > sh->S) return VC_ERR_SHAPE;
+  if ((e = check_bshd(k)) || (e = check_bshd(v))) return e;
+  vc::PrepArgs pa;
+  if ((e = check_prep(sh, prep, true, &pa))) return e;
+  if (rows == 0) return VC_OK;
+  if (!idx || !rk8 || !rk_scale || !rv8 || !workspace) return VC_ERR_NULL;
+  if (!aligned16(rk8) || !aligned16(rv8) || ((uintptr_t)workspace & 255u)) return VC_ERR_ALIGN;
+  if (((uintptr_t)idx | (uintptr_t)rk_scale) & 3u) return VC_ERR_ALIGN;
+  if (workspace_bytes < vc::repair_workspace_bytes(*sh)) return VC_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  if ((pa.flags & VC_PREP_K_CENTER) &&
+      (e = hip_status(vc::launch_k_center_sums(*sh, as_bshd(k), pa, (unsigned long long*)prep->workspace, st))))
+    return e;
+  return hip_status(vc::launch_repair_prepare(*sh, as_bshd(k), as_bshd(v), pa, rows, idx, rk8, rk_scale, rv8,
+                                              workspace, st));
 }
 
 __attribute__((visibility("default"))) int32_t vc_pack_v_bf16(const vc_shape* sh, const vc_bshd* v, uint16_t* vt,

@@ -14,6 +14,7 @@
 // reduction, E4M3 conversion with the hardware round-half-even convert.
 #include "vc_common.hpp"
 #include "vc_prep.hpp"
+#include "vc_vscale.hpp"
 #include "vc_launch.hpp"
 
 namespace vc {
@@ -50,16 +51,6 @@ VC_DEV float block_max256(float m, float* red) {
   return m;
 }
 
-VC_DEV void scale_pair(float amax, float& s, float& inv) {
-  if (amax > 0.0f) {
-    s = amax / 448.0f;
-    inv = 448.0f / amax;
-  } else {
-    s = 1.0f;
-    inv = 1.0f;
-  }
-}
-
 // Q or K: one workgroup per (block j, head h, batch b).  PACK writes the
 // packed K layout (chunk-swizzled rows), otherwise plain row-major codes.
 // With preprocessing ([VC] §3.4, App. B), each valid row is first rotated
@@ -69,10 +60,15 @@ VC_DEV void scale_pair(float amax, float& s, float& inv) {
 // pre (Q: G = 8 fl(sm_scale log2 e), over D with the rotation; K: 1); the
 // block scale is the power of two pow2_block_exp picks for the products'
 // amax (the max of the rounded products).
-template <int D, bool PACK>
+// GATHER: block j holds rows gat[128 j + r] (r < 128) of the head's tokens,
+// the last listed row repeated past its end R ([OVC] "Why V residual
+// repair": the keys of the repair rows, prepared as at their own positions);
+// nblk then counts the output blocks.
+template <int D, bool PACK, bool GATHER>
 __global__ __launch_bounds__(256) void qk_block_quant(const uint16_t* __restrict__ x, int64_t sB, int64_t sS,
                                                       int64_t sH, int S, int H, int nblk, float pre, PrepArgs pp,
-                                                      uint8_t* __restrict__ codes, float* __restrict__ scale) {
+                                                      uint8_t* __restrict__ codes, float* __restrict__ scale,
+                                                      const int32_t* __restrict__ gat, int R) {
   constexpr int CPR = D / 8;             // 16-byte chunks per row
   constexpr int NCH = kBlk * CPR / 256;  // chunks per thread
   __shared__ float red[4];
@@ -80,10 +76,24 @@ __global__ __launch_bounds__(256) void qk_block_quant(const uint16_t* __restrict
   const int64_t bh = (int64_t)b * H + h;
   const uint16_t* xb = x + b * sB + h * sH;
   const int ch = t % CPR;  // the same chunk for every row of this thread
+  // token of block row r; K (PACK) rows past the end repeat the last row,
+  // so a ragged tile's max over all its rows is that of its valid rows
+  auto token = [&](int r) -> int {
+    if constexpr (GATHER) {
+      const int i = j * kBlk + r;
+      const int tok = gat[bh * R + (i < R ? i : R - 1)];
+      return tok < 0 ? 0 : (tok < S ? tok : S - 1);  // in bounds whatever the list holds
+    } else if constexpr (PACK) {
+      const int tok = j * kBlk + r;
+      return tok < S ? tok : S - 1;
+    } else {
+      return j * kBlk + r;
+    }
+  };
   float xv[NCH][8];
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    const int row = (t + 256 * i) / CPR, tok = j * kBlk + row;
+    const int row = (t + 256 * i) / CPR, tok = token(row);
     unpack8(tok < S ? *(const uint4*)(xb + (int64_t)tok * sS + ch * 8) : make_uint4(0, 0, 0, 0), xv[i]);
   }
   if (pp.flags) {
@@ -94,7 +104,7 @@ __global__ __launch_bounds__(256) void qk_block_quant(const uint16_t* __restrict
     }
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int row = (t + 256 * i) / CPR, tok = j * kBlk + row;
+      const int row = (t + 256 * i) / CPR, tok = token(row);
       if (tok < S) {
         if (pp.flags & kPrepRope) rope8(xv[i], pp.cs + (int64_t)tok * (D / 2) + ch * 4, pp.sn + (int64_t)tok * (D / 2) + ch * 4);
         if (pp.flags & kPrepCenter)
@@ -170,10 +180,10 @@ __global__ void zero_u64(unsigned long long* __restrict__ p, int64_t n) {
 }
 
 // V pass 1: per-(b,h) amax as ordered uint bits, accumulated into
-// v_scale[bh*D] (zeroed beforehand).  256 tokens per workgroup.
+// out[bh * stride] (zeroed beforehand).  256 tokens per workgroup.
 template <int D>
 __global__ __launch_bounds__(256) void v_amax(const uint16_t* __restrict__ x, int64_t sB, int64_t sS, int64_t sH,
-                                              int S, int H, float* __restrict__ v_scale) {
+                                              int S, int H, float* __restrict__ out, int stride) {
   constexpr int CPR = D / 8;
   constexpr int NCH = 256 * CPR / 256;
   __shared__ float red[4];
@@ -186,12 +196,12 @@ __global__ __launch_bounds__(256) void v_amax(const uint16_t* __restrict__ x, in
     if (tok < S) m = amax8(*(const uint4*)(xb + (int64_t)tok * sS + ch * 8), m);
   }
   m = block_max256(m, red);
-  if (t == 0) atomicMax((unsigned int*)(v_scale + ((int64_t)b * H + h) * D), __float_as_uint(m));
+  if (t == 0) atomicMax((unsigned int*)(out + ((int64_t)b * H + h) * stride), __float_as_uint(m));
 }
 
-__global__ void v_amax_zero(float* v_scale, int BH, int D) {
+__global__ void v_amax_zero(float* out, int BH, int stride) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < BH) v_scale[(int64_t)i * D] = 0.0f;
+  if (i < BH) out[(int64_t)i * stride] = 0.0f;
 }
 
 // V pass 2: convert one 128-token block and write it as a packed V tile
@@ -306,37 +316,63 @@ hipError_t launch_k_center_sums(const vc_shape& sh, Bshd x, PrepArgs pp, unsigne
   return hipGetLastError();
 }
 
-hipError_t launch_qk_quant(const vc_shape& sh, Bshd x, float pre, PrepArgs pp, uint8_t* codes, float* scale,
-                           bool pack, hipStream_t st) {
-  int nblk = (sh.S + kBlk - 1) / kBlk;
-  dim3 grid(nblk, sh.H, sh.B);
+namespace {
+template <bool GATHER>
+hipError_t qk_quant_t(const vc_shape& sh, Bshd x, float pre, PrepArgs pp, uint8_t* codes, float* scale, bool pack,
+                      int nb, const int32_t* gat, int R, hipStream_t st) {
+  dim3 grid(nb, sh.H, sh.B);
   if (sh.D == 128) {
     if (pack)
-      qk_block_quant<128, true><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nblk, pre, pp, codes, scale);
+      qk_block_quant<128, true, GATHER><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nb, pre, pp, codes,
+                                                               scale, gat, R);
     else
-      qk_block_quant<128, false><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nblk, pre, pp, codes, scale);
+      qk_block_quant<128, false, GATHER><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nb, pre, pp, codes,
+                                                                scale, gat, R);
   } else {
     if (pack)
-      qk_block_quant<64, true><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nblk, pre, pp, codes, scale);
+      qk_block_quant<64, true, GATHER><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nb, pre, pp, codes,
+                                                              scale, gat, R);
     else
-      qk_block_quant<64, false><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nblk, pre, pp, codes, scale);
+      qk_block_quant<64, false, GATHER><<<grid, 256, 0, st>>>(x.p, x.sB, x.sS, x.sH, sh.S, sh.H, nb, pre, pp, codes,
+                                                               scale, gat, R);
   }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_qk_quant(const vc_shape& sh, Bshd x, float pre, PrepArgs pp, uint8_t* codes, float* scale,
+                           bool pack, hipStream_t st) {
+  const int nblk = (sh.S + kBlk - 1) / kBlk;
+  return qk_quant_t<false>(sh, x, pre, pp, codes, scale, pack, nblk, nullptr, 0, st);
+}
+
+hipError_t launch_k_gather_quant(const vc_shape& sh, Bshd k, PrepArgs pp, const int32_t* idx, int R, uint8_t* k8,
+                                 float* k_scale, hipStream_t st) {
+  if (R <= 0) return hipSuccess;
+  return qk_quant_t<true>(sh, k, 1.0f, pp, k8, k_scale, true, (R + kBlk - 1) / kBlk, idx, R, st);
+}
+
+hipError_t launch_v_amax(const vc_shape& sh, Bshd v, float* out, int stride, hipStream_t st) {
+  const int BH = sh.B * sh.H;
+  v_amax_zero<<<(BH + 255) / 256, 256, 0, st>>>(out, BH, stride);
+  dim3 g1((sh.S + 255) / 256, sh.H, sh.B);
+  if (sh.D == 128)
+    v_amax<128><<<g1, 256, 0, st>>>(v.p, v.sB, v.sS, v.sH, sh.S, sh.H, out, stride);
+  else
+    v_amax<64><<<g1, 256, 0, st>>>(v.p, v.sB, v.sS, v.sH, sh.S, sh.H, out, stride);
   return hipGetLastError();
 }
 
 hipError_t launch_v_quant(const vc_shape& sh, Bshd v, uint8_t* v8, float* v_scale, hipStream_t st) {
   int nblk = (sh.S + kBlk - 1) / kBlk;
-  int BH = sh.B * sh.H;
-  v_amax_zero<<<(BH + 255) / 256, 256, 0, st>>>(v_scale, BH, sh.D);
-  dim3 g1((sh.S + 255) / 256, sh.H, sh.B), g2(nblk, sh.H, sh.B);
-  if (sh.D == 128) {
-    v_amax<128><<<g1, 256, 0, st>>>(v.p, v.sB, v.sS, v.sH, sh.S, sh.H, v_scale);
+  launch_v_amax(sh, v, v_scale, sh.D, st);
+  dim3 g2(nblk, sh.H, sh.B);
+  if (sh.D == 128)
     v_convert<128><<<g2, 256, 0, st>>>(v.p, v.sB, v.sS, v.sH, sh.S, sh.H, nblk, v_scale, v8);
-  } else {
-    v_amax<64><<<g1, 256, 0, st>>>(v.p, v.sB, v.sS, v.sH, sh.S, sh.H, v_scale);
+  else
     v_convert<64><<<g2, 256, 0, st>>>(v.p, v.sB, v.sS, v.sH, sh.S, sh.H, nblk, v_scale, v8);
-  }
-  v_finalize<<<BH, 128, 0, st>>>(v_scale, sh.D);
+  v_finalize<<<sh.B * sh.H, 128, 0, st>>>(v_scale, sh.D);
   return hipGetLastError();
 }
 

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define VC_ABI_VERSION 4
+#define VC_ABI_VERSION 5
 
 typedef enum vc_status {
   VC_OK = 0,
@@ -149,8 +149,10 @@ size_t vc_prep_workspace_size(const vc_shape* shape);
  *   y = fl(x * pre); amax = max |y| over the block's valid rows;
  *   e = the smallest integer >= -127 with amax <= 448 * 2^e (e = 0 for a
  *   block of zeros); scale = 2^e; code = E4M3_rne(y * 2^-e).
- *   Rows >= S are written as code 0.  So Q * G ~= q8 * q_scale and
- *   K ~= k8 * k_scale.
+ *   Q rows >= S are written as code 0; K rows >= S repeat the codes of
+ *   row S - 1 (so the ragged last tile's max over all its rows is that of
+ *   its valid rows -- the attention kernel relies on it when repair tiles
+ *   follow that tile).  So Q * G ~= q8 * q_scale and K ~= k8 * k_scale.
  *   q8:           uint8 [B][H][S_pad][D] row-major
  *   k8:           packed K (B*H*S_pad*D bytes)
  *   q_scale, k_scale: fp32 [B][H][nblk] (powers of two)
@@ -233,6 +235,46 @@ int32_t vc_smooth_group(const vc_shape* shape, const vc_bshd* k, const vc_bshd* 
 
 /* ----------------------------------------------------------------------- */
 
+/*
+ * V residual repair rows ([OVC] "Why V residual repair"; plain path only).
+ * With one FP8 scale per head, token j keeps the residual
+ * r_j = V_j - s * Vhat_j, s = amax / 448, Vhat_j = E4M3_rne(V_j * (448 / amax))
+ * (per element, each operation rounded once in fp32).  The R tokens of
+ * largest residual energy sum_d r_jd^2 (fp64, summed over d = 0..D-1 in
+ * order; ties go to the lower token index) become repair rows: the key of
+ * the token, prepared as K is (vc_quantize's prep, at the token's own
+ * position), paired with the residual as a value row.  The pages pick
+ * R = ceil(rho S) with rho = 0.5%; the caller passes R.
+ *
+ * vc_repair_prepare writes, per (b, h), with nrb = ceil(R / 128):
+ *   idx      int32 [B][H][R]: the selected token indices, ascending;
+ *   rk8      packed K tiles [B][H][nrb] (the packed K layout with nrb in
+ *            place of nblk): repair row i < R holds key idx[i]; rows past R
+ *            repeat key idx[R-1] (so a tile's max is that of its real rows);
+ *   rk_scale fp32 [B][H][nrb]: power-of-two block scales as vc_quantize's;
+ *   rv8      packed V tiles [B][H][nrb]: code E4M3_rne(r * (448 / amax)),
+ *            the head's own V scale (so v_scale of vc_quantize applies);
+ *            rows past R are code 0.
+ * prep: K's preprocessing, as passed to vc_quantize (NULL for none).
+ * rows: R in [0, S]; R = 0 writes nothing.
+ * workspace: device, 256-byte aligned, >= vc_repair_workspace_size(shape)
+ * bytes; its contents on entry do not matter.
+ */
+size_t vc_repair_workspace_size(const vc_shape* shape);
+int32_t vc_repair_prepare(const vc_shape* shape, const vc_prep_params* prep, const vc_bshd* k, const vc_bshd* v,
+                          int32_t rows, int32_t* idx, uint8_t* rk8, float* rk_scale, uint8_t* rv8, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Repair rows for vc_attn_fwd (rows = 0 or a NULL pointer to this: none). */
+typedef struct vc_repair_rows {
+  int32_t rows;          /* R from vc_repair_prepare */
+  const uint8_t* k8;     /* rk8 */
+  const float* k_scale;  /* rk_scale */
+  const uint8_t* v8;     /* rv8 */
+} vc_repair_rows;
+
+/* ----------------------------------------------------------------------- */
+
 #define VC_ATTN_SEQUENTIAL 1u /* visit key blocks 0..nblk-1 instead of mid-window */
 
 typedef struct vc_attn_params {
@@ -271,6 +313,11 @@ typedef struct vc_attn_params {
  * with V-Smooth A += r * (hi + lo) of mu_split[t], as the three bf16
  * products r_hi hi + r_hi lo + r_lo hi on the matrix cores (r_hi = bf16(r),
  * r_lo = bf16(r - r_hi)), once per 8 visited tiles.
+ * repair (plain path only; with mu_split VC_ERR_UNSUPPORTED): after the
+ * nblk key blocks, the ceil(R / 128) repair tiles of vc_repair_prepare are
+ * visited in order, as above with their own key scales, except that l does
+ * not grow (their keys are counted once already) and only repair rows < R
+ * count towards the max.
  * Output: O = bf16((A / l) * v_scale[d]) written to `o` ([B,S,H,D] strided),
  * rows in the original query order.
  * Inputs are those of vc_quantize (plain path: q8 .. v_scale from it) or, for
@@ -282,7 +329,7 @@ typedef struct vc_attn_params {
  */
 int32_t vc_attn_fwd(const vc_shape* shape, const vc_attn_params* p, const uint8_t* q8, const float* q_scale,
                     const uint8_t* k8, const float* k_scale, const uint8_t* v8, const float* v_scale,
-                    const uint32_t* mu_split, const vc_bshd_out* o, void* stream);
+                    const uint32_t* mu_split, const vc_repair_rows* repair, const vc_bshd_out* o, void* stream);
 
 /* ----------------------------------------------------------------------- */
 

@@ -49,3 +49,12 @@ def unpack_v(packed: np.ndarray, D: int) -> np.ndarray:
     # [..., nblk, D, 128] -> [..., D, nblk*128]
     out = np.moveaxis(out, -3, -2)
     return out.reshape(lead + (D, S_pad))
+
+
+def k_matches(packed: np.ndarray, D: int, codes: np.ndarray, S: int) -> bool:
+    """vc_quantize's packed K against the oracle's row-major K codes: rows
+    < S equal, rows S .. S_pad - 1 copies of row S - 1 (the library pads K
+    with the last key; the oracle with zeros, which the method never reads)."""
+    got = unpack_k(packed, D)
+    return bool((got[..., :S, :] == codes[..., :S, :]).all()
+                and (got[..., S:, :] == got[..., S - 1:S, :]).all())

@@ -29,7 +29,8 @@ def vc():
 def test_header_declares_the_calls():
     names = _declared()
     for n in ["vc_abi_version", "vc_status_str", "vc_quantize", "vc_smooth_group_workspace_size",
-              "vc_smooth_group", "vc_attn_fwd", "vc_pack_v_bf16", "vc_attn_fwd_bf16", "vc_expcast_codes"]:
+              "vc_smooth_group", "vc_repair_workspace_size", "vc_repair_prepare", "vc_attn_fwd",
+              "vc_pack_v_bf16", "vc_attn_fwd_bf16", "vc_expcast_codes"]:
         assert n in names
 
 
@@ -40,7 +41,7 @@ def test_library_exports_every_declared_symbol(vc):
 
 
 def test_abi_version_and_status_strings(vc):
-    assert vc.vc_abi_version() == vc.ABI_VERSION == 4
+    assert vc.vc_abi_version() == vc.ABI_VERSION == 5
     assert vc.vc_status_str(0) == "VC_OK"
     for s in range(1, 7):
         assert vc.vc_status_str(s).startswith("VC_ERR_")
@@ -163,20 +164,54 @@ def test_attn_validation(vc):
     o = m.vc_bshd_out(FAKE, 256 * 2 * 128, 2 * 128, 128)
     good = m.vc_attn_params(0.0, 2, 0)
     args = [P(FAKE)] * 6
-    assert L.vc_attn_fwd(ctypes.byref(sh), None, *args, None, ctypes.byref(o), st) == 1
-    assert L.vc_attn_fwd(ctypes.byref(sh), ctypes.byref(good), P(FAKE), None, *[P(FAKE)] * 4, None,
-                         ctypes.byref(o), st) == 1
-    assert L.vc_attn_fwd(ctypes.byref(sh), ctypes.byref(m.vc_attn_params(0.0, -1, 0)), *args, None,
-                         ctypes.byref(o), st) == 4
-    assert L.vc_attn_fwd(ctypes.byref(sh), ctypes.byref(m.vc_attn_params(-1.0, 2, 0)), *args, None,
-                         ctypes.byref(o), st) == 4
-    assert L.vc_attn_fwd(ctypes.byref(sh), ctypes.byref(m.vc_attn_params(0.0, 2, 8)), *args, None,
-                         ctypes.byref(o), st) == 4
-    assert L.vc_attn_fwd(ctypes.byref(sh), ctypes.byref(good), P(FAKE + 4), *[P(FAKE)] * 5, None,
-                         ctypes.byref(o), st) == 3
-    assert L.vc_attn_fwd(ctypes.byref(sh), ctypes.byref(good), *args, None, None, st) == 1
-    assert L.vc_attn_fwd(ctypes.byref(m.vc_shape(1, 2, 256, 32)), ctypes.byref(good), *args, None,
-                         ctypes.byref(o), st) == 2
+    ob = ctypes.byref(o)
+    assert L.vc_attn_fwd(ctypes.byref(sh), None, *args, None, None, ob, st) == 1
+    assert L.vc_attn_fwd(ctypes.byref(sh), ctypes.byref(good), P(FAKE), None, *[P(FAKE)] * 4, None, None,
+                         ob, st) == 1
+    assert L.vc_attn_fwd(ctypes.byref(sh), ctypes.byref(m.vc_attn_params(0.0, -1, 0)), *args, None, None,
+                         ob, st) == 4
+    assert L.vc_attn_fwd(ctypes.byref(sh), ctypes.byref(m.vc_attn_params(-1.0, 2, 0)), *args, None, None,
+                         ob, st) == 4
+    assert L.vc_attn_fwd(ctypes.byref(sh), ctypes.byref(m.vc_attn_params(0.0, 2, 8)), *args, None, None,
+                         ob, st) == 4
+    assert L.vc_attn_fwd(ctypes.byref(sh), ctypes.byref(good), P(FAKE + 4), *[P(FAKE)] * 5, None, None,
+                         ob, st) == 3
+    assert L.vc_attn_fwd(ctypes.byref(sh), ctypes.byref(good), *args, None, None, None, st) == 1
+    assert L.vc_attn_fwd(ctypes.byref(m.vc_shape(1, 2, 256, 32)), ctypes.byref(good), *args, None, None,
+                         ob, st) == 2
+    # repair rows: count in [0, S], plain path only, pointers present and aligned
+    def rep(rows, k8=FAKE, ks=FAKE, v8=FAKE):
+        return ctypes.byref(m.vc_repair_rows(rows, k8, ks, v8))
+    assert L.vc_attn_fwd(ctypes.byref(sh), ctypes.byref(good), *args, None, rep(-1), ob, st) == 2
+    assert L.vc_attn_fwd(ctypes.byref(sh), ctypes.byref(good), *args, None, rep(257), ob, st) == 2
+    assert L.vc_attn_fwd(ctypes.byref(sh), ctypes.byref(good), *args, P(FAKE), rep(2), ob, st) == 4
+    assert L.vc_attn_fwd(ctypes.byref(sh), ctypes.byref(good), *args, None, rep(2, k8=None), ob, st) == 1
+    assert L.vc_attn_fwd(ctypes.byref(sh), ctypes.byref(good), *args, None, rep(2, v8=FAKE + 8), ob, st) == 3
+    assert L.vc_attn_fwd(ctypes.byref(sh), ctypes.byref(good), *args, None, rep(2, ks=FAKE + 2), ob, st) == 3
+
+
+def test_repair_validation(vc):
+    L, m = vc.lib(), vc
+    P = ctypes.c_void_p
+    sh = _shape()
+    st = ctypes.c_void_p(0)
+    x = m.vc_bshd(FAKE, 256 * 2 * 128, 2 * 128, 128)
+    xb = ctypes.byref(x)
+    wsb = int(L.vc_repair_workspace_size(ctypes.byref(sh)))
+    assert wsb == 256 + 2 * 256 * 8  # amax bits (one 256-byte line) + fp64 energies
+    outs = [P(FAKE)] * 4
+    assert L.vc_repair_prepare(ctypes.byref(sh), None, xb, xb, -1, *outs, P(FAKE), wsb, st) == 2
+    assert L.vc_repair_prepare(ctypes.byref(sh), None, xb, xb, 257, *outs, P(FAKE), wsb, st) == 2
+    assert L.vc_repair_prepare(ctypes.byref(sh), None, xb, None, 2, *outs, P(FAKE), wsb, st) == 1
+    assert L.vc_repair_prepare(ctypes.byref(sh), None, xb, xb, 2, P(FAKE), None, P(FAKE), P(FAKE), P(FAKE),
+                               wsb, st) == 1
+    assert L.vc_repair_prepare(ctypes.byref(sh), None, xb, xb, 2, *outs, P(FAKE + 16), wsb, st) == 3
+    assert L.vc_repair_prepare(ctypes.byref(sh), None, xb, xb, 2, P(FAKE + 2), *outs[1:], P(FAKE), wsb, st) == 3
+    assert L.vc_repair_prepare(ctypes.byref(sh), None, xb, xb, 2, *outs, P(FAKE), wsb - 1, st) == 5
+    pp = m.vc_prep_params(m.VC_PREP_K_CENTER, None, None, None, 0)  # centring without its workspace
+    assert L.vc_repair_prepare(ctypes.byref(sh), ctypes.byref(pp), xb, xb, 2, *outs, P(FAKE), wsb, st) == 1
+    # zero rows: validated, nothing enqueued, outputs may be NULL
+    assert L.vc_repair_prepare(ctypes.byref(sh), None, xb, xb, 0, None, None, None, None, None, 0, st) == 0
 
 
 def test_expcast_validation(vc):
