@@ -183,6 +183,39 @@ def cpu_baseline(w, q, k, v, target_s=12.0):
     }
 
 
+def repair_measurement(vc, w, q, k, v, flops, rho=0.005, n=3):
+    """Open-VC's V residual repair on the same inputs, plain path: time of
+    vc_repair_prepare for R = ceil(rho S) rows per head, and of vc_attn_fwd
+    without and with the repair tiles (HIP events, mean of n launches)."""
+    import torch
+
+    qz = vc.vc_quantize(q, k, v, sm_scale=w.sm_scale)
+    R = vc.repair_count(w.S, rho)
+    ws = torch.empty(vc.vc_repair_workspace_size(w.B, w.H, w.S, w.D), dtype=torch.uint8, device=q.device)
+    rp = vc.vc_repair_prepare(k, v, R, workspace=ws)
+    o = torch.empty_like(q)
+    args = (qz["q8"], qz["q_scale"], qz["k8"], qz["k_scale"], qz["v8"], qz["v_scale"], None)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    t_prep = timed(lambda: vc.vc_repair_prepare(k, v, R, workspace=ws, out=rp))
+    t_plain = timed(lambda: vc.vc_attn_fwd(*args, S=w.S, out=o))
+    t_rep = timed(lambda: vc.vc_attn_fwd(*args, S=w.S, out=o, repair=rp))
+    del qz, rp, ws, o
+    return {"rho": rho, "rows_per_head": R, "prepare_ms": round(t_prep, 3), "attn_plain_ms": round(t_plain, 3),
+            "attn_with_repair_ms": round(t_rep, 3),
+            "tflops_with_repair": round(flops / (t_rep * 1e-3) / 1e12, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -191,6 +224,7 @@ def main():
     ap.add_argument("--workload", default="wan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--no-repair", action="store_true", help="skip the Open-VC repair-row measurement")
     ap.add_argument("--traffic-job", action="store_true",
                     help="one attention launch + calibration copy, for rocprofv3 --pmc runs")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON", "COMMAND"),
@@ -301,6 +335,11 @@ def main():
         except vc.VcError as ex:
             log(f"bf16 baseline unavailable: {ex}")
 
+    repair = None
+    if not args.no_repair:
+        repair = repair_measurement(vc, w, q, k, v, flops)
+        log(f"repair rows: {repair}")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
@@ -331,6 +370,7 @@ def main():
         "path_tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
         "roofline": roof,
         "bf16_baseline": bf16,
+        "open_vc_repair": repair,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -159,12 +159,14 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
   const uint8_t* vb = v8 + (int64_t)bh * D * S_pad;  // packed: tile t at + t * 128 * D
   const float* ksb = k_scale + (int64_t)bh * nblk;
   // repair tile r is visit nblk + r, and tile_at(i) = i past the regular
-  // visits, so the repair bases are shifted down by nblk tiles (integer
-  // arithmetic: the shifted address itself is never read) and a visit's
-  // source is base(i) + tile_at(i) * TB either way
+  // visits, so the repair bases of the copies are shifted down by nblk tiles
+  // (integer arithmetic: the shifted address itself is never read) and a
+  // visit's source is base(i) + tile_at(i) * TB either way
   const uint8_t* rkb = (const uint8_t*)((uintptr_t)(rk8 + (int64_t)bh * nrb * TB) - (uintptr_t)nblk * TB);
   const uint8_t* rvb = (const uint8_t*)((uintptr_t)(rv8 + (int64_t)bh * nrb * TB) - (uintptr_t)nblk * TB);
-  const float* rksb = (const float*)((uintptr_t)(rk_scale + (int64_t)bh * nrb) - (uintptr_t)nblk * sizeof(float));
+  // the key scales through plain pointers into the arguments, which keeps
+  // their read a scalar load
+  const float* rksb = rk_scale + (int64_t)bh * nrb;
   // E8M0 block scale of the query tile (Q's codes carry 8 sm_scale log2 e)
   const int sq = __builtin_amdgcn_readfirstlane(e8m0_of_pow2(q_scale[(int64_t)bh * nblk + qt]));
 
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
   auto repair_visit = [&](int i) { return !VS && i >= nblk; };
   auto ksrc = [&](int i) { return (repair_visit(i) ? rkb : kb) + (int64_t)tile_at(i) * TB; };
   auto vsrc = [&](int i) { return (repair_visit(i) ? rvb : vb) + (int64_t)tile_at(i) * TB; };
-  auto kscale = [&](int i) { return (repair_visit(i) ? rksb : ksb)[tile_at(i)]; };
+  auto kscale = [&](int i) { return repair_visit(i) ? rksb[i - nblk] : ksb[tile_at(i)]; };
 
   const unsigned loff = (unsigned)l * 16u;
   // copies of half B, wave wq: 1 KB blocks 4r + wq of a tile; with V-Smooth
@@ -341,9 +343,11 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
     if constexpr (PV) {
       const int i = j - 1;
       const int slot = i & 7;
+      // repair rows: numerator only (a scalar 0 / 1 factor: rr * 1 is exact)
+      const float keep = repair_visit(i) ? 0.0f : 1.0f;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        if (!repair_visit(i)) Lq[s] += rr[s];  // repair rows: numerator only
+        Lq[s] = __builtin_fmaf(rr[s], keep, Lq[s]);
         if (VS) {
           if (slot == 2 * g) rb[s][0] = rr[s];
           if (slot == 2 * g + 1) rb[s][1] = rr[s];
@@ -504,7 +508,7 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
   // steady state, rolled: stages picked at run time (j mod 3)
   {
     int ck = 1, cv = 0;
-    for (int j = 1; j < n - 1; ++j) {
+    auto steady = [&](int j, auto mask_tag) {
       uint8_t* const Kc = ck == 0 ? kst0 : (ck == 1 ? kst1 : kst2);
       uint8_t* const Vc = cv == 0 ? vst0 : (cv == 1 ? vst1 : vst2);
       mphase(j, Kc, Vc, std::true_type{}, std::true_type{}, std::true_type{});
@@ -515,7 +519,7 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
       // running max above then covered its pad keys, harmless because
       // vc_quantize makes them copies of the last key; their codes are
       // cleared here so that the row sum counts only the valid keys
-      if (!VS && j == tail_visit) {
+      if (decltype(mask_tag)::value && j == tail_visit) {
         const int lim = S - (nblk - 1) * kBlk;
 #pragma unroll
         for (int t8 = 0; t8 < 8; ++t8) {
@@ -528,6 +532,13 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
       phase_sync();
       ck = ck == 2 ? 0 : ck + 1;
       cv = cv == 2 ? 0 : cv + 1;
+    };
+    // the loop with that check only where it can matter, so the common loop
+    // carries no test
+    if (!VS && tail_visit > 0 && tail_visit < n - 1) {
+      for (int j = 1; j < n - 1; ++j) steady(j, std::true_type{});
+    } else {
+      for (int j = 1; j < n - 1; ++j) steady(j, std::false_type{});
     }
   }
   // j = n - 1 (may be the ragged tile); stages chosen at run time
