@@ -83,6 +83,15 @@ def lib():
                                             P, P, P]
         L.vco_repair_select.argtypes = [P, i64, i32, i32, i32, P, P]
         L.vco_repair_rows.argtypes = [P, i64, i32, i32, P, i32, P]
+        L.vco_e2m1_decode.argtypes = [ctypes.c_uint8]
+        L.vco_e2m1_decode.restype = ctypes.c_double
+        L.vco_e2m1_encode.argtypes = [f32]
+        L.vco_e2m1_encode.restype = ctypes.c_uint8
+        L.vco_mx_block_exp.argtypes = [f32]
+        L.vco_mx_block_exp.restype = ctypes.c_int
+        L.vco_mxfp4_rows.argtypes = [P, i32, i32, f32, P, P]
+        L.vco_mxfp4_cols.argtypes = [P, i32, i32, P, P]
+        L.vco_attn4_emulate_rows.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, P, i32, P, P, P]
         _lib = L
     return _lib
 
@@ -419,5 +428,109 @@ def pipeline_head(q, k, v, b, h, *, vsmooth, nclust=64, iters=4, seed=0, sm_scal
         out.update(repair_idx=idx, repair_energy=energy, repair_k_codes=rk, repair_k_scale=rks,
                    repair_v_codes=rv)
     of, ob, st = attn_emulate_rows(qc, qs, kc, ks, vc, vs, mu, S, 0.125, rows, window, flags, repair)
+    out.update(out_f32=of, out_bf16=ob, stats=st, rows=rows)
+    return out
+
+
+# --------------------------------------------------------------------------- #
+# 4-bit path (MXFP4: E2M1 elements, one power-of-two scale per 32)
+# --------------------------------------------------------------------------- #
+
+def e2m1_decode(codes) -> np.ndarray:
+    """Values of E2M1 codes (low 4 bits of each entry)."""
+    table = np.array([lib().vco_e2m1_decode(c) for c in range(16)], np.float64)
+    return table[np.asarray(codes).astype(np.int64) & 15]
+
+
+def e2m1_encode(x) -> np.ndarray:
+    L = lib()
+    x = np.asarray(x, np.float32)
+    return np.array([L.vco_e2m1_encode(float(v)) for v in x.ravel()], np.uint8).reshape(x.shape)
+
+
+def mx_block_exp(amax: float) -> int:
+    return int(lib().vco_mx_block_exp(float(amax)))
+
+
+def q4_prefactor(sm_scale: float) -> float:
+    """fl32(sm_scale * fl32(log2 e)): Q's factor on the 4-bit path, so the
+    matrix cores emit scores in log2 units."""
+    return float(np.float32(np.float32(sm_scale) * np.float32(1.4426950408889634)))
+
+
+def mxfp4_rows(y: np.ndarray, pre: float = 1.0):
+    """fp32 rows [S, D] (times pre) in blocks of 32 channels.  Returns codes
+    uint8 [S_pad, D] (one code per byte; rows >= S zero) and exponents int32
+    [S_pad, D/32] (rows >= S zero)."""
+    y = np.ascontiguousarray(y, np.float32)
+    S, D = y.shape
+    S_pad = (S + 127) // 128 * 128
+    codes = np.zeros((S_pad, D), np.uint8)
+    exps = np.zeros((S_pad, D // 32), np.int32)
+    lib().vco_mxfp4_rows(_p(y), S, D, float(pre), _p(codes), _p(exps))
+    return codes, exps
+
+
+def mxfp4_cols(x: np.ndarray):
+    """fp32 [S, D] (rows = keys) in blocks of 32 keys per channel.  Returns
+    codes uint8 [D, S_pad] and exponents int32 [D, S_pad/32]."""
+    x = np.ascontiguousarray(x, np.float32)
+    S, D = x.shape
+    S_pad = (S + 127) // 128 * 128
+    codes = np.zeros((D, S_pad), np.uint8)
+    exps = np.zeros((D, S_pad // 32), np.int32)
+    lib().vco_mxfp4_cols(_p(x), S, D, _p(codes), _p(exps))
+    return codes, exps
+
+
+def attn4_emulate_rows(q_codes, q_exps, k_codes, k_exps, v_codes_t, v_exps, mu, S, rows, window=2, flags=0):
+    """One head of the 4-bit path (see vco_attn4_emulate_rows).  mu: fp32
+    [nblk, D] block means or None.  Returns (out_f32, out_bf16, stats)."""
+    arrs = [np.ascontiguousarray(a, t) for a, t in ((q_codes, np.uint8), (q_exps, np.int32), (k_codes, np.uint8),
+                                                  (k_exps, np.int32), (v_codes_t, np.uint8), (v_exps, np.int32))]
+    D = arrs[0].shape[1]
+    rows = np.ascontiguousarray(rows, np.int32)
+    n = rows.size
+    of = np.zeros((n, D), np.float32)
+    ob = np.zeros((n, D), np.uint16)
+    st = np.zeros((n, 2), np.float64)
+    mup = None
+    if mu is not None:
+        mu = np.ascontiguousarray(mu, np.float32)
+        mup = _p(mu)
+    lib().vco_attn4_emulate_rows(*[_p(a) for a in arrs], mup, S, D, window, flags, _p(rows), n, _p(of), _p(ob),
+                                 _p(st))
+    return of, ob, st
+
+
+def pipeline4_head(q, k, v, b, h, *, vsmooth, nclust=64, iters=4, seed=0, sm_scale=None, rows=None, window=2,
+                   flags=0):
+    """The 4-bit pipeline for one head from bf16 inputs [B,S,H,D]: Q (times
+    q4_prefactor) and K in MXFP4 row blocks; V, or with V-Smooth the residual
+    R = fl32(V' - mu) of the grouping (same k-means, pi and block means as the
+    8-bit path), in MXFP4 key blocks; then the emulation of the listed rows."""
+    B, S, H, D = q.shape
+    sm_scale = 1.0 / np.sqrt(D) if sm_scale is None else sm_scale
+    rows = np.arange(S) if rows is None else np.asarray(rows)
+    qc, qe = mxfp4_rows(bf16_bits_to_f32(_head(q, b, h)), q4_prefactor(sm_scale))
+    out = dict(q_codes=qc, q_exps=qe)
+    kh, vh = _head(k, b, h), _head(v, b, h)
+    mu = None
+    if vsmooth:
+        labels, cent = kmeans_head(vh, nclust, iters, seed, b, h, H)
+        perm = argsort_labels(labels, nclust)
+        g = smooth_apply_head(kh, vh, perm)
+        mu = bf16_bits_to_f32(g["mu_bf16"]).astype(np.float32)
+        vp = bf16_bits_to_f32(vh[perm]).astype(np.float32)
+        blk = np.arange(S) // 128
+        r = (vp - mu[blk]).astype(np.float32)  # one fp32 subtraction per element
+        kc, ke = mxfp4_rows(bf16_bits_to_f32(kh[perm]))
+        vc, ve = mxfp4_cols(r)
+        out.update(labels=labels, perm=perm, mu=mu, residual=r)
+    else:
+        kc, ke = mxfp4_rows(bf16_bits_to_f32(kh))
+        vc, ve = mxfp4_cols(bf16_bits_to_f32(vh))
+    out.update(k_codes=kc, k_exps=ke, v_codes=vc, v_exps=ve)
+    of, ob, st = attn4_emulate_rows(qc, qe, kc, ke, vc, ve, mu, S, rows, window, flags)
     out.update(out_f32=of, out_bf16=ob, stats=st, rows=rows)
     return out

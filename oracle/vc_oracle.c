@@ -703,3 +703,165 @@ EXPORT void vco_attn_emulate_rows(const uint8_t* q_codes, const float* q_scale, 
     free(order);
   }
 }
+
+/* ------------------------------------------------------------------------ */
+/* 4-bit path: V-Smooth at 4 bits, no ExpCast ([VC] §4.1 "Implementation":  */
+/* 4 bits with V-Smooth alone; [VC] §4.1 "Scope of ExpCast-FP8": P is kept  */
+/* as a microscaled 4-bit format, no affine log-to-code map exists for it). */
+/* The pages' format is NVFP4 (per-16 E4M3 scales); the format here is     */
+/* OCP MXFP4, the one gfx950's matrix cores take: E2M1 elements, one E8M0    */
+/* (power-of-two) scale per 32 elements.                                    */
+/* Readings: the block scale is the smallest 2^e (e >= -127) with           */
+/* amax <= 6 * 2^e (2^0 for a block of zeros), as for the FP8 Q/K blocks;   */
+/* elements are E2M1 round-half-even of x * 2^-e (saturating at 6, never    */
+/* reached with that scale); Q/K blocks are 32 channels of a row (Q first   */
+/* multiplied by fl(sm_scale * log2 e), so scores come out in log2 units);  */
+/* V (or V-Smooth's residual) and P blocks are 32 consecutive keys of a     */
+/* 128-key tile, per channel and per query row; p = fl32(2^fl32(s - M))     */
+/* with the running max M over the true scores, every increase applied;    */
+/* the row sum adds the dequantised P; the block mean is restored per tile  */
+/* as A += r mu ([VC] §3.2 Eq. 6).                                           */
+/* ------------------------------------------------------------------------ */
+
+/* E2M1 (OCP MX): sign, 2 exponent bits (bias 1), 1 mantissa bit. */
+EXPORT double vco_e2m1_decode(uint8_t c) {
+  const int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+  const double mag = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+  return s ? -mag : mag;
+}
+
+/* Nearest E2M1 value, ties to the even code (mantissa bit 0), magnitudes
+ * above 6 saturating to 6; -0 for negative inputs that round to zero. */
+EXPORT uint8_t vco_e2m1_encode(float y) {
+  const double a = fabs((double)y);
+  int best = 0;
+  double bd = a; /* distance to code 0 */
+  for (int c = 1; c < 8; ++c) {
+    const double d = fabs(a - vco_e2m1_decode((uint8_t)c));
+    if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1)) {
+      bd = d;
+      best = c;
+    }
+  }
+  if (a > 6.0) best = 7;
+  return (uint8_t)(best | (signbit(y) ? 8 : 0));
+}
+
+/* Smallest e >= -127 with amax <= 6 * 2^e; 0 for amax == 0. */
+EXPORT int vco_mx_block_exp(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  int e = -127;
+  while ((double)amax > ldexp(6.0, e)) ++e;
+  return e;
+}
+
+/* Rows of y (fp32 [S][D]) times pre, in blocks of 32 channels: codes [S][D]
+ * (one E2M1 code per byte) and exponents [S][D/32]. */
+EXPORT void vco_mxfp4_rows(const float* y, int32_t S, int32_t D, float pre, uint8_t* codes, int32_t* exps) {
+  for (int32_t r = 0; r < S; ++r)
+    for (int32_t b = 0; b < D / 32; ++b) {
+      float amax = 0.0f;
+      for (int32_t c = 32 * b; c < 32 * b + 32; ++c) amax = fmaxf(amax, fabsf(y[(int64_t)r * D + c] * pre));
+      const int e = vco_mx_block_exp(amax);
+      exps[(int64_t)r * (D / 32) + b] = e;
+      for (int32_t c = 32 * b; c < 32 * b + 32; ++c)
+        codes[(int64_t)r * D + c] = vco_e2m1_encode(ldexpf(y[(int64_t)r * D + c] * pre, -e));
+    }
+}
+
+/* Columns of x (fp32 [S][D], rows = keys) in blocks of 32 keys per channel:
+ * codes_t [D][S_pad], exps [D][S_pad/32]; keys >= S are code 0 and do not
+ * enter the block maximum. */
+EXPORT void vco_mxfp4_cols(const float* x, int32_t S, int32_t D, uint8_t* codes_t, int32_t* exps) {
+  const int32_t S_pad = (S + 127) / 128 * 128, nb = S_pad / 32;
+  for (int32_t d = 0; d < D; ++d)
+    for (int32_t b = 0; b < nb; ++b) {
+      float amax = 0.0f;
+      for (int32_t k = 32 * b; k < 32 * b + 32 && k < S; ++k) amax = fmaxf(amax, fabsf(x[(int64_t)k * D + d]));
+      const int e = vco_mx_block_exp(amax);
+      exps[(int64_t)d * nb + b] = e;
+      for (int32_t k = 32 * b; k < 32 * b + 32; ++k)
+        codes_t[(int64_t)d * S_pad + k] = k < S ? vco_e2m1_encode(ldexpf(x[(int64_t)k * D + d], -e)) : 0;
+    }
+}
+
+/*
+ * 4-bit attention, one query row at a time (rows in token order).
+ * q_codes [S_pad][D] / q_exps [S_pad][D/32] (Q carrying fl(sm log2 e)),
+ * k_codes, k_exps likewise, v_codes_t [D][S_pad] / v_exps [D][S_pad/32],
+ * mu [nblk][D] fp32 block means or NULL (plain).  Key blocks in the order
+ * of vco_tile_order.  Out: out_f32 [n][D], out_bf16 [n][D], stats [n][2] =
+ * {rescales, final max} (may be NULL).
+ */
+EXPORT void vco_attn4_emulate_rows(const uint8_t* q_codes, const int32_t* q_exps, const uint8_t* k_codes,
+                                   const int32_t* k_exps, const uint8_t* v_codes_t, const int32_t* v_exps,
+                                   const float* mu, int32_t S, int32_t D, int32_t window, int32_t flags,
+                                   const int32_t* rows, int32_t n, float* out_f32, uint16_t* out_bf16,
+                                   double* stats) {
+  const int32_t nblk = (S + 127) / 128, S_pad = nblk * 128, nb32 = S_pad / 32;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int32_t ri = 0; ri < n; ++ri) {
+    const int32_t i = rows[ri];
+    int32_t* order = (int32_t*)malloc(sizeof(int32_t) * (size_t)nblk);
+    vco_tile_order(i / 128, nblk, window, flags & VCO_SEQUENTIAL, order);
+    double* qd = (double*)malloc(sizeof(double) * (size_t)D);
+    double* A = (double*)calloc((size_t)D, sizeof(double));
+    for (int32_t d = 0; d < D; ++d)
+      qd[d] = ldexp(vco_e2m1_decode(q_codes[(int64_t)i * D + d]), q_exps[(int64_t)i * (D / 32) + d / 32]);
+    float acc[128], p[128];
+    double l = 0.0;
+    float M = -INFINITY;
+    int32_t rescales = 0;
+    for (int32_t oi = 0; oi < nblk; ++oi) {
+      const int32_t t = order[oi], k0 = t * 128, k1 = k0 + 128 < S ? k0 + 128 : S;
+      float mx = -INFINITY;
+      for (int32_t kk = k0; kk < k1; ++kk) {
+        double s = 0.0; /* exact for the operands' few significant bits */
+        for (int32_t d = 0; d < D; ++d)
+          s += qd[d] * ldexp(vco_e2m1_decode(k_codes[(int64_t)kk * D + d]), k_exps[(int64_t)kk * (D / 32) + d / 32]);
+        acc[kk - k0] = (float)s;
+        mx = fmaxf(mx, acc[kk - k0]);
+      }
+      const float Mn = fmaxf(M, mx);
+      if (Mn > M) {
+        if (M != -INFINITY) {
+          const double alpha = exp2((double)M - (double)Mn);
+          for (int32_t d = 0; d < D; ++d) A[d] *= alpha;
+          l *= alpha;
+          rescales += 1;
+        }
+        M = Mn;
+      }
+      for (int32_t kk = k0; kk < k1; ++kk) p[kk - k0] = (float)exp2((double)(acc[kk - k0] - M));
+      double r = 0.0;
+      for (int32_t b0 = k0; b0 < k1; b0 += 32) { /* P's blocks of 32 keys */
+        const int32_t b1 = b0 + 32 < k1 ? b0 + 32 : k1;
+        float amax = 0.0f;
+        for (int32_t kk = b0; kk < b1; ++kk) amax = fmaxf(amax, p[kk - k0]);
+        const int e = vco_mx_block_exp(amax);
+        for (int32_t kk = b0; kk < b1; ++kk) {
+          const double w = ldexp(vco_e2m1_decode(vco_e2m1_encode(ldexpf(p[kk - k0], -e))), e);
+          if (w == 0.0) continue;
+          r += w;
+          for (int32_t d = 0; d < D; ++d)
+            A[d] += w * ldexp(vco_e2m1_decode(v_codes_t[(int64_t)d * S_pad + kk]), v_exps[(int64_t)d * nb32 + kk / 32]);
+        }
+      }
+      if (mu)
+        for (int32_t d = 0; d < D; ++d) A[d] += r * (double)mu[(int64_t)t * D + d];
+      l += r;
+    }
+    for (int32_t d = 0; d < D; ++d) {
+      const float o = (float)(A[d] / l);
+      out_f32[(int64_t)ri * D + d] = o;
+      out_bf16[(int64_t)ri * D + d] = f32_to_bf16_rne(o);
+    }
+    if (stats) {
+      stats[2 * ri] = rescales;
+      stats[2 * ri + 1] = M;
+    }
+    free(A);
+    free(qd);
+    free(order);
+  }
+}
