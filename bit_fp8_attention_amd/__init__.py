@@ -9,8 +9,8 @@ no GPU is present, calls fail loudly.
 
 Entry points (same names as the C ABI): vc_abi_version, vc_status_str,
 vc_quantize, vc_smooth_group_workspace_size, vc_smooth_group,
-vc_repair_workspace_size, vc_repair_prepare, vc_attn_fwd, vc_pack_v_bf16,
-vc_attn_fwd_bf16, vc_expcast_codes; and vsmooth_schedule, the host-side rule
+vc_repair_workspace_size, vc_repair_prepare, vc_attn_fwd, vc_quantize4,
+vc_attn_fwd4, vc_pack_v_bf16, vc_attn_fwd_bf16, vc_expcast_codes; and vsmooth_schedule, the host-side rule
 for which denoising steps group, reuse or run plain, and repair_count, the
 number of repair rows for a fraction rho of the tokens.
 """
@@ -101,6 +101,10 @@ def lib():
         L.vc_repair_prepare.restype = i32
         L.vc_attn_fwd.argtypes = [P] * 12
         L.vc_attn_fwd.restype = i32
+        L.vc_quantize4.argtypes = [P, f32] + [P] * 12
+        L.vc_quantize4.restype = i32
+        L.vc_attn_fwd4.argtypes = [P] * 11
+        L.vc_attn_fwd4.restype = i32
         L.vc_pack_v_bf16.argtypes = [P] * 4
         L.vc_pack_v_bf16.restype = i32
         L.vc_attn_fwd_bf16.argtypes = [P] * 7
@@ -361,6 +365,55 @@ def vc_repair_prepare(k, v, rows: int, *, prep=None, workspace=None, out=None):
                                  _stream())
     _check(st, "vc_repair_prepare")
     return o
+
+
+# --------------------------------------------------------------------------- #
+# the 4-bit path (MXFP4)
+# --------------------------------------------------------------------------- #
+
+def vc_quantize4(q=None, k=None, v=None, *, sm_scale: float = 0.0, perm=None, mu_bf16=None, out=None):
+    """MXFP4 operands (see vc_attn.h).  q, k, v: bf16 [B,S,H,D] (q or k/v may
+    be None); perm (int32 [B,H,S]) and mu_bf16 ([B,H,nblk,D]) from
+    vc_smooth_group for V-Smooth.  Returns dict with q4, q4_scale, k4,
+    k4_scale, v4, v4_scale."""
+    ref = next(x for x in (q, k, v) if x is not None)
+    sh = _shape_of(ref)
+    B, H, S, D = sh.B, sh.H, sh.S, sh.D
+    nb = nblk_of(S)
+    dev = ref.device
+    o = dict(out or {})
+    if q is not None:
+        o.setdefault("q4", torch.empty((B, H, nb * 128, D // 2), dtype=torch.uint8, device=dev))
+        o.setdefault("q4_scale", torch.empty((B, H, nb * 128, D // 32), dtype=torch.uint8, device=dev))
+    if k is not None:
+        o.setdefault("k4", torch.empty((B, H, nb, 128, D // 2), dtype=torch.uint8, device=dev))
+        o.setdefault("k4_scale", torch.empty((B, H, nb, 512), dtype=torch.uint8, device=dev))
+        o.setdefault("v4", torch.empty((B, H, nb, D, 64), dtype=torch.uint8, device=dev))
+        o.setdefault("v4_scale", torch.empty((B, H, nb, 512), dtype=torch.uint8, device=dev))
+    qd, kd, vd = _bshd(q), _bshd(k), _bshd(v)
+    st = lib().vc_quantize4(ctypes.byref(sh), float(sm_scale), ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd),
+                            _ptr(perm), _ptr(mu_bf16), _ptr(o.get("q4")), _ptr(o.get("q4_scale")),
+                            _ptr(o.get("k4")), _ptr(o.get("k4_scale")), _ptr(o.get("v4")), _ptr(o.get("v4_scale")),
+                            _stream())
+    _check(st, "vc_quantize4")
+    return o
+
+
+def vc_attn_fwd4(q4, q4_scale, k4, k4_scale, v4, v4_scale, mu_bf16=None, *, S: int, out=None, window: int = 2,
+                 sequential: bool = False):
+    """4-bit attention on vc_quantize4's operands.  Returns bf16 [B,S,H,D]."""
+    B, H, S_pad, D2 = q4.shape
+    D = 2 * D2
+    assert S_pad == nblk_of(S) * 128
+    sh = vc_shape(B, H, S, D)
+    if out is None:
+        out = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=q4.device)
+    p = vc_attn_params(0.0, window, VC_ATTN_SEQUENTIAL if sequential else 0)
+    od = _bshd_out(out)
+    st = lib().vc_attn_fwd4(ctypes.byref(sh), ctypes.byref(p), _ptr(q4), _ptr(q4_scale), _ptr(k4), _ptr(k4_scale),
+                            _ptr(v4), _ptr(v4_scale), _ptr(mu_bf16), ctypes.byref(od), _stream())
+    _check(st, "vc_attn_fwd4")
+    return out
 
 
 def vc_pack_v_bf16(v, *, out=None):

@@ -12,7 +12,7 @@ OUT = os.path.join(HERE, "libvcattn.so")
 BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["vc_capi.hip", "vc_quantize.hip", "vc_group.hip", "vc_repair.hip", "vc_attn_fp8.hip", "vc_attn_bf16.hip"]
+SOURCES = ["vc_capi.hip", "vc_quantize.hip", "vc_group.hip", "vc_repair.hip", "vc_attn_fp8.hip", "vc_attn_mxfp4.hip", "vc_attn_bf16.hip"]
 
 # -ffp-contract=off: every fused multiply-add in the kernels is an explicit
 # __builtin_fmaf, so rounding matches the stated arithmetic.  Packed fp32 ops
@@ -27,6 +27,7 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=o
 EXTRA = {
     "vc_attn_fp8.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
     "vc_attn_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+    "vc_attn_mxfp4.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
 }
 
 

@@ -220,6 +220,57 @@ __attribute__((visibility("default"))) int32_t vc_repair_prepare(const vc_shape*
                                               workspace, st));
 }
 
+__attribute__((visibility("default"))) int32_t vc_quantize4(const vc_shape* sh, float sm_scale, const vc_bshd* q,
+                                                             const vc_bshd* k, const vc_bshd* v,
+                                                             const int32_t* perm, const uint16_t* mu_bf16,
+                                                             uint8_t* q4, uint8_t* q4_scale, uint8_t* k4,
+                                                             uint8_t* k4_scale, uint8_t* v4, uint8_t* v4_scale,
+                                                             void* stream) {
+  int32_t e = check_shape(sh);
+  if (e) return e;
+  if (!(sm_scale >= 0.0f) || isinf(sm_scale)) return VC_ERR_UNSUPPORTED;
+  const bool dq = q && q->ptr, dk = k && k->ptr, dv = v && v->ptr;
+  if (dk != dv) return VC_ERR_NULL;             // K and V go together
+  if ((perm == nullptr) != (mu_bf16 == nullptr)) return VC_ERR_NULL;  // V-Smooth: both
+  if (perm && !dk) return VC_ERR_NULL;
+  if (dq) {
+    if ((e = check_bshd(q))) return e;
+    if (!q4 || !q4_scale) return VC_ERR_NULL;
+    if (!aligned16(q4)) return VC_ERR_ALIGN;
+  }
+  if (dk) {
+    if ((e = check_bshd(k)) || (e = check_bshd(v))) return e;
+    if (!k4 || !k4_scale || !v4 || !v4_scale) return VC_ERR_NULL;
+    if (!aligned16(k4) || !aligned16(v4) || (((uintptr_t)k4_scale | (uintptr_t)v4_scale) & 7u)) return VC_ERR_ALIGN;
+    if (((uintptr_t)perm & 3u) || ((uintptr_t)mu_bf16 & 15u)) return VC_ERR_ALIGN;
+  }
+  const float sm = sm_scale == 0.0f ? 1.0f / sqrtf((float)sh->D) : sm_scale;
+  const float pre = sm * 1.44269504088896340736f;  // fl(sm_scale * fl(log2 e)): scores in log2 units
+  const Bshd none{nullptr, 0, 0, 0};
+  return hip_status(vc::launch_quant4(*sh, pre, dq ? as_bshd(q) : none, dk ? as_bshd(k) : none,
+                                      dv ? as_bshd(v) : none, perm, mu_bf16, q4, q4_scale, k4, k4_scale, v4,
+                                      v4_scale, (hipStream_t)stream));
+}
+
+__attribute__((visibility("default"))) int32_t vc_attn_fwd4(const vc_shape* sh, const vc_attn_params* p,
+                                                             const uint8_t* q4, const uint8_t* q4_scale,
+                                                             const uint8_t* k4, const uint8_t* k4_scale,
+                                                             const uint8_t* v4, const uint8_t* v4_scale,
+                                                             const uint16_t* mu_bf16, const vc_bshd_out* o,
+                                                             void* stream) {
+  int32_t e = check_shape(sh);
+  if (e) return e;
+  if (!p || !q4 || !q4_scale || !k4 || !k4_scale || !v4 || !v4_scale) return VC_ERR_NULL;
+  if ((e = check_out(o))) return e;
+  if (!aligned16(q4) || !aligned16(k4) || !aligned16(v4)) return VC_ERR_ALIGN;
+  if ((((uintptr_t)k4_scale | (uintptr_t)v4_scale) & 7u) || ((uintptr_t)mu_bf16 & 15u)) return VC_ERR_ALIGN;
+  if (p->window < 0 || (p->flags & ~VC_ATTN_SEQUENTIAL)) return VC_ERR_UNSUPPORTED;
+  if (!(p->sm_scale >= 0.0f) || isinf(p->sm_scale)) return VC_ERR_UNSUPPORTED;
+  BshdOut ob{(uint16_t*)o->ptr, o->sB, o->sS, o->sH};
+  return hip_status(vc::launch_attn4(*sh, p->window, p->flags, q4, q4_scale, k4, k4_scale, v4, v4_scale, mu_bf16,
+                                     ob, (hipStream_t)stream));
+}
+
 __attribute__((visibility("default"))) int32_t vc_pack_v_bf16(const vc_shape* sh, const vc_bshd* v, uint16_t* vt,
                                                                void* stream) {
   int32_t e = check_shape(sh);

@@ -69,6 +69,15 @@ hipError_t launch_attn_fp8(const vc_shape& sh, int window, uint32_t flags, const
                            const uint8_t* k8, const float* k_scale, const uint8_t* v8, const float* v_scale,
                            const uint32_t* mu_split, RepairTiles rp, BshdOut o, hipStream_t st);
 
+// vc_attn_mxfp4.hip (the 4-bit path)
+// Q rows (times pre) into q4 / q4s; K and V (through perm, minus mu_bf16, when given) into the packed tiles
+hipError_t launch_quant4(const vc_shape& sh, float pre, Bshd q, Bshd k, Bshd v, const int32_t* perm,
+                         const uint16_t* mu, uint8_t* q4, uint8_t* q4s, uint8_t* k4, uint8_t* k4s, uint8_t* v4,
+                         uint8_t* v4s, hipStream_t st);
+hipError_t launch_attn4(const vc_shape& sh, int window, uint32_t flags, const uint8_t* q4, const uint8_t* q4s,
+                        const uint8_t* k4, const uint8_t* k4s, const uint8_t* v4, const uint8_t* v4s,
+                        const uint16_t* mu, BshdOut o, hipStream_t st);
+
 // vc_attn_bf16.hip
 hipError_t launch_attn_bf16(const vc_shape& sh, float sm_scale, int window, uint32_t flags, Bshd q, Bshd k,
                             const uint16_t* vt, BshdOut o, hipStream_t st);

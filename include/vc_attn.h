@@ -334,6 +334,58 @@ int32_t vc_attn_fwd(const vc_shape* shape, const vc_attn_params* p, const uint8_
 /* ----------------------------------------------------------------------- */
 
 /*
+ * The 4-bit path: V-Smooth at 4 bits without ExpCast ([VC] §4.1
+ * "Implementation" -- 4 bits run V-Smooth alone -- and "Scope of ExpCast-FP8":
+ * P is kept in a microscaled 4-bit format, for which no affine log-to-code
+ * map exists).  The pages' format is NVFP4; gfx950's matrix cores take OCP
+ * MXFP4: E2M1 elements (0, 0.5, 1, 1.5, 2, 3, 4, 6 and negatives) with one
+ * E8M0 scale byte (2^(byte - 127)) per 32 elements.  A block's scale is the
+ * smallest 2^e (e >= -127) with amax <= 6 * 2^e (2^0 for zeros); elements
+ * are E2M1, round half to even, of x / 2^e.
+ *
+ * vc_quantize4 -- Q, K, V into MXFP4 (any of q or k/v may be NULL to skip;
+ * k and v go together).  Q is multiplied first by fl32(sm_scale * fl32(log2
+ * e)) (sm_scale 0 selects 1/sqrt(D)), so scores come out in log2 units.
+ * With perm and mu_bf16 (V-Smooth, from vc_smooth_group) K and V are taken
+ * through perm and V becomes the residual fl32(V' - mu_j) of [VC] §3.2
+ * Eq. 4; without them (both NULL) the plain 4-bit path.
+ * Layouts, per (b, h), nblk = ceil(S / 128), S_pad = 128 nblk:
+ *   q4       uint8 [S_pad][D/2]: byte c = channels 2c (low nibble), 2c + 1;
+ *   q4_scale uint8 [S_pad][D/32]: one E8M0 byte per 32 channels of a row;
+ *   k4       per tile t, 64 D bytes: tile row 16 a + 4 g + v (a < 8, g < 4,
+ *            v < 4), D/2 bytes as q4, holds key 128 t + 32 g + 4 a + v;
+ *   k4_scale per tile 512 bytes: byte (16 c + (r & 15)) * 8 + (r >> 4) is
+ *            the scale of tile row r, channels [32 c, 32 c + 32) (127 for
+ *            c >= D/32);
+ *   v4       per tile, D channel rows of 64 bytes: byte c of row d holds
+ *            keys 128 t + 2c (low nibble) and 128 t + 2c + 1;
+ *   v4_scale per tile 512 bytes: byte (16 g + (d & 15)) * 8 + (d >> 4) is
+ *            the scale of channel d, keys [128 t + 32 g, 128 t + 32 g + 32)
+ *            (127 for d >= D);
+ * rows / keys >= S are zero codes and do not enter any block maximum.
+ * q4, k4, v4 16-byte aligned; k4_scale, v4_scale 8-byte; mu_bf16 16-byte.
+ */
+int32_t vc_quantize4(const vc_shape* shape, float sm_scale, const vc_bshd* q, const vc_bshd* k, const vc_bshd* v,
+                     const int32_t* perm, const uint16_t* mu_bf16, uint8_t* q4, uint8_t* q4_scale, uint8_t* k4,
+                     uint8_t* k4_scale, uint8_t* v4, uint8_t* v4_scale, void* stream);
+
+/*
+ * vc_attn_fwd4 -- non-causal 4-bit attention on vc_quantize4's operands,
+ * keys in the order of vc_attn_fwd.  Per query row and key tile:
+ * s = Q4 . K4 (block-scaled matrix cores, log2 units); M' = max(M, max s),
+ * the numerator and denominator rescaled by 2^(M - M') on every increase;
+ * p = 2^(s - M') (fp32); P in MXFP4 blocks of the tile's 32 consecutive
+ * keys; l += sum of the dequantised P; A += P . V4 (block-scaled), and with
+ * mu_bf16 (V-Smooth) A += r * mu_t, r the tile's sum of P.  Output
+ * bf16(A / l) to `o`.  p->sm_scale is validated only (Q carries it).
+ */
+int32_t vc_attn_fwd4(const vc_shape* shape, const vc_attn_params* p, const uint8_t* q4, const uint8_t* q4_scale,
+                     const uint8_t* k4, const uint8_t* k4_scale, const uint8_t* v4, const uint8_t* v4_scale,
+                     const uint16_t* mu_bf16, const vc_bshd_out* o, void* stream);
+
+/* ----------------------------------------------------------------------- */
+
+/*
  * vc_pack_v_bf16 -- key-contiguous, tile-major copy of V for the BF16
  * baseline (B*H*S_pad*D bf16 values, keys >= S zero): per (b, h), tile j and
  * half hf in {0, 1}, element ((b*H + h)*nblk + j)*128*D + hf*64*D + d*64

@@ -30,7 +30,7 @@ def test_header_declares_the_calls():
     names = _declared()
     for n in ["vc_abi_version", "vc_status_str", "vc_quantize", "vc_smooth_group_workspace_size",
               "vc_smooth_group", "vc_repair_workspace_size", "vc_repair_prepare", "vc_attn_fwd",
-              "vc_pack_v_bf16", "vc_attn_fwd_bf16", "vc_expcast_codes"]:
+              "vc_quantize4", "vc_attn_fwd4", "vc_pack_v_bf16", "vc_attn_fwd_bf16", "vc_expcast_codes"]:
         assert n in names
 
 

@@ -1,0 +1,143 @@
+"""GPU parity of the 4-bit path (MXFP4; [VC] §4.1: 4-bit V-Smooth without
+ExpCast) against the oracle, through the C ABI.
+
+Bit-exact: vc_quantize4's codes and E8M0 scales for Q (times fl(sm log2 e)),
+K and V, plain and with V-Smooth (K' and the residual V' - mu from the
+grouping), unpacked with the header's layout formulas.  Attention output:
+relative L2 <= 1e-2 against the oracle's 4-bit emulation (differences come
+only from the matrix cores' fp32 accumulation order and v_exp_f32, which can
+move a probability across an E2M1 rounding boundary).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import vcsynth
+
+pytestmark = pytest.mark.gpu
+
+REL_L2_TOL = 1e-2
+
+
+@pytest.fixture(scope="module")
+def vc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_fp8_attention_amd as m
+    m.lib()
+    return m
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def nibbles(b):
+    """uint8 [..., n] -> codes [..., 2n] (low nibble first)."""
+    b = np.asarray(b, np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), np.uint8)
+    out[..., 0::2] = b & 15
+    out[..., 1::2] = b >> 4
+    return out
+
+
+def k4_row_of_key(k):
+    k = np.asarray(k)
+    return 16 * ((k & 31) >> 2) + 4 * (k >> 5) + (k & 3)
+
+
+def unpack_k4(k4, k4s, D):
+    """Per head: k4 [nblk, 128, D/2], k4s [nblk, 512] -> codes [S_pad, D],
+    exponents [S_pad, D/32] in key order."""
+    nblk = k4.shape[0]
+    keys = np.arange(128)
+    rows = k4_row_of_key(keys)
+    codes = nibbles(k4)[:, rows, :].reshape(nblk * 128, D)
+    exps = np.zeros((nblk * 128, D // 32), np.int32)
+    for c in range(D // 32):
+        idx = (16 * c + (rows & 15)) * 8 + (rows >> 4)
+        exps[:, c] = (k4s[:, idx].astype(np.int32) - 127).reshape(-1)
+    return codes, exps
+
+
+def unpack_v4(v4, v4s, D):
+    """Per head: v4 [nblk, D, 64], v4s [nblk, 512] -> codes_t [D, S_pad],
+    exponents [D, S_pad/32]."""
+    nblk = v4.shape[0]
+    codes = np.moveaxis(nibbles(v4), 0, 1).reshape(D, nblk * 128)
+    d = np.arange(D)
+    exps = np.zeros((D, nblk * 4), np.int32)
+    for g in range(4):
+        idx = (16 * g + (d & 15)) * 8 + (d >> 4)
+        exps[:, g::4] = (v4s[:, idx].astype(np.int32) - 127).T
+    return codes, exps
+
+
+def _f32(x_bits):
+    return oracle.bf16_bits_to_f32(x_bits).astype(np.float32)
+
+
+@pytest.mark.parametrize("S,D,vsmooth", [(1000, 128, False), (300, 64, False), (129, 128, False), (1000, 128, True),
+                                         (700, 64, True)])
+def test_quantize4_bitexact(vc, S, D, vsmooth):
+    print(f"case quantize4 S={S} D={D} vsmooth={vsmooth}", flush=True)
+    B, H = 1, 2
+    q, k, v = vcsynth.random_qkv(B, S, H, D, seed=S + D, v_kind="t3")
+    sm = float(np.float32(1 / math.sqrt(D)))
+    kw = {}
+    if vsmooth:
+        g = vc.vc_smooth_group(k.cuda(), v.cuda(), 16, 3, 5)
+        kw = dict(perm=g["perm"], mu_bf16=g["mu_bf16"])
+    out = vc.vc_quantize4(q.cuda(), k.cuda(), v.cuda(), sm_scale=sm, **kw)
+    torch.cuda.synchronize()
+    qb, kb, vb = (vcsynth.bf16_bits(x) for x in (q, k, v))
+    for h in range(H):
+        qc, qe = oracle.mxfp4_rows(_f32(qb[0, :, h]), oracle.q4_prefactor(sm))
+        assert (nibbles(_np(out["q4"])[0, h]) == qc).all(), h
+        assert ((_np(out["q4_scale"])[0, h].astype(np.int32) - 127) == qe).all(), h
+        kh, vh = kb[0, :, h], vb[0, :, h]
+        if vsmooth:
+            perm = _np(kw["perm"])[0, h]
+            mu = oracle.bf16_bits_to_f32(_np(kw["mu_bf16"])[0, h].view(np.uint16)).astype(np.float32)
+            kc, ke = oracle.mxfp4_rows(_f32(kh[perm]))
+            vc_, ve = oracle.mxfp4_cols((_f32(vh[perm]) - mu[np.arange(S) // 128]).astype(np.float32))
+        else:
+            kc, ke = oracle.mxfp4_rows(_f32(kh))
+            vc_, ve = oracle.mxfp4_cols(_f32(vh))
+        gk, gke = unpack_k4(_np(out["k4"])[0, h], _np(out["k4_scale"])[0, h], D)
+        gv, gve = unpack_v4(_np(out["v4"])[0, h], _np(out["v4_scale"])[0, h], D)
+        assert (gk == kc).all() and (gke == ke).all(), ("k", h)
+        assert (gv == vc_).all() and (gve == ve).all(), ("v", h)
+
+
+@pytest.mark.parametrize("S,D,vsmooth,seq", [(1000, 128, False, False), (300, 64, False, True), (1024, 128, False, False),
+                                             (1000, 128, True, False), (700, 64, True, False), (100, 128, False, False)])
+def test_attn4_parity(vc, S, D, vsmooth, seq):
+    print(f"case attn4 S={S} D={D} vsmooth={vsmooth} seq={seq}", flush=True)
+    B, H = 1, 2
+    q, k, v = vcsynth.random_qkv(B, S, H, D, seed=7 * S + D, v_kind="t3")
+    q = (q.float() * 2).to(torch.bfloat16)  # sharper rows
+    sm = float(np.float32(1 / math.sqrt(D)))
+    kw, mu = {}, None
+    if vsmooth:
+        g = vc.vc_smooth_group(k.cuda(), v.cuda(), 16, 3, 11)
+        kw = dict(perm=g["perm"], mu_bf16=g["mu_bf16"])
+        mu = g["mu_bf16"]
+    z = vc.vc_quantize4(q.cuda(), k.cuda(), v.cuda(), sm_scale=sm, **kw)
+    o = vc.vc_attn_fwd4(z["q4"], z["q4_scale"], z["k4"], z["k4_scale"], z["v4"], z["v4_scale"], mu, S=S,
+                        sequential=seq)
+    torch.cuda.synchronize()
+    og = o.float().cpu().numpy()
+    qb, kb, vb = (vcsynth.bf16_bits(x) for x in (q, k, v))
+    for h in range(H):
+        res = oracle.pipeline4_head(qb, kb, vb, 0, h, vsmooth=vsmooth, nclust=16, iters=3, seed=11, sm_scale=sm,
+                                    flags=oracle.SEQUENTIAL if seq else 0)
+        if vsmooth:  # the GPU grouping is bit-exact with the oracle's (tested elsewhere); check it here too
+            assert (_np(kw["perm"])[0, h] == res["perm"]).all(), h
+        emu = oracle.bf16_bits_to_f32(res["out_bf16"])
+        err = np.linalg.norm(og[0, :, h] - emu) / np.linalg.norm(emu)
+        print(f"  head {h}: rel-L2 {err:.2e}", flush=True)
+        assert err <= REL_L2_TOL, (h, err)
