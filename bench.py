@@ -216,6 +216,38 @@ def repair_measurement(vc, w, q, k, v, flops, rho=0.005, n=3):
             "tflops_with_repair": round(flops / (t_rep * 1e-3) / 1e12, 1)}
 
 
+FP4_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 matrix-core peak
+
+
+def mxfp4_measurement(vc, w, q, k, v, g, flops, n=3):
+    """The 4-bit path (V-Smooth without ExpCast, MXFP4) on the same inputs and
+    grouping: vc_quantize4 (Q, and K/V through pi minus the block means) and
+    vc_attn_fwd4, HIP events, mean of n launches after one warm-up."""
+    import torch
+
+    z = vc.vc_quantize4(q, k, v, sm_scale=w.sm_scale, perm=g["perm"], mu_bf16=g["mu_bf16"])
+    o = torch.empty_like(q)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    tq = timed(lambda: vc.vc_quantize4(q, k, v, sm_scale=w.sm_scale, perm=g["perm"], mu_bf16=g["mu_bf16"], out=z))
+    ta = timed(lambda: vc.vc_attn_fwd4(z["q4"], z["q4_scale"], z["k4"], z["k4_scale"], z["v4"], z["v4_scale"],
+                                       g["mu_bf16"], S=w.S, out=o))
+    tf = flops / (ta * 1e-3) / 1e12
+    del z, o
+    return {"format": "MXFP4 (E2M1, E8M0 per 32)", "vsmooth": True, "quantize4_ms": round(tq, 3),
+            "attn_ms": round(ta, 3), "tflops": round(tf, 1), "frac_fp4_peak": round(tf / FP4_PEAK_TFLOPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -225,6 +257,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-repair", action="store_true", help="skip the Open-VC repair-row measurement")
+    ap.add_argument("--no-mxfp4", action="store_true", help="skip the 4-bit (MXFP4) path measurement")
     ap.add_argument("--traffic-job", action="store_true",
                     help="one attention launch + calibration copy, for rocprofv3 --pmc runs")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON", "COMMAND"),
@@ -340,6 +373,11 @@ def main():
         repair = repair_measurement(vc, w, q, k, v, flops)
         log(f"repair rows: {repair}")
 
+    mx4 = None
+    if not args.no_mxfp4 and vs_on:
+        mx4 = mxfp4_measurement(vc, w, q, k, v, g, flops)
+        log(f"mxfp4 path: {mx4}")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
@@ -371,6 +409,7 @@ def main():
         "roofline": roof,
         "bf16_baseline": bf16,
         "open_vc_repair": repair,
+        "mxfp4_path": mx4,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

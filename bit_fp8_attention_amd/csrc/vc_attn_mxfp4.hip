@@ -17,11 +17,14 @@
 //  - k4: per tile 128 rows of D/2 bytes; tile row 16 t + 4 g + v holds key
 //    32 g + 4 t + v of the tile, so that the S^T accumulator of MFMA block t,
 //    register v, in lane group g holds key 32 g + 4 t + v: lane group g then
-//    holds keys [32 g, 32 g + 32), one P block, in its own registers.
+//    holds keys [32 g, 32 g + 32), one P block, in its own registers.  The
+//    16-byte chunk c of row r sits at chunk c ^ k4swz(r), so that the 16 rows
+//    a fragment read touches spread over all LDS banks.
 //    k4_scale per tile 512 bytes [g][lr][t] (the scale of tile row 16 t + lr,
 //    channel block g; 127 where g >= D/32).
 //  - v4: per tile D channel rows of 64 bytes (keys 0..127 of the tile,
-//    key 2c in the low nibble of byte c); v4_scale per tile 512 bytes
+//    key 2c in the low nibble of byte c; 16-byte chunk c of row d at chunk
+//    c ^ ((d >> 2) & 3)); v4_scale per tile 512 bytes
 //    [g][lr][m] (the scale of channel 16 m + lr, keys [32 g, 32 g + 32)).
 #include "vc_common.hpp"
 #include "vc_launch.hpp"
@@ -50,6 +53,11 @@ VC_DEV u32 cvt8_fp4(const float (&x)[8], float scale) {
 
 // tile row holding key k of the tile (inverse of the row -> key map above)
 VC_DEV int k4_row_of_key(int k) { return 16 * ((k & 31) >> 2) + 4 * (k >> 5) + (k & 3); }
+// chunk swizzles: 4 rows of 64 bytes (2 of 32 at D = 64) fill the 256-byte
+// bank width, so rows r and r + 4 (r + 8) would collide without them
+template <int D>
+VC_DEV int k4swz(int r) { return D == 128 ? (r >> 2) & 3 : (r >> 3) & 1; }
+VC_DEV int v4swz(int d) { return (d >> 2) & 3; }
 
 // ---- quantisers (HBM-bound) ----
 
@@ -160,7 +168,7 @@ __global__ __launch_bounds__(256) void kv4_tile_kernel(const uint16_t* __restric
       wd[c] = cvt8_fp4(tt, sc);
     }
     const int row = k4_row_of_key(key);
-    *(uint4*)(kt + row * (D / 2) + 16 * blk) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    *(uint4*)(kt + row * (D / 2) + 16 * (blk ^ k4swz<D>(row))) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
     kts[(16 * blk + (row & 15)) * 8 + (row >> 4)] = (uint8_t)(e + 127);
   }
   // channel blocks the head dimension does not fill: scale 2^0
@@ -207,7 +215,7 @@ __global__ __launch_bounds__(256) void kv4_tile_kernel(const uint16_t* __restric
       for (int i = 0; i < 8; ++i) tt[i] = vt[(32 * g + 8 * c + i) * LD + d];
       wd[c] = cvt8_fp4(tt, sc);
     }
-    *(uint4*)(vtp + d * 64 + 16 * g) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    *(uint4*)(vtp + d * 64 + 16 * (g ^ v4swz(d))) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
     vts[(16 * g + (d & 15)) * 8 + (d >> 4)] = (uint8_t)(e + 127);
   }
   for (int item = tid; item < 64 * 8; item += 256)  // channel blocks past D / 16: scale 2^0
@@ -294,7 +302,11 @@ __global__ __launch_bounds__(512, 1) void attn4_kernel(
 
   const v8i ones = {0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};  // E2M1 1.0
   const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
-  float M[2] = {-INFINITY, -INFINITY};
+  // M: running max of the sub-tile's query (log2 units); the score product
+  // starts its accumulator at -M, so it emits s - M directly (0 before the
+  // first tile, which always sets M)
+  float M[2] = {0.f, 0.f};
+  v4f cinit[2] = {zero4, zero4};
   float L[2] = {0.f, 0.f};
   v4f O[2][NM];
 #pragma unroll
@@ -318,14 +330,18 @@ __global__ __launch_bounds__(512, 1) void attn4_kernel(
     const uint8_t* Vt = vst[st];
     // S^T = K Q^T: block t8 is tile rows 16 t8 + lr, channel block g
     v4f Sc[2][8];
+    uint4 kv[8];
 #pragma unroll
     for (int t8 = 0; t8 < 8; ++t8) {
-      uint4 kv = make_uint4(0, 0, 0, 0);
-      if (g < NB) kv = *(const uint4*)(Kt + (16 * t8 + lr) * (D / 2) + 16 * g);
-      const v8i kf = {(int)kv.x, (int)kv.y, (int)kv.z, (int)kv.w, 0, 0, 0, 0};
+      const int r = 16 * t8 + lr;
+      kv[t8] = g < NB ? *(const uint4*)(Kt + r * (D / 2) + 16 * (g ^ k4swz<D>(r))) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int t8 = 0; t8 < 8; ++t8) {
+      const v8i kf = {(int)kv[t8].x, (int)kv[t8].y, (int)kv[t8].z, (int)kv[t8].w, 0, 0, 0, 0};
       const int ks = sbyte(ksc, t8);
 #pragma unroll
-      for (int s = 0; s < 2; ++s) Sc[s][t8] = mfma_fp4(kf, qf[s], zero4, ks, qsc[s]);
+      for (int s = 0; s < 2; ++s) Sc[s][t8] = mfma_fp4(kf, qf[s], cinit[s], ks, qsc[s]);
     }
     const int t = tile_at(i);
     if (t == nblk - 1 && (S % kBlk) != 0) {  // keys past S: no probability
@@ -348,16 +364,23 @@ __global__ __launch_bounds__(512, 1) void attn4_kernel(
       for (int t8 = 0; t8 < 8; ++t8)
 #pragma unroll
         for (int v = 0; v < 4; ++v) lm = fmaxf(lm, Sc[s][t8][v]);
-      const float rm = max_over_groups(lm);
-      const float Mn = fmaxf(M[s], rm);
-      if (__any(Mn > M[s])) {
-        const float alpha = M[s] == Mn ? 1.0f : __builtin_amdgcn_exp2f(M[s] - Mn);  // 0 on the first tile
-        L[s] *= alpha;
+      const float rm = max_over_groups(lm);  // the row's max of s - M
+      const bool rise = i == 0 || rm > 0.0f;
+      if (__any(rise)) {
+        const float delta = rise ? -rm : 0.0f;  // M - M'
+        if (i != 0) {
+          const float alpha = __builtin_amdgcn_exp2f(delta);
+          L[s] *= alpha;
 #pragma unroll
-        for (int m = 0; m < NM; ++m) O[s][m] = O[s][m] * alpha;
-        M[s] = Mn;
+          for (int m = 0; m < NM; ++m) O[s][m] = O[s][m] * alpha;
+        }
+        M[s] -= delta;
+        cinit[s] = v4f{-M[s], -M[s], -M[s], -M[s]};
+        lm += delta;
+#pragma unroll
+        for (int t8 = 0; t8 < 8; ++t8) Sc[s][t8] = Sc[s][t8] + delta;
       }
-      const float pmax = __builtin_amdgcn_exp2f(lm - M[s]);
+      const float pmax = __builtin_amdgcn_exp2f(lm);
       const int e = mx_block_exp(pmax);
       const float sc = ldexpf(1.0f, e);
       pe[s] = e + 127;
@@ -368,7 +391,7 @@ __global__ __launch_bounds__(512, 1) void attn4_kernel(
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) p8[4 * u + v] = __builtin_amdgcn_exp2f(Sc[s][2 * q + u][v] - M[s]);
+          for (int v = 0; v < 4; ++v) p8[4 * u + v] = __builtin_amdgcn_exp2f(Sc[s][2 * q + u][v]);
         P[s][q] = (int)cvt8_fp4(p8, sc);
       }
       P[s][4] = P[s][5] = P[s][6] = P[s][7] = 0;
@@ -382,7 +405,8 @@ __global__ __launch_bounds__(512, 1) void attn4_kernel(
     }
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      const uint4 vv = *(const uint4*)(Vt + (16 * m + lr) * 64 + 16 * g);
+      const int d = 16 * m + lr;
+      const uint4 vv = *(const uint4*)(Vt + d * 64 + 16 * (g ^ v4swz(d)));
       const v8i vf = {(int)vv.x, (int)vv.y, (int)vv.z, (int)vv.w, 0, 0, 0, 0};
       const int vs = sbyte(vsc, m);
 #pragma unroll

@@ -49,13 +49,26 @@ def k4_row_of_key(k):
     return 16 * ((k & 31) >> 2) + 4 * (k >> 5) + (k & 3)
 
 
+def unswizzle(t, sw):
+    """[..., R, 16 * nc] rows whose 16-byte chunk c sits at c ^ sw(r) -> logical."""
+    R, W = t.shape[-2], t.shape[-1]
+    nc = W // 16
+    x = t.reshape(t.shape[:-1] + (nc, 16))
+    out = np.empty_like(x)
+    r = np.arange(R)
+    for c in range(nc):
+        out[..., c, :] = x[..., r, c ^ sw(r), :]
+    return out.reshape(t.shape)
+
+
 def unpack_k4(k4, k4s, D):
     """Per head: k4 [nblk, 128, D/2], k4s [nblk, 512] -> codes [S_pad, D],
     exponents [S_pad, D/32] in key order."""
     nblk = k4.shape[0]
     keys = np.arange(128)
     rows = k4_row_of_key(keys)
-    codes = nibbles(k4)[:, rows, :].reshape(nblk * 128, D)
+    sw = (lambda r: (r >> 2) & 3) if D == 128 else (lambda r: (r >> 3) & 1)
+    codes = nibbles(unswizzle(k4, sw))[:, rows, :].reshape(nblk * 128, D)
     exps = np.zeros((nblk * 128, D // 32), np.int32)
     for c in range(D // 32):
         idx = (16 * c + (rows & 15)) * 8 + (rows >> 4)
@@ -67,7 +80,7 @@ def unpack_v4(v4, v4s, D):
     """Per head: v4 [nblk, D, 64], v4s [nblk, 512] -> codes_t [D, S_pad],
     exponents [D, S_pad/32]."""
     nblk = v4.shape[0]
-    codes = np.moveaxis(nibbles(v4), 0, 1).reshape(D, nblk * 128)
+    codes = np.moveaxis(nibbles(unswizzle(v4, lambda d: (d >> 2) & 3)), 0, 1).reshape(D, nblk * 128)
     d = np.arange(D)
     exps = np.zeros((D, nblk * 4), np.int32)
     for g in range(4):
