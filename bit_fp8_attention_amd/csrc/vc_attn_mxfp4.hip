@@ -248,7 +248,9 @@ __global__ __launch_bounds__(512, 1) void attn4_kernel(
   constexpr int NB = D / 32;
   __shared__ __attribute__((aligned(1024))) uint8_t kst[2][TB];
   __shared__ __attribute__((aligned(1024))) uint8_t vst[2][TB];
-  __shared__ __attribute__((aligned(16))) uint16_t mst[2][VS ? D : 8];
+  // V-Smooth: ring of the block-mean rows (bf16) of the last 16 visited tiles
+  constexpr int MR = VS ? 16 : 1;
+  __shared__ __attribute__((aligned(16))) uint16_t mring[MR][VS ? D : 8];
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int pr = __builtin_amdgcn_readfirstlane(lin % npair);
@@ -290,7 +292,7 @@ __global__ __launch_bounds__(512, 1) void attn4_kernel(
       lds_dma16_raw(ks + loff, &kst[st][w * CW]);
       lds_dma16_raw(vs + loff, &vst[st][w * CW]);
     }
-    if (VS && w == 0 && l < D / 8) lds_dma16_raw((const uint8_t*)(mu + t * D) + loff, &mst[st][0]);
+    if (VS && w == 0 && l < D / 8) lds_dma16_raw((const uint8_t*)(mu + t * D) + loff, &mring[i & (MR - 1)][0]);
   };
   // per-lane scale bytes of tile i: 8 K scales (blocks t8) and 8 V scales (blocks m)
   auto load_scales = [&](int i, uint2& ks, uint2& vs) {
@@ -313,6 +315,17 @@ __global__ __launch_bounds__(512, 1) void attn4_kernel(
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int m = 0; m < NM; ++m) O[s][m] = zero4;
+
+  // V-Smooth: row sums of the window slots 2g, 2g + 1 (lane group g), restored
+  // every 8 tiles on the bf16 matrix cores as A += r mu^T: lane group g
+  // carries its two slots in K slots 8g .. 8g + 7 as
+  //   mean side: (mu0, 0, mu1, 0, mu0, 0, mu1, 0)   (mu is exact in bf16)
+  //   sum side:  (r0.hi, r0.hi, r1.hi, r1.hi, r0.lo, 0, r1.lo, 0)
+  float rb[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+  if (VS) {  // rows never written must read as finite zeros
+    for (int e2 = tid; e2 < MR * D; e2 += 512) (&mring[0][0])[e2] = 0;
+    __syncthreads();
+  }
 
   uint2 ksc, vsc;
   issue(0, 0);
@@ -371,6 +384,10 @@ __global__ __launch_bounds__(512, 1) void attn4_kernel(
         if (i != 0) {
           const float alpha = __builtin_amdgcn_exp2f(delta);
           L[s] *= alpha;
+          if (VS) {
+            rb[s][0] *= alpha;
+            rb[s][1] *= alpha;
+          }
 #pragma unroll
           for (int m = 0; m < NM; ++m) O[s][m] = O[s][m] * alpha;
         }
@@ -412,15 +429,38 @@ __global__ __launch_bounds__(512, 1) void attn4_kernel(
 #pragma unroll
       for (int s = 0; s < 2; ++s) O[s][m] = mfma_fp4(vf, P[s], O[s][m], vs, pe[s]);
     }
-    if (VS) {  // A += r mu: lane (g, lr) holds channels 16 m + 4 g + v of query lr
+    if (VS) {
+      const int slot = i & 7;
 #pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        const uint2 mw = *(const uint2*)&mst[st][16 * m + 4 * g];
-        const float mv[4] = {bf16_lo(mw.x), bf16_hi(mw.x), bf16_lo(mw.y), bf16_hi(mw.y)};
+      for (int s2 = 0; s2 < 2; ++s2) {
+        if (slot == 2 * g) rb[s2][0] = rr[s2];
+        if (slot == 2 * g + 1) rb[s2][1] = rr[s2];
+      }
+      if (slot == 7 || i == nblk - 1) {
+        v8bf Ar[2];
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
+        for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) O[s][m][v] = __builtin_fmaf(rr[s], mv[v], O[s][m][v]);
+          for (int jj = 0; jj < 2; ++jj) {
+            const __bf16 hi = (__bf16)rb[s2][jj];
+            const __bf16 lo = (__bf16)(rb[s2][jj] - (float)hi);
+            Ar[s2][2 * jj + 0] = hi;
+            Ar[s2][2 * jj + 1] = hi;
+            Ar[s2][4 + 2 * jj + 0] = lo;
+            Ar[s2][4 + 2 * jj + 1] = (__bf16)0.0f;
+            rb[s2][jj] = 0.f;
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          // window slot 2g + jj is visit i - slot + 2g + jj; slots past i hold
+          // zero row sums, so whatever finite row the ring holds there adds nothing
+          const u32 m0 = mring[(i - slot + 2 * g) & (MR - 1)][16 * m + lr];
+          const u32 m1 = mring[(i - slot + 2 * g + 1) & (MR - 1)][16 * m + lr];
+          const v8bf Bm = __builtin_bit_cast(v8bf, (v4u){m0, m1, m0, m1});
+          O[0][m] = mfma_bf16(Bm, Ar[0], O[0][m]);
+          O[1][m] = mfma_bf16(Bm, Ar[1], O[1][m]);
+        }
       }
     }
     ksc = ksn;
