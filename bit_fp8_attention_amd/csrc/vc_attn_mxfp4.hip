@@ -224,10 +224,13 @@ __global__ __launch_bounds__(256) void kv4_tile_kernel(const uint16_t* __restric
 
 // ---- attention ----
 //
-// One workgroup = two 128-query tiles of one (b, h) (8 waves x 32 queries,
-// waves 0-3 tile 2p, waves 4-7 tile 2p + 1), sharing one stream of K/V
-// tiles in the mid-window order through a 2-stage LDS ring that all waves
-// fill with global_load_lds_dwordx4.  Per tile and 16-query sub-tile:
+// One workgroup = one 128-query tile of one (b, h) (4 waves x 32 queries),
+// two workgroups per CU: their barriers are independent, so one
+// workgroup's VALU work overlaps the other's matrix-core work on each SIMD
+// (with both tiles in one 8-wave workgroup the shared per-tile barrier kept
+// the two waves of a SIMD in the same phase: 8-9% slower).  K/V tiles come
+// in the mid-window order through a 2-stage LDS ring that the 4 waves fill
+// with global_load_lds_dwordx4.  Per tile and 16-query sub-tile:
 // S^T = K Q^T (scores in log2 units), the running max on the true scores,
 // p = 2^(s - M) (v_exp_f32), one E8M0 block scale per lane (its 32 keys),
 // E2M1 codes, row sum (ones x P^T) and A^T += V^T P^T on the block-scaled
@@ -238,7 +241,7 @@ VC_DEV v4f mfma_fp4(v8i a, v8i b, v4f c, int sa, int sb) {
 }
 
 template <int D, bool VS>
-__global__ __launch_bounds__(512, 1) void attn4_kernel(
+__global__ __launch_bounds__(256, 2) void attn4_kernel(
     const uint8_t* __restrict__ q4, const uint8_t* __restrict__ q4s, const uint8_t* __restrict__ k4,
     const uint8_t* __restrict__ k4s, const uint8_t* __restrict__ v4, const uint8_t* __restrict__ v4s,
     const uint16_t* __restrict__ mu, uint16_t* __restrict__ o, int64_t oB, int64_t oS, int64_t oH, int S, int H,
@@ -257,12 +260,11 @@ __global__ __launch_bounds__(512, 1) void attn4_kernel(
   const int bh = __builtin_amdgcn_readfirstlane(lin / npair);
   const int tid = threadIdx.x, l = tid & 63, lr = l & 15, g = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool hb = w >= 4;
   const int wq = w & 3;
-  const bool live = 2 * pr + (hb ? 1 : 0) < nblk;
-  const int qt = __builtin_amdgcn_readfirstlane(live ? 2 * pr + (hb ? 1 : 0) : nblk - 1);
+  const bool live = true;
+  const int qt = pr;  // one query tile per workgroup
   const int64_t S_pad = (int64_t)nblk * kBlk;
-  const int start = __builtin_amdgcn_readfirstlane(sequential ? 0 : min(2 * pr + 1 + window, nblk - 1));
+  const int start = __builtin_amdgcn_readfirstlane(sequential ? 0 : min((qt | 1) + window, nblk - 1));
   auto tile_at = [&](int i) -> int { return sequential ? i : (i <= start ? start - i : i); };
 
   // Q fragments and scales of the wave's two 16-query sub-tiles
@@ -282,15 +284,18 @@ __global__ __launch_bounds__(512, 1) void attn4_kernel(
   }
 
   // copies of tile i into stage st: each wave 1/8 of the K and of the V tile
-  constexpr int CW = TB / 8;  // bytes per wave (1 KB at D = 128)
+  constexpr int CW = TB / 4;  // bytes per wave (2 KB at D = 128)
   const unsigned loff = (unsigned)l * 16u;
   auto issue = [&](int i, int st) {
     const int64_t t = (int64_t)bh * nblk + tile_at(i);
     const uint8_t* ks = k4 + t * TB + w * CW;
     const uint8_t* vs = v4 + t * TB + w * CW;
-    if (l * 16 < CW) {
-      lds_dma16_raw(ks + loff, &kst[st][w * CW]);
-      lds_dma16_raw(vs + loff, &vst[st][w * CW]);
+#pragma unroll
+    for (int r = 0; r < (CW + 1023) / 1024; ++r) {
+      if (l * 16 < CW - 1024 * r) {
+        lds_dma16_raw(ks + 1024 * r + loff, &kst[st][w * CW + 1024 * r]);
+        lds_dma16_raw(vs + 1024 * r + loff, &vst[st][w * CW + 1024 * r]);
+      }
     }
     if (VS && w == 0 && l < D / 8) lds_dma16_raw((const uint8_t*)(mu + t * D) + loff, &mring[i & (MR - 1)][0]);
   };
@@ -323,7 +328,7 @@ __global__ __launch_bounds__(512, 1) void attn4_kernel(
   //   sum side:  (r0.hi, r0.hi, r1.hi, r1.hi, r0.lo, 0, r1.lo, 0)
   float rb[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
   if (VS) {  // rows never written must read as finite zeros
-    for (int e2 = tid; e2 < MR * D; e2 += 512) (&mring[0][0])[e2] = 0;
+    for (int e2 = tid; e2 < MR * D; e2 += 256) (&mring[0][0])[e2] = 0;
     __syncthreads();
   }
 
@@ -517,22 +522,22 @@ hipError_t launch_attn4(const vc_shape& sh, int window, uint32_t flags, const ui
                         const uint8_t* k4, const uint8_t* k4s, const uint8_t* v4, const uint8_t* v4s,
                         const uint16_t* mu, BshdOut o, hipStream_t st) {
   const int nblk = (sh.S + kBlk - 1) / kBlk;
-  const int npair = (nblk + 1) / 2;
+  const int npair = nblk;  // workgroups per head: one query tile each
   const int seq = (flags & VC_ATTN_SEQUENTIAL) ? 1 : 0;
   const unsigned n = (unsigned)((int64_t)npair * sh.H * sh.B);
   if (sh.D == 128) {
     if (mu)
-      attn4_kernel<128, true><<<n, 512, 0, st>>>(q4, q4s, k4, k4s, v4, v4s, mu, o.p, o.sB, o.sS, o.sH, sh.S, sh.H,
+      attn4_kernel<128, true><<<n, 256, 0, st>>>(q4, q4s, k4, k4s, v4, v4s, mu, o.p, o.sB, o.sS, o.sH, sh.S, sh.H,
                                                  nblk, npair, window, seq);
     else
-      attn4_kernel<128, false><<<n, 512, 0, st>>>(q4, q4s, k4, k4s, v4, v4s, nullptr, o.p, o.sB, o.sS, o.sH, sh.S,
+      attn4_kernel<128, false><<<n, 256, 0, st>>>(q4, q4s, k4, k4s, v4, v4s, nullptr, o.p, o.sB, o.sS, o.sH, sh.S,
                                                   sh.H, nblk, npair, window, seq);
   } else {
     if (mu)
-      attn4_kernel<64, true><<<n, 512, 0, st>>>(q4, q4s, k4, k4s, v4, v4s, mu, o.p, o.sB, o.sS, o.sH, sh.S, sh.H,
+      attn4_kernel<64, true><<<n, 256, 0, st>>>(q4, q4s, k4, k4s, v4, v4s, mu, o.p, o.sB, o.sS, o.sH, sh.S, sh.H,
                                                 nblk, npair, window, seq);
     else
-      attn4_kernel<64, false><<<n, 512, 0, st>>>(q4, q4s, k4, k4s, v4, v4s, nullptr, o.p, o.sB, o.sS, o.sH, sh.S,
+      attn4_kernel<64, false><<<n, 256, 0, st>>>(q4, q4s, k4, k4s, v4, v4s, nullptr, o.p, o.sB, o.sS, o.sH, sh.S,
                                                  sh.H, nblk, npair, window, seq);
   }
   return hipGetLastError();
