@@ -222,3 +222,35 @@ def test_expcast_validation(vc):
     assert L.vc_expcast_codes(P(FAKE), P(FAKE), P(FAKE), -1, 1, P(FAKE), st) == 2
     assert L.vc_expcast_codes(None, P(FAKE), P(FAKE), 4, 1, P(FAKE), st) == 1
     assert L.vc_expcast_codes(P(FAKE + 2), P(FAKE), P(FAKE), 4, 1, P(FAKE), st) == 3
+
+
+def test_mxfp4_validation(vc):
+    L, m = vc.lib(), vc
+    P = ctypes.c_void_p
+    sh = _shape()
+    st = ctypes.c_void_p(0)
+    x = m.vc_bshd(FAKE, 256 * 2 * 128, 2 * 128, 128)
+    xb = ctypes.byref(x)
+    none = m.vc_bshd(None, 0, 0, 0)
+    outs = [P(FAKE)] * 6
+    # K without V, perm without mu, perm without K
+    assert L.vc_quantize4(ctypes.byref(sh), 0.0, xb, xb, ctypes.byref(none), None, None, *outs, st) == 1
+    assert L.vc_quantize4(ctypes.byref(sh), 0.0, xb, xb, xb, P(FAKE), None, *outs, st) == 1
+    assert L.vc_quantize4(ctypes.byref(sh), 0.0, xb, ctypes.byref(none), ctypes.byref(none), P(FAKE), P(FAKE),
+                          *outs, st) == 1
+    # bad softmax scale, misaligned outputs, a bad shape
+    assert L.vc_quantize4(ctypes.byref(sh), -1.0, xb, xb, xb, None, None, *outs, st) == 4
+    assert L.vc_quantize4(ctypes.byref(sh), 0.0, xb, xb, xb, None, None, P(FAKE + 8), *outs[1:], st) == 3
+    assert L.vc_quantize4(ctypes.byref(sh), 0.0, xb, xb, xb, None, None, P(FAKE), P(FAKE), P(FAKE),
+                          P(FAKE + 4), P(FAKE), P(FAKE), st) == 3
+    assert L.vc_quantize4(ctypes.byref(m.vc_shape(1, 2, 256, 96)), 0.0, xb, xb, xb, None, None, *outs, st) == 2
+    o = m.vc_bshd_out(FAKE, 256 * 2 * 128, 2 * 128, 128)
+    good = m.vc_attn_params(0.0, 2, 0)
+    args = [P(FAKE)] * 6
+    assert L.vc_attn_fwd4(ctypes.byref(sh), None, *args, None, ctypes.byref(o), st) == 1
+    assert L.vc_attn_fwd4(ctypes.byref(sh), ctypes.byref(good), P(FAKE), None, *[P(FAKE)] * 4, None,
+                          ctypes.byref(o), st) == 1
+    assert L.vc_attn_fwd4(ctypes.byref(sh), ctypes.byref(good), *args, P(FAKE + 8), ctypes.byref(o), st) == 3
+    assert L.vc_attn_fwd4(ctypes.byref(sh), ctypes.byref(m.vc_attn_params(0.0, -1, 0)), *args, None,
+                          ctypes.byref(o), st) == 4
+    assert L.vc_attn_fwd4(ctypes.byref(sh), ctypes.byref(good), *args, None, None, st) == 1

@@ -86,3 +86,31 @@ def test_longcat_full_size(vc):
 
 def test_plain_full_size(vc):
     _run(vc, "plain", heads=[0, 11, 23], rows_per_head=24, seed_rows=4)
+
+
+def test_wan_full_size_mxfp4(vc):
+    # the 4-bit path at the headline shape: the same grouping, vc_quantize4,
+    # vc_attn_fwd4; sampled rows of two heads against the oracle's 4-bit
+    # emulation
+    w = vcsynth.WORKLOADS["wan"]
+    print(f"case full size wan, 4-bit: B={w.B} H={w.H} S={w.S} D={w.D}", flush=True)
+    q, k, v = vcsynth.make_qkv("wan", device="cuda")
+    g = vc.vc_smooth_group(k, v, w.clusters, w.iters, w.seed)
+    z = vc.vc_quantize4(q, k, v, sm_scale=w.sm_scale, perm=g["perm"], mu_bf16=g["mu_bf16"])
+    o = vc.vc_attn_fwd4(z["q4"], z["q4_scale"], z["k4"], z["k4_scale"], z["v4"], z["v4_scale"], g["mu_bf16"], S=w.S)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all().item()
+    perm = g["perm"].cpu().numpy()
+    qb, kb, vb = (vcsynth.bf16_bits(x) for x in (q, k, v))
+    og = o.float().cpu().numpy()
+    del q, k, v, o, z
+    rng = np.random.default_rng(5)
+    for h in (0, 39):
+        rows = np.unique(np.append(np.sort(rng.choice(w.S, 8, replace=False)), w.S - 1))
+        res = oracle.pipeline4_head(qb, kb, vb, 0, h, vsmooth=True, nclust=w.clusters, iters=w.iters, seed=w.seed,
+                                    sm_scale=w.sm_scale, rows=rows, window=2)
+        assert (perm[0, h] == res["perm"]).all(), ("perm", h)
+        emu = oracle.bf16_bits_to_f32(res["out_bf16"])
+        err = _rel_l2(og[0, rows, h], emu)
+        print(f"  head {h}: {rows.size} rows, rel-L2 {err:.2e}", flush=True)
+        assert err <= REL_L2_TOL, (h, err)
