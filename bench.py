@@ -217,6 +217,49 @@ def repair_measurement(vc, w, q, k, v, flops, rho=0.005, n=3):
 
 
 FP4_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 matrix-core peak
+HBM_PEAK_GBPS = 8000.0
+
+
+def prep_measurement(vc, w, q, k, v, qz, g, ws, clusters, iters, attn_ms, ms_q, ms_g, n=3):
+    """The preparation passes against HBM bandwidth (algorithmic bytes over
+    their timed mean), and the grouping cost amortised over a 50-step
+    schedule ([VC] §3.4 and App. A: grouping on the first ceil(50 / 4) = 13
+    steps, the permutation recomputed at steps 0, 4, 8, 12 and reused in
+    between), as a share of one attention call."""
+    import torch
+
+    B, H, S, D = w.B, w.H, w.S, w.D
+    nb = (S + 127) // 128
+    bf = 2 * B * S * H * D            # one bf16 tensor
+    f8 = B * H * nb * 128 * D         # one FP8 operand
+    q_bytes = bf + f8 + 4 * B * H * nb
+    apply_bytes = 3 * bf + 2 * f8 + 8 * B * H * S + 6 * B * H * nb * D  # gather K, V; residual pass; K', R; labels, pi; means
+    group_bytes = iters * bf + apply_bytes
+    tq = sum(ms_q) / len(ms_q)
+    tg = sum(ms_g) / len(ms_g)
+    # the reuse step: the permutation of the last grouping, gather + means + residuals only
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    vc.vc_smooth_group(k, v, clusters, iters, w.seed, workspace=ws, out=dict(g), reuse_perm=g["perm"])
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n):
+        vc.vc_smooth_group(k, v, clusters, iters, w.seed, workspace=ws, out=dict(g), reuse_perm=g["perm"])
+    e1.record()
+    e1.synchronize()
+    tr = e0.elapsed_time(e1) / n
+    steps, window = 50, 13
+    regroups = sum(1 for s in range(window) if s % 4 == 0)
+    per_step = (regroups * tg + (window - regroups) * tr) / steps
+    gb = lambda b, t: round(b / (t * 1e-3) / 1e9, 1)  # noqa: E731
+    return {"vc_quantize_q": {"gb": round(q_bytes / 1e9, 3), "ms": round(tq, 3), "GBps": gb(q_bytes, tq),
+                              "frac_hbm": round(gb(q_bytes, tq) / HBM_PEAK_GBPS, 3)},
+            "vc_smooth_group": {"gb": round(group_bytes / 1e9, 3), "ms": round(tg, 3), "GBps": gb(group_bytes, tg),
+                                "frac_hbm": round(gb(group_bytes, tg) / HBM_PEAK_GBPS, 3)},
+            "vc_smooth_group_reuse_perm": {"gb": round(apply_bytes / 1e9, 3), "ms": round(tr, 3),
+                                           "GBps": gb(apply_bytes, tr),
+                                           "frac_hbm": round(gb(apply_bytes, tr) / HBM_PEAK_GBPS, 3)},
+            "grouping_amortised_50_steps": {"ms_per_step": round(per_step, 3),
+                                            "pct_of_attention": round(100 * per_step / attn_ms, 2)}}
 
 
 def mxfp4_measurement(vc, w, q, k, v, g, flops, n=3):
@@ -368,6 +411,11 @@ def main():
         except vc.VcError as ex:
             log(f"bf16 baseline unavailable: {ex}")
 
+    prep = None
+    if vs_on:
+        prep = prep_measurement(vc, w, q, k, v, qz, g, ws, clusters, iters, attn_ms, ms_q, ms_g)
+        log(f"prep: {prep}")
+
     repair = None
     if not args.no_repair:
         repair = repair_measurement(vc, w, q, k, v, flops)
@@ -408,6 +456,7 @@ def main():
         "path_tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
         "roofline": roof,
         "bf16_baseline": bf16,
+        "prep_passes": prep,
         "open_vc_repair": repair,
         "mxfp4_path": mx4,
         "cpu_baseline": cpu,
