@@ -167,9 +167,9 @@ def cpu_baseline(w, q, k, v, target_s=12.0):
         t0 = time.perf_counter()
         oracle.attn_emulate_rows(prep["q_codes"], prep["q_scale"], kc, ks, vc_, vs, mu, w.S, 0.125, rows)
         elapsed = time.perf_counter() - t0
-        if elapsed >= target_s / 4 or n >= w.S:
+        if elapsed >= 0.8 * target_s or n >= w.S:
             break
-        n = min(w.S, int(n * max(2.0, target_s / 4 / max(elapsed, 1e-3))))
+        n = min(w.S, int(n * max(2.0, target_s / max(elapsed, 1e-3))))
     flops = 4.0 * n * w.S * w.D
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {
