@@ -354,29 +354,34 @@ __global__ __launch_bounds__(256, 2) void attn4_kernel(
       const int r = 16 * t8 + lr;
       kv[t8] = g < NB ? *(const uint4*)(Kt + r * (D / 2) + 16 * (g ^ k4swz<D>(r))) : make_uint4(0, 0, 0, 0);
     }
-#pragma unroll
-    for (int t8 = 0; t8 < 8; ++t8) {
-      const v8i kf = {(int)kv[t8].x, (int)kv[t8].y, (int)kv[t8].z, (int)kv[t8].w, 0, 0, 0, 0};
-      const int ks = sbyte(ksc, t8);
-#pragma unroll
-      for (int s = 0; s < 2; ++s) Sc[s][t8] = mfma_fp4(kf, qf[s], cinit[s], ks, qsc[s]);
-    }
     const int t = tile_at(i);
-    if (t == nblk - 1 && (S % kBlk) != 0) {  // keys past S: no probability
-      const int lim = S - t * kBlk;
-#pragma unroll
-      for (int t8 = 0; t8 < 8; ++t8)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (32 * g + 4 * t8 + v >= lim) {
-            Sc[0][t8][v] = -INFINITY;
-            Sc[1][t8][v] = -INFINITY;
-          }
-    }
+    const bool ragged = t == nblk - 1 && (S % kBlk) != 0;  // keys past S: no probability
     v8i P[2];
     int pe[2];
+    float lmx[2], rr[2];
+    // one sub-tile (16 query rows) at a time: scores; running max and
+    // rescale; probabilities and their codes; row sum and P.V.  Sub-tile 1's
+    // scores come after sub-tile 0's rescale, and sub-tile 0's P.V after
+    // sub-tile 1's, so each stretch between the rescale branches pairs one
+    // sub-tile's matrix-core work with the other's VALU work
+    auto qk = [&](int s) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+      for (int t8 = 0; t8 < 8; ++t8) {
+        const v8i kf = {(int)kv[t8].x, (int)kv[t8].y, (int)kv[t8].z, (int)kv[t8].w, 0, 0, 0, 0};
+        Sc[s][t8] = mfma_fp4(kf, qf[s], cinit[s], sbyte(ksc, t8), qsc[s]);
+      }
+    };
+    auto mask = [&](int s) {
+      if (ragged) {
+        const int lim = S - t * kBlk;
+#pragma unroll
+        for (int t8 = 0; t8 < 8; ++t8)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (32 * g + 4 * t8 + v >= lim) Sc[s][t8][v] = -INFINITY;
+      }
+    };
+    auto rescale = [&](int s) {
       float lm = -INFINITY;  // the lane's max (its 32 keys: one P block)
 #pragma unroll
       for (int t8 = 0; t8 < 8; ++t8)
@@ -402,7 +407,10 @@ __global__ __launch_bounds__(256, 2) void attn4_kernel(
 #pragma unroll
         for (int t8 = 0; t8 < 8; ++t8) Sc[s][t8] = Sc[s][t8] + delta;
       }
-      const float pmax = __builtin_amdgcn_exp2f(lm);
+      lmx[s] = lm;
+    };
+    auto probs = [&](int s) {
+      const float pmax = __builtin_amdgcn_exp2f(lmx[s]);
       const int e = mx_block_exp(pmax);
       const float sc = ldexpf(1.0f, e);
       pe[s] = e + 127;
@@ -417,23 +425,46 @@ __global__ __launch_bounds__(256, 2) void attn4_kernel(
         P[s][q] = (int)cvt8_fp4(p8, sc);
       }
       P[s][4] = P[s][5] = P[s][6] = P[s][7] = 0;
-    }
-    // row sums and A^T += V^T P^T
-    float rr[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    };
+    // V's fragments, read once for both sub-tiles
+    v8i vf[NM];
+    auto pv = [&](int s) {
+      // row sum and A^T += V^T P^T
       rr[s] = mfma_fp4(ones, P[s], zero4, 127, pe[s])[0];
       L[s] += rr[s];
-    }
+#pragma unroll
+      for (int m = 0; m < NM; ++m) O[s][m] = mfma_fp4(vf[m], P[s], O[s][m], sbyte(vsc, m), pe[s]);
+    };
+    qk(0);
+    mask(0);
+    rescale(0);
+    qk(1);
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       const int d = 16 * m + lr;
       const uint4 vv = *(const uint4*)(Vt + d * 64 + 16 * (g ^ v4swz(d)));
-      const v8i vf = {(int)vv.x, (int)vv.y, (int)vv.z, (int)vv.w, 0, 0, 0, 0};
-      const int vs = sbyte(vsc, m);
-#pragma unroll
-      for (int s = 0; s < 2; ++s) O[s][m] = mfma_fp4(vf, P[s], O[s][m], vs, pe[s]);
+      vf[m] = v8i{(int)vv.x, (int)vv.y, (int)vv.z, (int)vv.w, 0, 0, 0, 0};
     }
+    probs(0);
+    // sub-tile 0's codes stay ahead of sub-tile 1's branches, and its
+    // conversion work is spread between sub-tile 1's score products
+    asm volatile("" ::"v"(P[0][0]), "v"(P[0][1]), "v"(P[0][2]), "v"(P[0][3]), "v"(pe[0]));
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+    mask(1);
+    rescale(1);
+    pv(0);
+    probs(1);
+    // and sub-tile 1's between sub-tile 0's row sum and P.V products
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+    pv(1);
     if (VS) {
       const int slot = i & 7;
 #pragma unroll
