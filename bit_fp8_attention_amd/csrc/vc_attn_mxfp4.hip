@@ -452,7 +452,7 @@ __global__ __launch_bounds__(256, 2) void attn4_kernel(
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
     }
     mask(1);
     rescale(1);
@@ -462,7 +462,7 @@ __global__ __launch_bounds__(256, 2) void attn4_kernel(
 #pragma unroll
     for (int k = 0; k < 9; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
     }
     pv(1);
     if (VS) {
