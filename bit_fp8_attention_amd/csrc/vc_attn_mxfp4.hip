@@ -41,6 +41,14 @@ VC_DEV int mx_block_exp(float amax) {
   return e;
 }
 
+// mx_block_exp for a probability maximum p in [0, 1] (finite), without the
+// loop: with p = m 2^f, m in [0.5, 1), the answer is f - 3, plus one when
+// m > 0.75 (then 6 2^(f - 3) = 0.75 2^f < p), at least -127; 0 for p = 0
+VC_DEV int mx_block_exp_prob(float p) {
+  const int e = __builtin_amdgcn_frexp_expf(p) - 3 + (__builtin_amdgcn_frexp_mantf(p) > 0.75f ? 1 : 0);
+  return p > 0.0f ? max(e, -127) : 0;
+}
+
 // 8 fp32 -> 8 E2M1 nibbles (one dword, element i in nibble i) at scale 2^e
 VC_DEV u32 cvt8_fp4(const float (&x)[8], float scale) {
   u32 w = 0u;
@@ -410,8 +418,8 @@ __global__ __launch_bounds__(256, 2) void attn4_kernel(
       lmx[s] = lm;
     };
     auto probs = [&](int s) {
-      const float pmax = __builtin_amdgcn_exp2f(lmx[s]);
-      const int e = mx_block_exp(pmax);
+      const float pmax = __builtin_amdgcn_exp2f(lmx[s]);  // in [0, 1]: lmx <= 0
+      const int e = mx_block_exp_prob(pmax);
       const float sc = ldexpf(1.0f, e);
       pe[s] = e + 127;
       // key 32 g + 4 t8 + v is nibble 4 t8 + v of the lane's P operand
