@@ -604,6 +604,9 @@ __global__ __launch_bounds__(256) void label_scatter(const int32_t* __restrict__
   }
 }
 
+// A gathered token index, clamped into [0, S) (negative values to 0).
+VC_DEV int clamp_tok(int t, int S) { return min(max(t, 0), S - 1); }
+
 template <int D>
 struct ApplyMap {
   static constexpr int CPR = D / 8;         // 16-byte chunks per row
@@ -629,11 +632,14 @@ __global__ __launch_bounds__(256) void group_apply1(const uint16_t* __restrict__
   const int64_t bh = (int64_t)b * H + h;
   const int ch = t % Mp::CPR, rg = t / Mp::CPR;
   const int nvalid = min(kBlk, S - j * kBlk);
+  // perm may be the caller's (VC_GROUP_REUSE_PERM): every gathered index is
+  // clamped into [0, S), so a malformed permutation gives wrong codes, never
+  // an access outside K, V or the RoPE tables
   int tok[Mp::RPT];
 #pragma unroll
   for (int r = 0; r < Mp::RPT; ++r) {
     int row = rg * Mp::RPT + r;
-    tok[r] = row < nvalid ? perm[bh * S + j * kBlk + row] : -1;
+    tok[r] = row < nvalid ? clamp_tok(perm[bh * S + j * kBlk + row], S) : -1;
   }
   // ---- K' = K[pi], per-block E4M3 ----
   // With preprocessing ([VC] App. B: centring statistics, RoPE, gather,
@@ -769,7 +775,7 @@ __global__ __launch_bounds__(256) void group_apply2(const uint16_t* __restrict__
     const int row = rg * Mp::RPT + r;
     u32 c0 = 0, c1 = 0;
     if (row < nvalid) {
-      const int tk = perm[bh * S + j * kBlk + row];
+      const int tk = clamp_tok(perm[bh * S + j * kBlk + row], S);  // as in pass 1
       uint4 w = *(const uint4*)(vb + (int64_t)tk * vS + ch * 8);
       const float* mu = mu_l + ch * 8;
       const float* iv = inv_l + ch * 8;

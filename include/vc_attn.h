@@ -411,8 +411,12 @@ int32_t vc_attn_fwd_bf16(const vc_shape* shape, const vc_attn_params* p, const v
 /*
  * vc_expcast_codes -- the ExpCast code map alone, for bit-exact checks
  * ([VC] §3.3 Eq. 7): codes[i] = min(120, Round_even_clamped0(fma(a[r], x[i],
- * b[r]))) with r = i / row_len, evaluated by the same device routine the
- * attention kernel uses, plus the explicit upper clip.
+ * b[r]))) with r = i / row_len: one fp32 fused multiply-add, then the
+ * round-half-even integer conversion clamped at 0 (v_cvt_pk_u8_f32), then the
+ * explicit upper clip.  It is a routine of its own: vc_attn_fwd forms the
+ * pre-rounding value inside its score product instead (the accumulator
+ * starts at the code offset) and applies the same conversion to it, so its
+ * codes are observable only through its output.
  * x: fp32 [n]; a, b: fp32 [n / row_len]; codes: uint8 [n].  n % row_len == 0.
  */
 int32_t vc_expcast_codes(const float* x, const float* a, const float* b, int64_t n, int32_t row_len,

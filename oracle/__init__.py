@@ -67,7 +67,6 @@ def lib():
         L.vco_expcast_codes.argtypes = [P, P, P, i64, i32, P]
         L.vco_expcast_code_u.argtypes = [ctypes.c_double, ctypes.c_double]
         L.vco_expcast_code_u.restype = ctypes.c_int
-        L.vco_quantize_blocks.argtypes = [P, i64, i32, i32, P, P]
         L.vco_quantize_blocks_pow2.argtypes = [P, i64, i32, i32, f32, P, P]
         L.vco_prep_rows.argtypes = [P, i64, i32, i32, i32, P, P, P, P]
         L.vco_quantize_f32_blocks_pow2.argtypes = [P, i32, i32, f32, P, P]

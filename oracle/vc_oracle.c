@@ -281,28 +281,6 @@ EXPORT void vco_quantize_f32_blocks_pow2(const float* y, int32_t S, int32_t D, f
 }
 
 /*
- * One head, amax/448 rule (kept for reference comparisons).  x: bf16 rows,
- * row r at x + r*ld (D contiguous).
- * Out: codes [nblk*128][D] (rows >= S are zero), scale [nblk].
- */
-EXPORT void vco_quantize_blocks(const uint16_t* x, int64_t ld, int32_t S, int32_t D, uint8_t* codes,
-                                float* scale) {
-  int32_t nblk = (S + 127) / 128;
-  for (int32_t j = 0; j < nblk; ++j) {
-    int32_t r0 = j * 128, r1 = r0 + 128 < S ? r0 + 128 : S;
-    float amax = 0.0f;
-    for (int32_t r = r0; r < r1; ++r)
-      for (int32_t d = 0; d < D; ++d) amax = fmaxf(amax, fabsf(bf16_to_f32(x[r * ld + d])));
-    float s, inv;
-    scale_pair(amax, &s, &inv);
-    scale[j] = s;
-    for (int32_t r = r0; r < j * 128 + 128; ++r)
-      for (int32_t d = 0; d < D; ++d)
-        codes[(int64_t)r * D + d] = (r < S) ? vco_e4m3_encode(bf16_to_f32(x[r * ld + d]) * inv) : 0;
-  }
-}
-
-/*
  * Per-head V (plain path).  Out: codes in key-contiguous order
  * codes_t[d][S_pad] (pad keys zero), one scale.
  */

@@ -2,11 +2,13 @@
 
 Bit-exact: ExpCast codes on identical fp32 inputs, vc_quantize codes and
 scales, k-means labels / centroids / permutation, block means, scaled means
-(as the stored bf16 hi/lo pairs), residual codes and K' codes.  Attention output: relative L2 <= 1e-2 against
-the quantised-pipeline emulation (differences come only from the matrix
-cores' fp32 accumulation order flipping a code at a rounding boundary, and
-from exp2f versus exact alpha), and within the Eq. 15 envelope of the fp64
-softmax.
+(as the stored bf16 hi/lo pairs), residual codes and K' codes.  Attention
+output: relative L2 <= 1e-2 against the quantised-pipeline emulation per
+head, and every element the bf16 rounding of a value within the bound of
+tests/expcast_ref.py (elementwise_tol: the fp32 order of the matrix cores'
+sums and exp2f rescales, plus one code step only for keys whose code lies
+within 1e-3 of a rounding boundary); and within the Eq. 15 envelope of the
+fp64 softmax.
 """
 import math
 
@@ -14,6 +16,7 @@ import numpy as np
 import pytest
 import torch
 
+import expcast_ref as ER
 import oracle
 import vcsynth
 from oracle import exact
@@ -156,6 +159,10 @@ def _plain_case(vc, q, k, v, sm_scale, window=2, sequential=False, rows_per_head
                                        flags=oracle.SEQUENTIAL if sequential else 0)
             emu = oracle.bf16_bits_to_f32(res["out_bf16"])
             errs.append(_rel_l2(og[b, rows, h], emu))
+            # every element: bf16 of a value within the fp32-order / boundary-code bound
+            st = ER.check_rows(og[b, rows, h], res, S, rows, window, sequential)
+            print(f"  b{b} h{h}: rel-L2 {errs[-1]:.2e}, row max {st['row_rel_l2_max']:.2e}, "
+                  f"bit-identical {st['bit_identical']:.4f}", flush=True)
     return max(errs), og
 
 
@@ -318,6 +325,27 @@ def test_smooth_group_reuse_perm_bitexact(vc, S, H, D):
         _apply_matches(g2, ref, 0, h, D)
 
 
+def test_smooth_group_reuse_perm_clamped(vc):
+    # a caller's permutation with entries outside [0, S): the apply kernels
+    # clamp every gathered index into [0, S), so the result is the apply step
+    # on the clamped list (wrong codes for a wrong list, never an access
+    # outside K or V)
+    print("case group reuse perm, out-of-range entries clamped", flush=True)
+    S, H, D = 300, 2, 128
+    q, k, v = vcsynth.random_qkv(1, S, H, D, seed=8, v_kind="t3")
+    rng = np.random.default_rng(8)
+    perm = np.stack([rng.permutation(S) for _ in range(H)])[None].astype(np.int32)
+    perm[0, 0, [3, 150, 299]] = [-7, S + 5, 2 ** 31 - 1]
+    perm[0, 1, [0, 128]] = [-(2 ** 31), S]
+    g = vc.vc_smooth_group(k.cuda(), v.cuda(), 16, 2, 3, reuse_perm=torch.from_numpy(perm).cuda())
+    torch.cuda.synchronize()
+    kb, vb = vcsynth.bf16_bits(k), vcsynth.bf16_bits(v)
+    for h in range(H):
+        pc = np.clip(perm[0, h].astype(np.int64), 0, S - 1).astype(np.int32)
+        ref = oracle.smooth_apply_head(np.ascontiguousarray(kb[0, :, h]), np.ascontiguousarray(vb[0, :, h]), pc)
+        _apply_matches(g, ref, 0, h, D)
+
+
 # --------------------------------------------------------------------------- #
 # attention, V-Smooth path
 # --------------------------------------------------------------------------- #
@@ -340,6 +368,9 @@ def _vsmooth_case(vc, q, k, v, clusters, iters, seed, sm, rows_per_head=None, wi
                                        sm_scale=sm, rows=rows, window=window)
             emu = oracle.bf16_bits_to_f32(res["out_bf16"])
             errs.append(_rel_l2(og[b, rows, h], emu))
+            st = ER.check_rows(og[b, rows, h], res, S, rows, window, vsmooth=True)
+            print(f"  b{b} h{h}: rel-L2 {errs[-1]:.2e}, row max {st['row_rel_l2_max']:.2e}, "
+                  f"bit-identical {st['bit_identical']:.4f}", flush=True)
             res_all[(b, h)] = res
     return max(errs), og, res_all
 

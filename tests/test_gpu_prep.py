@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 import torch
 
+import expcast_ref as ER
 import oracle
 import vcsynth
 from oracle import exact
@@ -119,6 +120,10 @@ def test_attn_with_prep_parity(vc, vsmooth):
         emu = oracle.bf16_bits_to_f32(res["out_bf16"])
         err = np.linalg.norm(og[0, :, h] - emu) / np.linalg.norm(emu)
         assert err <= REL_L2_TOL, (h, err)
+        # every element (tests/expcast_ref.py): the scores come from the prepared codes
+        st = ER.check_rows(og[0, :, h], res, S, np.arange(S), 2, vsmooth=vsmooth)
+        print(f"  head {h}: rel-L2 {err:.2e}, row max {st['row_rel_l2_max']:.2e}, "
+              f"bit-identical {st['bit_identical']:.4f}", flush=True)
         # and close to exact attention on the rotary-embedded operands
         qr, _ = oracle.prep_rows(qb[0, :, h], oracle.PREP_ROPE, cs, sn)
         kr, _ = oracle.prep_rows(kb[0, :, h], oracle.PREP_ROPE, cs, sn)

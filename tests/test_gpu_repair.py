@@ -16,6 +16,7 @@ import numpy as np
 import pytest
 import torch
 
+import expcast_ref as ER
 import oracle
 import vcsynth
 from oracle import exact
@@ -145,6 +146,10 @@ def test_attn_with_repair_parity(vc, S, D, rho, seq):
         emu = oracle.bf16_bits_to_f32(res["out_bf16"])
         err = _rel_l2(og[0, :, h], emu)
         assert err <= REL_L2_TOL, (h, err)
+        # every element, repair keys included (tests/expcast_ref.py)
+        st = ER.check_rows(og[0, :, h], res, S, np.arange(S), 2, seq)
+        print(f"  head {h}: rel-L2 {err:.2e}, row max {st['row_rel_l2_max']:.2e}, "
+              f"bit-identical {st['bit_identical']:.4f}", flush=True)
 
 
 def test_attn_repair_lowers_error(vc):

@@ -249,3 +249,57 @@ def test_exact_exp_diagnostic_is_closer_on_average():
     ea = np.linalg.norm(a["out_f32"] - ref) / np.linalg.norm(ref)
     eb = np.linalg.norm(b["out_f32"] - ref) / np.linalg.norm(ref)
     assert ea < 0.1 and eb < 0.1
+
+
+# --------------------------------------------------------------------------- #
+# per-score weights read back through a one-hot V
+# --------------------------------------------------------------------------- #
+
+def _log2_scores(res, S):
+    """Log2-domain scores the emulation sees: s_Q s_K (Qhat . Khat) / 8 (Q's
+    codes carry G = 8 fl(sm log2 e)), in fp64 (exact products and sums)."""
+    blk = np.arange(S) // 128
+    qd = oracle.e4m3_decode(res["q_codes"][:S]) * res["q_scale"][blk][:, None].astype(np.float64)
+    kd = oracle.e4m3_decode(res["k_codes"][:S]) * res["k_scale"][blk][:, None].astype(np.float64)
+    return (qd @ kd.T) / 8.0
+
+
+@pytest.mark.parametrize("S,window,seq,exact_exp", [(300, 2, False, False), (300, 0, False, False),
+                                                    (300, 2, True, False), (700, 2, False, False),
+                                                    (300, 2, False, True), (700, 1, True, True)])
+def test_emulation_weights_per_score(S, window, seq, exact_exp):
+    # V = one-hot on key tile j (key 128 j + d carries 1 in channel d): output
+    # channel d of every row is that key's final weight over the row sum,
+    # w_k 448 s_V / l.  Every weight of every row is compared with the
+    # definition applied score by score (tests/expcast_ref.py): the ExpCast
+    # code (or, with EXACT_EXP, torch's E4M3 cast of 2^(u+8)) at the running
+    # max after the key's tile, rescaled by the later increases
+    import expcast_ref as ER
+    D, sm = 128, 3 / math.sqrt(128)
+    nblk = (S + 127) // 128
+    q, k, _ = vcsynth.random_qkv(1, S, 1, D, seed=S + window)
+    qb, kb = vcsynth.bf16_bits(q), vcsynth.bf16_bits(k)
+    flags = (oracle.SEQUENTIAL if seq else 0) | (oracle.EXACT_EXP if exact_exp else 0)
+    n_rescale = 0
+    for j in range(nblk):
+        v = np.zeros((1, S, 1, D), np.float32)
+        nk = min(128, S - 128 * j)
+        v[0, 128 * j + np.arange(nk), 0, np.arange(nk)] = 1.0
+        res = oracle.pipeline_head(qb, kb, _bits(v), 0, 0, vsmooth=False, sm_scale=sm, window=window, flags=flags)
+        assert (res["v_codes"][np.arange(nk), 128 * j + np.arange(nk)] == 0x7E).all()  # 448
+        u = _log2_scores(res, S)
+        unit = 448.0 * float(res["v_scale"][0])
+        n_flip = 0
+        for i in range(S):
+            w, l, dw = ER.row_weights(u[i], S, ER.tile_visits(i // 128, nblk, window, seq), exact_exp=exact_exp,
+                                      eps=1e-4)
+            kk = 128 * j + np.arange(nk)
+            want = w[kk] / l * unit
+            tol = 2e-6 * want + (dw[kk] + w[kk] * dw.sum() / l) / l * unit
+            got = res["out_f32"][i, :nk].astype(np.float64)
+            assert np.all(np.abs(got - want) <= tol + 1e-30), (j, i)
+            assert np.all(got[nk:] == 0) if nk < D else True
+            n_flip += int((dw > 0).sum())
+        assert n_flip <= 1e-3 * S * S, n_flip  # keys within 1e-4 of a boundary are rare: the check is tight
+        n_rescale += int(res["stats"][:, 0].sum())
+    assert n_rescale > 0  # rows whose max rose after their first tile

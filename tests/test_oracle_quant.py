@@ -84,3 +84,66 @@ def test_q_prefactor_folds_scale_into_codes():
     ref = x.astype(np.float64) * G
     big = np.abs(ref) >= 2.0 ** -6 * float(s[0])
     assert np.all(np.abs(dec - ref)[big] <= np.abs(ref)[big] * 2.0 ** -4 + 1e-30)
+
+
+# --------------------------------------------------------------------------- #
+# per-head V quantiser ([VC] §3.1, X_q = s_X * Xhat; [OVC] "Scheduling around
+# ExpCast": one V scale per head, V stored key-contiguous)
+# --------------------------------------------------------------------------- #
+
+def _v_head(vals):
+    """quantize_v on one head: codes [D, S_pad], scale repeated over D."""
+    x = _bits(vals)
+    c, s = oracle.quantize_v(x[None, :, None, :])
+    return c[0, 0], s[0, 0], oracle.bf16_bits_to_f32(x).astype(np.float32)
+
+
+def _torch_e4m3(x64):
+    return torch.from_numpy(np.asarray(x64, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+@pytest.mark.parametrize("S,D,scale", [(300, 128, 2.5), (1, 64, 0.01), (129, 64, 4000.0), (1024, 128, 1e-3)])
+def test_v_head_scale_and_codes_match_torch(S, D, scale):
+    rng = np.random.default_rng(S + D)
+    c, s, x = _v_head(rng.standard_t(3, (S, D)).astype(np.float32) * np.float32(scale))
+    amax = np.float32(np.abs(x).max())             # over all S x D of the head
+    assert (s == np.float32(amax / np.float32(448))).all()   # fl32(amax / 448), one value per head
+    inv = np.float32(np.float32(448) / amax)       # fl32(448 / amax)
+    want = _torch_e4m3(x * inv)                    # fp32 product, then torch's RNE cast
+    S_pad = (S + 127) // 128 * 128
+    assert c.shape == (D, S_pad)
+    assert (c[:, :S] == want.T).all()              # key-contiguous: codes_t[d][token]
+    assert (c[:, S:] == 0).all()                   # pad keys are code 0
+
+
+def test_v_head_amax_is_over_all_channels():
+    # one channel carries a x100 outlier: the head's single scale follows it,
+    # so the other channels' codes are those of the outlier's scale (a
+    # per-channel amax would give each channel its own scale and far larger
+    # codes there)
+    rng = np.random.default_rng(3)
+    S, D = 500, 64
+    v = rng.standard_normal((S, D)).astype(np.float32)
+    v[17, 5] = 300.0
+    c, s, x = _v_head(v)
+    assert (s == s[0]).all() and s[0] == np.float32(np.float32(300.0) / np.float32(448))
+    inv = np.float32(np.float32(448) / np.float32(300.0))
+    assert (c[:, :S] == _torch_e4m3(x * inv).T).all()
+    per_channel = np.stack([_torch_e4m3(x[:, d] * np.float32(448 / np.abs(x[:, d]).max())) for d in range(D)])
+    assert (c[0, :S] != per_channel[0]).mean() > 0.9
+    assert c[5, 17] == 0x7E  # the outlier itself maps to 448
+
+
+def test_v_head_zero_scale_one():
+    c, s, _ = _v_head(np.zeros((200, 64), np.float32))
+    assert (s == 1.0).all() and (c == 0).all()
+
+
+def test_v_head_dequantised_within_half_step():
+    # s * decode(code) ~= x within E4M3's half-step where the scaled value is normal
+    rng = np.random.default_rng(11)
+    c, s, x = _v_head(rng.standard_normal((256, 128)).astype(np.float32) * 5)
+    dec = oracle.e4m3_decode(c[:, :256]).T * float(s[0])
+    ref = x.astype(np.float64)
+    big = np.abs(ref) >= 2.0 ** -6 * float(s[0])
+    assert np.all(np.abs(dec - ref)[big] <= np.abs(ref)[big] * 2.0 ** -4 * (1 + 1e-6))
