@@ -9,6 +9,7 @@ no GPU is present, calls fail loudly.
 
 Entry points (same names as the C ABI): vc_abi_version, vc_status_str,
 vc_quantize, vc_smooth_group_workspace_size, vc_smooth_group,
+vc_smooth_group_noalloc_bytes, vc_smooth_group_noalloc,
 vc_repair_workspace_size, vc_repair_prepare, vc_attn_fwd, vc_quantize4,
 vc_attn_fwd4, vc_pack_v_bf16, vc_attn_fwd_bf16, vc_expcast_codes; and vsmooth_schedule, the host-side rule
 for which denoising steps group, reuse or run plain, and repair_count, the
@@ -30,7 +31,7 @@ VC_OK = 0
 VC_ATTN_SEQUENTIAL = 1
 VC_GROUP_WARM_START = 1
 VC_GROUP_REUSE_PERM = 2
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 
 class VcError(RuntimeError):
@@ -95,6 +96,10 @@ def lib():
         L.vc_smooth_group_workspace_size.restype = sz
         L.vc_smooth_group.argtypes = [P] * 15 + [sz, P]
         L.vc_smooth_group.restype = i32
+        L.vc_smooth_group_noalloc_bytes.argtypes = [P, i32, ctypes.c_uint32]
+        L.vc_smooth_group_noalloc_bytes.restype = sz
+        L.vc_smooth_group_noalloc.argtypes = [P] * 15
+        L.vc_smooth_group_noalloc.restype = i32
         L.vc_repair_workspace_size.argtypes = [P]
         L.vc_repair_workspace_size.restype = sz
         L.vc_repair_prepare.argtypes = [P, P, P, P, i32, P, P, P, P, P, sz, P]
@@ -233,6 +238,24 @@ def vc_smooth_group(k, v, clusters: int, iters: int, seed: int, *, workspace=Non
     reuse_perm: int32 [B,H,S] permutation of an earlier call
     (VC_GROUP_REUSE_PERM): no k-means, no sort; only the gather, block means
     and residual codes run on k, v; centroids and labels are not produced."""
+    return _smooth_group(k, v, clusters, iters, seed, workspace, out, warm_start, reuse_perm, prep, noalloc=False)
+
+
+def vc_smooth_group_noalloc_bytes(B: int, H: int, S: int, D: int, clusters: int, prep_flags: int = 0) -> int:
+    sh = vc_shape(B, H, S, D)
+    return int(lib().vc_smooth_group_noalloc_bytes(ctypes.byref(sh), clusters, prep_flags))
+
+
+def vc_smooth_group_noalloc(k, v, clusters: int, iters: int, seed: int, *, out=None, warm_start=None,
+                            reuse_perm=None, prep=None):
+    """vc_smooth_group through the C entry point that allocates nothing: its
+    workspace (and the centring sums) live in the library's static per-GPU
+    scratch.  Outputs missing from `out` are allocated here, by the binding,
+    as torch tensors; pass them all for a call that allocates nothing."""
+    return _smooth_group(k, v, clusters, iters, seed, None, out, warm_start, reuse_perm, prep, noalloc=True)
+
+
+def _smooth_group(k, v, clusters, iters, seed, workspace, out, warm_start, reuse_perm, prep, noalloc):
     if warm_start is not None and reuse_perm is not None:
         raise ValueError("warm_start and reuse_perm exclude each other")
     sh = _shape_of(v)
@@ -264,18 +287,25 @@ def vc_smooth_group(k, v, clusters: int, iters: int, seed: int, *, workspace=Non
     o.setdefault("r_scale", torch.empty((B, H, D), dtype=torch.float32, device=dev))
     o.setdefault("mu_bf16", torch.empty((B, H, nb, D), dtype=torch.int16, device=dev))
     o.setdefault("mu_split", torch.empty((B, H, nb, D), dtype=torch.int32, device=dev))
+    p = vc_group_params(clusters, iters, seed, flags)
+    kd, vd = _bshd(k), _bshd(v)
+    outs = (_ptr(o.get("centroids")), _ptr(o.get("labels")), _ptr(o["perm"]), _ptr(o["k8"]), _ptr(o["k_scale"]),
+            _ptr(o["r8"]), _ptr(o["r_scale"]), _ptr(o["mu_bf16"]), _ptr(o["mu_split"]))
+    if noalloc:
+        pp = None
+        if prep and prep.get("flags"):
+            pp = vc_prep_params(int(prep["flags"]), _ptr(prep.get("rope_cos")), _ptr(prep.get("rope_sin")), None, 0)
+        st = lib().vc_smooth_group_noalloc(ctypes.byref(sh), ctypes.byref(kd), ctypes.byref(vd), ctypes.byref(p),
+                                           ctypes.byref(pp) if pp is not None else None, *outs, _stream())
+        _check(st, "vc_smooth_group_noalloc")
+        return o
     wsb = vc_smooth_group_workspace_size(B, H, S, D, clusters)
     if workspace is None:
         workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
-    p = vc_group_params(clusters, iters, seed, flags)
-    kd, vd = _bshd(k), _bshd(v)
     pp, _ws = _prep(prep, k, True)
     st = lib().vc_smooth_group(ctypes.byref(sh), ctypes.byref(kd), ctypes.byref(vd), ctypes.byref(p),
-                               ctypes.byref(pp) if pp is not None else None,
-                               _ptr(o.get("centroids")), _ptr(o.get("labels")), _ptr(o["perm"]), _ptr(o["k8"]),
-                               _ptr(o["k_scale"]), _ptr(o["r8"]), _ptr(o["r_scale"]), _ptr(o["mu_bf16"]),
-                               _ptr(o["mu_split"]), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                               _stream())
+                               ctypes.byref(pp) if pp is not None else None, *outs, _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream())
     _check(st, "vc_smooth_group")
     return o
 

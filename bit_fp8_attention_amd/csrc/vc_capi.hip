@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <mutex>
+
 #include "vc_launch.hpp"
 
 namespace {
@@ -56,6 +58,8 @@ __attribute__((visibility("default"))) const char* vc_status_str(int32_t s) {
     case VC_ERR_UNSUPPORTED: return "VC_ERR_UNSUPPORTED: parameter outside the supported set";
     case VC_ERR_WORKSPACE: return "VC_ERR_WORKSPACE: workspace too small";
     case VC_ERR_HIP: return "VC_ERR_HIP: a HIP launch failed";
+    case VC_ERR_SCRATCH:
+      return "VC_ERR_SCRATCH: the shape needs more than the library's static scratch (VC_GROUP_SCRATCH_BYTES)";
     default: return "unknown vc_status";
   }
 }
@@ -130,10 +134,15 @@ __attribute__((visibility("default"))) size_t vc_smooth_group_workspace_size(con
   return vc::group_workspace_bytes(*sh, clusters);
 }
 
-__attribute__((visibility("default"))) int32_t vc_smooth_group(
-    const vc_shape* sh, const vc_bshd* k, const vc_bshd* v, const vc_group_params* p, const vc_prep_params* prep,
-    float* centroids, int32_t* labels, int32_t* perm, uint8_t* k8, float* k_scale, uint8_t* r8, float* r_scale,
-    uint16_t* mu_bf16, uint32_t* mu_split, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by vc_smooth_group and vc_smooth_group_noalloc (everything
+// but the workspace).
+int32_t check_group(const vc_shape* sh, const vc_bshd* k, const vc_bshd* v, const vc_group_params* p,
+                    float* centroids, int32_t* labels, int32_t* perm, uint8_t* k8, float* k_scale, uint8_t* r8,
+                    float* r_scale, uint16_t* mu_bf16, uint32_t* mu_split) {
   int32_t e = check_shape(sh);
   if (e) return e;
   if ((e = check_bshd(k)) || (e = check_bshd(v))) return e;
@@ -141,26 +150,119 @@ __attribute__((visibility("default"))) int32_t vc_smooth_group(
   if (p->flags & ~(VC_GROUP_WARM_START | VC_GROUP_REUSE_PERM)) return VC_ERR_UNSUPPORTED;
   if ((p->flags & VC_GROUP_WARM_START) && (p->flags & VC_GROUP_REUSE_PERM)) return VC_ERR_UNSUPPORTED;
   const bool reuse = (p->flags & VC_GROUP_REUSE_PERM) != 0;
-  if ((!reuse && (!centroids || !labels)) || !perm || !k8 || !k_scale || !r8 || !r_scale || !mu_bf16 ||
-      !mu_split || !workspace)
+  if ((!reuse && (!centroids || !labels)) || !perm || !k8 || !k_scale || !r8 || !r_scale || !mu_bf16 || !mu_split)
     return VC_ERR_NULL;
   const int kmax = 8192 / sh->D;
   if (p->clusters < 1 || p->clusters > kmax || p->clusters > sh->S) return VC_ERR_UNSUPPORTED;
   if (p->iters < 1 || p->iters > 64) return VC_ERR_UNSUPPORTED;
-  if (!aligned16(k8) || !aligned16(r8) || ((uintptr_t)workspace & 255u)) return VC_ERR_ALIGN;
+  if (!aligned16(k8) || !aligned16(r8)) return VC_ERR_ALIGN;
   if (((uintptr_t)centroids | (uintptr_t)labels | (uintptr_t)perm | (uintptr_t)k_scale | (uintptr_t)r_scale |
        (uintptr_t)mu_split) & 3u)
     return VC_ERR_ALIGN;
   if (((uintptr_t)mu_bf16) & 1u) return VC_ERR_ALIGN;
-  if (workspace_bytes < vc::group_workspace_bytes(*sh, p->clusters)) return VC_ERR_WORKSPACE;
-  vc::PrepArgs pa;
-  if ((e = check_prep(sh, prep, true, &pa))) return e;
-  hipStream_t st = (hipStream_t)stream;
+  return VC_OK;
+}
+
+int32_t run_group(const vc_shape* sh, const vc_bshd* k, const vc_bshd* v, const vc_group_params* p,
+                  const vc_prep_params* prep, vc::PrepArgs pa, float* centroids, int32_t* labels, int32_t* perm,
+                  uint8_t* k8, float* k_scale, uint8_t* r8, float* r_scale, uint16_t* mu_bf16, uint32_t* mu_split,
+                  void* workspace, hipStream_t st) {
+  int32_t e;
   if ((pa.flags & VC_PREP_K_CENTER) &&
-      (e = hip_status(vc::launch_k_center_sums(*sh, as_bshd(k), pa, (unsigned long long*)prep->workspace, st))))
+      (e = hip_status(vc::launch_k_center_sums(*sh, as_bshd(k), pa, (unsigned long long*)pa.ksum, st))))
     return e;
   return hip_status(vc::launch_smooth_group(*sh, as_bshd(k), as_bshd(v), *p, centroids, labels, perm, k8, k_scale,
                                             r8, r_scale, mu_bf16, mu_split, workspace, pa, st));
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+// The no-allocation variant's scratch: one array per GPU the library runs
+// on, held until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device memory: its device address is taken once per
+// device with hipGetSymbolAddress and only that pointer reaches kernels.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[VC_GROUP_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of the current device's scratch, looked up on the first
+// call on that device.
+int32_t scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return VC_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return VC_ERR_HIP;
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return VC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+__attribute__((visibility("default"))) int32_t vc_smooth_group(
+    const vc_shape* sh, const vc_bshd* k, const vc_bshd* v, const vc_group_params* p, const vc_prep_params* prep,
+    float* centroids, int32_t* labels, int32_t* perm, uint8_t* k8, float* k_scale, uint8_t* r8, float* r_scale,
+    uint16_t* mu_bf16, uint32_t* mu_split, void* workspace, size_t workspace_bytes, void* stream) {
+  int32_t e = check_group(sh, k, v, p, centroids, labels, perm, k8, k_scale, r8, r_scale, mu_bf16, mu_split);
+  if (e) return e;
+  if (!workspace) return VC_ERR_NULL;
+  if ((uintptr_t)workspace & 255u) return VC_ERR_ALIGN;
+  if (workspace_bytes < vc::group_workspace_bytes(*sh, p->clusters)) return VC_ERR_WORKSPACE;
+  vc::PrepArgs pa;
+  if ((e = check_prep(sh, prep, true, &pa))) return e;
+  return run_group(sh, k, v, p, prep, pa, centroids, labels, perm, k8, k_scale, r8, r_scale, mu_bf16, mu_split,
+                   workspace, (hipStream_t)stream);
+}
+
+__attribute__((visibility("default"))) size_t vc_smooth_group_noalloc_bytes(const vc_shape* sh, int32_t clusters,
+                                                                            uint32_t prep_flags) {
+  if (check_shape(sh) || clusters < 1) return 0;
+  size_t n = round256(vc::group_workspace_bytes(*sh, clusters));
+  if (prep_flags & VC_PREP_K_CENTER) n += round256((size_t)sh->B * sh->H * sh->D * 8);
+  return n;
+}
+
+__attribute__((visibility("default"))) int32_t vc_smooth_group_noalloc(
+    const vc_shape* sh, const vc_bshd* k, const vc_bshd* v, const vc_group_params* p, const vc_prep_params* prep,
+    float* centroids, int32_t* labels, int32_t* perm, uint8_t* k8, float* k_scale, uint8_t* r8, float* r_scale,
+    uint16_t* mu_bf16, uint32_t* mu_split, void* stream) {
+  int32_t e = check_group(sh, k, v, p, centroids, labels, perm, k8, k_scale, r8, r_scale, mu_bf16, mu_split);
+  if (e) return e;
+  // the centring sums (VC_PREP_K_CENTER) follow the grouping workspace in
+  // the scratch; prep->workspace is not used
+  vc_prep_params pp{};
+  if (prep) {
+    pp = *prep;
+    pp.workspace = nullptr;
+    pp.workspace_bytes = 0;
+  }
+  const uint32_t pflags = prep ? prep->flags : 0u;
+  const size_t gbytes = round256(vc::group_workspace_bytes(*sh, p->clusters));
+  if (vc_smooth_group_noalloc_bytes(sh, p->clusters, pflags) > VC_GROUP_SCRATCH_BYTES) return VC_ERR_SCRATCH;
+  // validate the preparation first with a stand-in centring buffer: no HIP
+  // call happens before every argument is known to be good
+  if (pflags & VC_PREP_K_CENTER) {
+    pp.workspace = (void*)(uintptr_t)256;
+    pp.workspace_bytes = (size_t)sh->B * sh->H * sh->D * 8;
+  }
+  vc::PrepArgs pa;
+  if ((e = check_prep(sh, prep ? &pp : nullptr, true, &pa))) return e;
+  void* base = nullptr;
+  if ((e = scratch_on_current_device(&base))) return e;
+  if (pflags & VC_PREP_K_CENTER) pa.ksum = (const long long*)((unsigned char*)base + gbytes);
+  return run_group(sh, k, v, p, prep, pa, centroids, labels, perm, k8, k_scale, r8, r_scale, mu_bf16, mu_split,
+                   base, (hipStream_t)stream);
 }
 
 __attribute__((visibility("default"))) int32_t vc_attn_fwd(const vc_shape* sh, const vc_attn_params* p,

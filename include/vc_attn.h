@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define VC_ABI_VERSION 5
+#define VC_ABI_VERSION 6
 
 typedef enum vc_status {
   VC_OK = 0,
@@ -64,7 +64,8 @@ typedef enum vc_status {
   VC_ERR_ALIGN = 3,       /* pointer or stride not 16-byte aligned */
   VC_ERR_UNSUPPORTED = 4, /* parameter outside the supported set */
   VC_ERR_WORKSPACE = 5,   /* workspace too small */
-  VC_ERR_HIP = 6          /* a HIP launch failed */
+  VC_ERR_HIP = 6,         /* a HIP launch failed */
+  VC_ERR_SCRATCH = 7      /* the shape needs more than the static scratch holds */
 } vc_status;
 
 typedef struct vc_shape {
@@ -232,6 +233,37 @@ int32_t vc_smooth_group(const vc_shape* shape, const vc_bshd* k, const vc_bshd* 
                         const vc_prep_params* prep, float* centroids, int32_t* labels, int32_t* perm, uint8_t* k8,
                         float* k_scale, uint8_t* r8, float* r_scale, uint16_t* mu_bf16, uint32_t* mu_split,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * vc_smooth_group_noalloc -- vc_smooth_group without a workspace argument,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, semantics and outputs as vc_smooth_group (bit for bit), with the
+ * workspace (and, with VC_PREP_K_CENTER, the centring sums; prep->workspace
+ * is then not used) taken from a static device array of
+ * VC_GROUP_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends.  The array of the calling thread's current device
+ * is used, so `stream` must belong to that device; the call itself never
+ * allocates or frees.  Its device address is looked up once per device, on
+ * that device's first call (VC_ERR_HIP if the lookup fails).
+ * Limits: vc_smooth_group_noalloc_bytes(shape, clusters, prep flags) must be
+ * <= VC_GROUP_SCRATCH_BYTES (the Wan-shaped H = 40, S = 75600, D = 128 call
+ * with 64 clusters needs about 5.7 MB; H = 48, S = 84672 about 7.3 MB), else
+ * VC_ERR_SCRATCH and nothing is enqueued.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (different streams, or threads without ordering) race and give wrong
+ * results; calls ordered on one stream are safe.  Every part of the array a
+ * call reads is written by that call first.
+ */
+#define VC_GROUP_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* Scratch bytes vc_smooth_group_noalloc needs (0 for an invalid shape). */
+size_t vc_smooth_group_noalloc_bytes(const vc_shape* shape, int32_t clusters, uint32_t prep_flags);
+
+int32_t vc_smooth_group_noalloc(const vc_shape* shape, const vc_bshd* k, const vc_bshd* v, const vc_group_params* p,
+                                const vc_prep_params* prep, float* centroids, int32_t* labels, int32_t* perm,
+                                uint8_t* k8, float* k_scale, uint8_t* r8, float* r_scale, uint16_t* mu_bf16,
+                                uint32_t* mu_split, void* stream);
 
 /* ----------------------------------------------------------------------- */
 

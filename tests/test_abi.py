@@ -30,7 +30,8 @@ def test_header_declares_the_calls():
     names = _declared()
     for n in ["vc_abi_version", "vc_status_str", "vc_quantize", "vc_smooth_group_workspace_size",
               "vc_smooth_group", "vc_repair_workspace_size", "vc_repair_prepare", "vc_attn_fwd",
-              "vc_quantize4", "vc_attn_fwd4", "vc_pack_v_bf16", "vc_attn_fwd_bf16", "vc_expcast_codes"]:
+              "vc_quantize4", "vc_attn_fwd4", "vc_pack_v_bf16", "vc_attn_fwd_bf16", "vc_expcast_codes",
+              "vc_smooth_group_noalloc", "vc_smooth_group_noalloc_bytes"]:
         assert n in names
 
 
@@ -41,9 +42,9 @@ def test_library_exports_every_declared_symbol(vc):
 
 
 def test_abi_version_and_status_strings(vc):
-    assert vc.vc_abi_version() == vc.ABI_VERSION == 5
+    assert vc.vc_abi_version() == vc.ABI_VERSION == 6
     assert vc.vc_status_str(0) == "VC_OK"
-    for s in range(1, 7):
+    for s in range(1, 8):
         assert vc.vc_status_str(s).startswith("VC_ERR_")
     assert vc.vc_status_str(99) == "unknown vc_status"
 
@@ -124,6 +125,39 @@ def test_smooth_group_validation(vc):
     assert L.vc_smooth_group(ctypes.byref(small), ctypes.byref(ok), ctypes.byref(ok),
                              ctypes.byref(m.vc_group_params(11, 1, 0, 0)), None, *[P(FAKE)] * 9, P(FAKE), ws,
                              st) == 4
+
+
+def test_smooth_group_noalloc_validation(vc):
+    # the allocation-free grouping: the same argument checks, and shapes whose
+    # scratch need exceeds the static array are refused with VC_ERR_SCRATCH;
+    # every case here returns before any HIP call
+    L, m = vc.lib(), vc
+    P = ctypes.c_void_p
+    st = ctypes.c_void_p(0)
+    ok = m.vc_bshd(FAKE, 256 * 2 * 128, 2 * 128, 128)
+    sh = _shape()
+
+    def call(shape, p, prep=None, ptrs=None):
+        ptrs = [FAKE] * 9 if ptrs is None else ptrs
+        return L.vc_smooth_group_noalloc(ctypes.byref(shape), ctypes.byref(ok), ctypes.byref(ok), ctypes.byref(p),
+                                         ctypes.byref(prep) if prep is not None else None, *[P(x) for x in ptrs], st)
+    assert call(sh, m.vc_group_params(0, 4, 0, 0)) == 4                      # k < 1
+    assert call(sh, m.vc_group_params(64, 0, 0, 0)) == 4                     # iters < 1
+    assert call(sh, m.vc_group_params(64, 4, 0, 3)) == 4                     # exclusive flags
+    assert call(sh, m.vc_group_params(64, 4, 0, 2), ptrs=[FAKE, FAKE, None] + [FAKE] * 6) == 1
+    assert call(m.vc_shape(1, 2, 256, 96), m.vc_group_params(8, 4, 0, 0)) == 2
+    # the headline shapes fit the static scratch; 200 heads of 84672 tokens do not
+    need = m.vc_smooth_group_noalloc_bytes
+    lim = 16 << 20
+    assert 0 < need(1, 40, 75600, 128, 64) <= lim and 0 < need(1, 48, 84672, 128, 64) <= lim
+    assert need(1, 48, 84672, 128, 64, m.VC_PREP_K_CENTER) == need(1, 48, 84672, 128, 64) + 48 * 128 * 8
+    big = m.vc_shape(1, 200, 84672, 128)
+    assert need(1, 200, 84672, 128, 64) > lim
+    assert call(big, m.vc_group_params(64, 4, 0, 0)) == 7                    # VC_ERR_SCRATCH
+    assert vc.vc_status_str(7).startswith("VC_ERR_SCRATCH")
+    # the preparation is validated before the scratch is touched (RoPE without tables)
+    pp = m.vc_prep_params(m.VC_PREP_ROPE, None, None, None, 0)
+    assert call(sh, m.vc_group_params(64, 4, 0, 0), prep=pp) == 1
 
 
 def test_prep_validation(vc):
