@@ -18,6 +18,8 @@ in-house BF16 baseline on the same kernel skeleton gives the speedup.
 Usage: python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--workload wan]
        python bench.py --traffic-job          (under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)
        python bench.py --traffic-summary FETCH_DIR WRITE_DIR OUT_JSON COMMAND
+       python bench.py --prep-job [--workload minimax]   (the preparation passes, for --pmc runs)
+       python bench.py --counter-summary OUT_MD TITLE DIR [DIR ...]
 """
 from __future__ import annotations
 
@@ -138,6 +140,100 @@ def traffic_summary(fetch_dir, write_dir, out_path, command):
     with open(out_path, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
+
+
+def prep_job(w):
+    """The preparation passes once each on the workload: vc_quantize of Q, K
+    and V, a cold vc_smooth_group (k-means from the Forgy draw), a
+    vc_smooth_group reusing its permutation, then one plain device copy of
+    COPY_BYTES as the very last dispatch (the FETCH_SIZE / WRITE_SIZE
+    calibration of --counter-summary)."""
+    import torch
+
+    import bit_fp8_attention_amd as vc
+    import vcsynth
+    q, k, v = vcsynth.make_qkv(w.name, device="cuda")
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    vc.vc_quantize(q, k, v, sm_scale=w.sm_scale)
+    g = vc.vc_smooth_group(k, v, w.clusters or 64, w.iters or 4, w.seed)
+    vc.vc_smooth_group(k, v, w.clusters or 64, w.iters or 4, w.seed, reuse_perm=g["perm"])
+    b.copy_(a)
+    torch.cuda.synchronize()
+    log("prep job done")
+
+
+def counter_summary(out_path, title, dirs, command):
+    """Per-kernel table of every counter found under the rocprofv3 --pmc
+    output directories: value per dispatch (averaged over the kernel's
+    dispatches).  FETCH_SIZE and WRITE_SIZE (KiB per dispatch) also appear
+    as bytes, scaled by COPY_BYTES / (the counter's reading for the last
+    dispatch of the run, the calibration copy)."""
+    import csv
+    import glob
+    per = {}    # kernel -> counter -> [values]
+    calib = {}  # counter -> factor
+    traces = [d[len("trace="):] for d in dirs if d.startswith("trace=")]
+    dirs = [d for d in dirs if not d.startswith("trace=")]
+    for d in dirs:
+        by_disp = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    key = (int(r["Dispatch_Id"]), r["Counter_Name"])
+                    name = r["Kernel_Name"]
+                    prev = by_disp.get(key, (name, 0.0))
+                    by_disp[key] = (name, prev[1] + float(r["Counter_Value"]))
+        if not by_disp:
+            raise SystemExit(f"no counter rows under {d}")
+        last = max(k[0] for k in by_disp)
+        for (did, ctr), (name, val) in by_disp.items():
+            if did == last and ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+                calib[ctr] = COPY_BYTES / (val * 1024.0)
+                continue
+            if did == last or "vc::" not in name:  # the library's kernels only
+                continue
+            short = name.replace("vc::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+            per.setdefault(short, {}).setdefault(ctr, []).append(val)
+    ctrs = sorted({c for v in per.values() for c in v})
+    lines = [f"# {title}", "", "Command (from the repository root copied to the GPU host; OUT = gpurun_out):", "",
+             "    " + command.replace("\n", "\n    "), "",
+             "Library kernels only.  Value per dispatch, averaged over the kernel's dispatches; calls = dispatches "
+             "seen."]
+    if calib:
+        lines.append("FETCH_SIZE / WRITE_SIZE as bytes: each KiB counter times " +
+                     ", ".join(f"{c} {f:.3f}" for c, f in sorted(calib.items())) +
+                     f" (the {COPY_BYTES}-byte calibration copy, last dispatch).")
+    lines += ["", "| kernel | calls | " + " | ".join(ctrs) + " |", "|---|---|" + "---|" * len(ctrs)]
+    for kname in sorted(per):
+        row = per[kname]
+        n = max(len(v) for v in row.values())
+        cells = []
+        for c in ctrs:
+            if c not in row:
+                cells.append("")
+                continue
+            m = sum(row[c]) / len(row[c])
+            if c in calib:
+                cells.append(f"{m * 1024.0 * calib[c] / 1e9:.4f} GB")
+            else:
+                cells.append(f"{m:.4g}")
+        lines.append(f"| `{kname}` | {n} | " + " | ".join(cells) + " |")
+    for d in traces:  # kernel-trace runs (--kernel-trace --stats): durations
+        for f in glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True):
+            lines += ["", "Kernel durations (--kernel-trace --stats of the same job), microseconds:", "",
+                      "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if "vc::" not in r["Name"]:
+                        continue
+                    short = r["Name"].replace("vc::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+                    lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                                 f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def cpu_baseline(w, q, k, v, target_s=12.0):
@@ -305,9 +401,20 @@ def main():
                     help="one attention launch + calibration copy, for rocprofv3 --pmc runs")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON", "COMMAND"),
                     help="write the per-launch traffic record from the two counter runs")
+    ap.add_argument("--prep-job", action="store_true",
+                    help="the preparation passes once + calibration copy, for rocprofv3 --pmc runs")
+    ap.add_argument("--counter-summary", nargs="+", metavar="ARG",
+                    help="OUT_MD TITLE COMMAND DIR [DIR ...]: per-kernel counter table of --pmc runs "
+                         "(a DIR given as trace=DIR is a --kernel-trace --stats run: durations)")
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary)
+        return
+    if args.counter_summary:
+        a = args.counter_summary
+        if len(a) < 4:
+            raise SystemExit("--counter-summary OUT_MD TITLE COMMAND DIR [DIR ...]")
+        counter_summary(a[0], a[1], a[3:], a[2])
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -324,6 +431,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.traffic_job:
         traffic_job(w)
+        return
+    if args.prep_job:
+        prep_job(w)
         return
     t0 = time.perf_counter()
     q, k, v = vcsynth.make_qkv(w.name, device=dev)
