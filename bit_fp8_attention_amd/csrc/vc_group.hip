@@ -156,61 +156,82 @@ template <int D>
 __global__ __launch_bounds__(256) void group_init(const uint16_t* __restrict__ v, int64_t sB, int64_t sS, int64_t sH,
                                                   int S, int H, int k, uint64_t seed, int warm,
                                                   float* __restrict__ cent, GroupWs ws) {
-  __shared__ int mpos[512], mval[512];
   __shared__ int idx[256];
+  __shared__ float cl[8192];  // the k x D centroids (k D <= 8192)
   const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const int64_t bh = (int64_t)b * H + h;
-  if (warm) {
-    // warm start: the caller's centroids are the first iterate
-    float* cb = cent + bh * k * D;
-    for (int e = t; e < k * D; e += 256) ws.sums[bh * k * D + e] = 0;
-    for (int e = t; e < k; e += 256) ws.counts[bh * k + e] = 0;
-    for (int e = t; e < D; e += 256) ws.r_amax[bh * D + e] = 0u;
-    for (int c = t; c < k; c += 256) {
-      float n2 = 0.0f;
-      for (int d = 0; d < D; ++d) n2 = __builtin_fmaf(cb[c * D + d], cb[c * D + d], n2);
-      ws.norms[bh * k + c] = n2;
-    }
-    return;
-  }
-  if (t == 0) {
-    // partial Fisher-Yates over the identity [0, S), the touched positions
-    // kept in a small map (position -> value)
-    int n = 0;
-    uint64_t st = seed + 0x9E3779B97F4A7C15ull * (uint64_t)(1 + bh);
-    for (int i = 0; i < k; ++i) {
-      uint64_t r = splitmix64_next(st);
-      int j = i + (int)(((r >> 32) * (uint64_t)(unsigned)(S - i)) >> 32);
-      int ei = -1, ej = -1;
-      for (int e = 0; e < n; ++e) {
-        if (mpos[e] == i) ei = e;
-        if (mpos[e] == j) ej = e;
-      }
-      int ai = ei >= 0 ? mval[ei] : i;
-      int aj = ej >= 0 ? mval[ej] : j;
-      if (ei < 0) { mpos[n] = i; ei = n++; }
-      if (ej < 0 && j != i) { mpos[n] = j; ej = n++; }
-      mval[ei] = aj;
-      if (j != i) mval[ej] = ai;
-      idx[i] = aj;
-    }
-  }
-  __syncthreads();
-  const uint16_t* vb = v + b * sB + h * sH;
   float* cb = cent + bh * k * D;
-  for (int e = t; e < k * D; e += 256) {
-    int c = e / D, d = e % D;
-    cb[e] = bf16_to_f32(vb[(int64_t)idx[c] * sS + d]);
-  }
   for (int e = t; e < k * D; e += 256) ws.sums[bh * k * D + e] = 0;
   for (int e = t; e < k; e += 256) ws.counts[bh * k + e] = 0;
   for (int e = t; e < D; e += 256) ws.r_amax[bh * D + e] = 0u;
+  if (warm) {
+    // warm start: the caller's centroids are the first iterate
+    for (int e = t; e < k * D; e += 256) cl[e] = cb[e];
+  } else {
+    if (t < 64) {
+      // partial Fisher-Yates over the identity [0, S), the touched positions
+      // kept in a small map (position -> value) spread over wave 0's lanes:
+      // entry e in lane e % 64, slot e / 64 (at most 2 k <= 256 entries);
+      // each lookup is one compare per slot and a ballot
+      constexpr int NS = 4;
+      int pos[NS], val[NS];
+#pragma unroll
+      for (int m = 0; m < NS; ++m) pos[m] = val[m] = -1;
+      const int lane = t;
+      int n = 0;
+      uint64_t st = seed + 0x9E3779B97F4A7C15ull * (uint64_t)(1 + bh);
+      for (int i = 0; i < k; ++i) {
+        const uint64_t r = splitmix64_next(st);
+        const int j = i + (int)(((r >> 32) * (uint64_t)(unsigned)(S - i)) >> 32);
+        int ei = -1, ej = -1, ai = i, aj = j;
+#pragma unroll
+        for (int m = 0; m < NS; ++m) {
+          const unsigned long long bi = __ballot(pos[m] == i), bj = __ballot(pos[m] == j);
+          if (bi) {
+            const int L = __builtin_ctzll(bi);
+            ei = 64 * m + L;
+            ai = __shfl(val[m], L);
+          }
+          if (bj) {
+            const int L = __builtin_ctzll(bj);
+            ej = 64 * m + L;
+            aj = __shfl(val[m], L);
+          }
+        }
+        if (ei < 0) {
+          ei = n++;
+#pragma unroll
+          for (int m = 0; m < NS; ++m)
+            if (ei == 64 * m + lane) pos[m] = i;
+        }
+        if (ej < 0 && j != i) {
+          ej = n++;
+#pragma unroll
+          for (int m = 0; m < NS; ++m)
+            if (ej == 64 * m + lane) pos[m] = j;
+        }
+#pragma unroll
+        for (int m = 0; m < NS; ++m) {
+          if (ei == 64 * m + lane) val[m] = aj;
+          if (j != i && ej == 64 * m + lane) val[m] = ai;
+        }
+        if (lane == 0) idx[i] = aj;
+      }
+    }
+    __syncthreads();
+    const uint16_t* vb = v + b * sB + h * sH;
+    for (int e = t; e < k * D; e += 256) {
+      const int c = e / D, d = e % D;
+      const float x = bf16_to_f32(vb[(int64_t)idx[c] * sS + d]);
+      cb[e] = x;
+      cl[e] = x;
+    }
+  }
+  __syncthreads();
+  // norms: one fmaf chain per centroid over d = 0..D-1, from LDS
   for (int c = t; c < k; c += 256) {
     float n2 = 0.0f;
-    for (int d = 0; d < D; ++d) {
-      float x = bf16_to_f32(vb[(int64_t)idx[c] * sS + d]);
-      n2 = __builtin_fmaf(x, x, n2);
-    }
+    for (int d = 0; d < D; ++d) n2 = __builtin_fmaf(cl[c * D + d], cl[c * D + d], n2);
     ws.norms[bh * k + c] = n2;
   }
 }
@@ -245,7 +266,8 @@ __global__ __launch_bounds__(256) void amax_reset(int D, GroupWs ws) {
 // Work: 512 threads, kAssignTokens tokens per workgroup; wave w takes 16 TBW
 // tokens per step; lane (g, lr) loads channels 32 kc + 8 g .. + 7 of token
 // 16 tb + lr (the B operand) and, after the products, holds centroids
-// 16 cb + 4 g + v of that token.
+// 16 cb + 4 g + v of that token.  Labels go to LDS; once all are final, the
+// member sums are taken by walking runs of tokens (below).
 template <int D, int NCB>
 __global__ __launch_bounds__(512) void kmeans_assign_mx(const uint16_t* __restrict__ v, int64_t sB, int64_t sS,
                                                         int64_t sH, int S, int H, int k,
@@ -262,13 +284,16 @@ __global__ __launch_bounds__(512) void kmeans_assign_mx(const uint16_t* __restri
   __shared__ unsigned long long lsum[KP * LD];
   __shared__ int lcnt[KP];
   __shared__ __attribute__((aligned(16))) float lnrm[KP], lbc[KP];
+  __shared__ __attribute__((aligned(16))) unsigned char lbl[kAssignTokens];  // every token's label (k <= 255)
   __shared__ unsigned short otok[kAssignTokens];  // open tokens (offset in the workgroup's range)
   __shared__ u32 omask[kAssignTokens * NW];       // and their candidate sets
   __shared__ unsigned lmisc[2];                   // max |c|^2 (bits), open-list length
-  const int h = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  // heads vary fastest over the grid: the workgroups running at one time
+  // read whole [H, D] stripes of the token-major value tensor
+  const int h = blockIdx.x, b = blockIdx.z, t = threadIdx.x;
   const int l = t & 63, lr = l & 15, g = l >> 4, w = t >> 6;
   const int64_t bh = (int64_t)b * H + h;
-  const int base = blockIdx.x * kAssignTokens;
+  const int base = blockIdx.y * kAssignTokens;
   const float* __restrict__ cb = cent + bh * k * D;
   for (int e = t; e < KP * LD; e += 512) lsum[e] = 0ull;
   for (int c = t; c < KP; c += 512) {
@@ -336,27 +361,19 @@ __global__ __launch_bounds__(512) void kmeans_assign_mx(const uint16_t* __restri
             acc[cbk][tb] = mfma_bf16(af, __builtin_bit_cast(v8bf, xw[tb][kc]),
                                      (kc == 0 && part == 0) ? zero4 : acc[cbk][tb]);
         }
-    int lab[TBW];
-    u32 mlane = 0;  // max |x| bits over the lane's TBW tokens
 #pragma unroll
     for (int tb = 0; tb < TBW; ++tb) {
-      // |x|_inf (exact: packed 16-bit maxima of the magnitude bits) and |x|^2
-      typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-      u16x2 mm = {0, 0};
+      // |x|^2
       float x2 = 0.f;
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
         const u32 wd[4] = {xw[tb][kc].x, xw[tb][kc].y, xw[tb][kc].z, xw[tb][kc].w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          mm = __builtin_elementwise_max(mm, __builtin_bit_cast(u16x2, wd[q] & 0x7fff7fffu));
           x2 = __builtin_fmaf(bf16_lo(wd[q]), bf16_lo(wd[q]), x2);
           x2 = __builtin_fmaf(bf16_hi(wd[q]), bf16_hi(wd[q]), x2);
         }
       }
-      u32 m = max((u32)mm[0], (u32)mm[1]);
-      m = over_groups(m, [](u32 a, u32 c) { return max(a, c); });
-      mlane = max(mlane, m);
       x2 = __uint_as_float(over_groups(__float_as_uint(x2), [](u32 x, u32 y) {
         return __float_as_uint(__uint_as_float(x) + __uint_as_float(y));
       }));
@@ -399,71 +416,15 @@ __global__ __launch_bounds__(512) void kmeans_assign_mx(const uint16_t* __restri
         if (cm[q]) idx = 32 * q + __builtin_ctz(cm[q]);
       const int tok = t0 + 16 * tb + lr;
       const bool decided = cnt == 1 && idx < k;
-      lab[tb] = (tok < S && decided) ? idx : -1;
       if (tok < S && g == 0) {
         if (decided) {
           labels[bh * S + tok] = idx;
-          atomicAdd(&lcnt[idx], 1);
+          lbl[tok - base] = (unsigned char)idx;
         } else {
           const unsigned slot = atomicAdd(&lmisc[1], 1u);
           otok[slot] = (unsigned short)(tok - base);
 #pragma unroll
           for (int q = 0; q < NW; ++q) omask[slot * NW + q] = cm[q];
-        }
-      }
-    }
-    // member sums of the decided tokens: the lane's 32 channels of each.
-    // The lane's TBW tokens (16 apart) usually share a cluster: then each
-    // channel's TBW fixed-point values are added in registers first (int32 is
-    // exact for |x| < 32: |fx24| < 2^29, TBW <= 4) and go out as one atomic.
-    bool same = lab[0] >= 0;
-#pragma unroll
-    for (int tb = 1; tb < TBW; ++tb) same = same && lab[tb] == lab[0];
-    if (same && bf16_to_f32((uint16_t)mlane) < 32.0f) {
-      unsigned long long* ls = lsum + lab[0] * LD + 8 * g;
-#pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          int s0 = 0, s1 = 0;
-#pragma unroll
-          for (int tb = 0; tb < TBW; ++tb) {
-            const u32 wd = q == 0 ? xw[tb][kc].x : q == 1 ? xw[tb][kc].y : q == 2 ? xw[tb][kc].z : xw[tb][kc].w;
-            s0 += (int)fx24_small(wd & 0xffffu);
-            s1 += (int)fx24_small(wd >> 16);
-          }
-          atomicAdd(&ls[32 * kc + 2 * q], (unsigned long long)(long long)s0);
-          atomicAdd(&ls[32 * kc + 2 * q + 1], (unsigned long long)(long long)s1);
-        }
-      }
-    } else if (bf16_to_f32((uint16_t)mlane) < 128.0f) {
-#pragma unroll
-      for (int tb = 0; tb < TBW; ++tb) {
-        if (lab[tb] < 0) continue;
-        unsigned long long* ls = lsum + lab[tb] * LD + 8 * g;
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
-          const u32 wd[4] = {xw[tb][kc].x, xw[tb][kc].y, xw[tb][kc].z, xw[tb][kc].w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            atomicAdd(&ls[32 * kc + 2 * q], (unsigned long long)fx24_small(wd[q] & 0xffffu));
-            atomicAdd(&ls[32 * kc + 2 * q + 1], (unsigned long long)fx24_small(wd[q] >> 16));
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int tb = 0; tb < TBW; ++tb) {
-        if (lab[tb] < 0) continue;
-        unsigned long long* ls = lsum + lab[tb] * LD + 8 * g;
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
-          const u32 wd[4] = {xw[tb][kc].x, xw[tb][kc].y, xw[tb][kc].z, xw[tb][kc].w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            atomicAdd(&ls[32 * kc + 2 * q], (unsigned long long)fx24(bf16_lo(wd[q])));
-            atomicAdd(&ls[32 * kc + 2 * q + 1], (unsigned long long)fx24(bf16_hi(wd[q])));
-          }
         }
       }
     }
@@ -497,15 +458,94 @@ __global__ __launch_bounds__(512) void kmeans_assign_mx(const uint16_t* __restri
     }
     if (best < 0) best = exact_label<D>(x, cb, nb, k);  // an empty set cannot happen; stay exact regardless
     labels[bh * S + tok] = best;
-    atomicAdd(&lcnt[best], 1);
-    unsigned long long* ls = lsum + best * LD;
+    lbl[tok - base] = (unsigned char)best;
+  }
+  __syncthreads();
+  // member sums and counts.  Every label is known now: each group of D / 8
+  // lanes walks its own run of consecutive tokens, lane c adding channels
+  // 8 c .. 8 c + 7 of each token into 64-bit registers, and adds them to
+  // the cluster's LDS sums only where the label changes (tokens in raster
+  // order come in long runs of one label).  Rows come 16 at a time, each
+  // batch added while the next one loads.  In an LDS sum row, channel
+  // 8 c + e sits at position 8 c + ((e + c / 2) & 7): the 16 lanes of one
+  // flush instruction then hit 16 distinct bank pairs.  Fixed-point sums are
+  // exact, so the order does not matter.
+  {
+    constexpr int LPT = D / 8;                       // lanes per token
+    constexpr int GPW = 64 / LPT;                    // token groups per wave
+    constexpr int SPAN = kAssignTokens / (8 * GPW);  // tokens per group (a multiple of 16)
+    constexpr int PF = 16;                           // rows per batch
+    const int grp = l / LPT, c = l % LPT;
+    const int r0 = base + (w * GPW + grp) * SPAN;
+    const int r1 = min(r0 + SPAN, S);
+    int cur = -1, run = 0;
+    long long acc[8];
 #pragma unroll
-    for (int d = 0; d < D; ++d) atomicAdd(&ls[d], (unsigned long long)fx24(x[d]));
+    for (int e = 0; e < 8; ++e) acc[e] = 0;
+    auto flush = [&]() {
+      unsigned long long* ls = lsum + cur * LD + 8 * c;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        atomicAdd(&ls[(e + (c >> 1)) & 7], (unsigned long long)acc[e]);
+        acc[e] = 0;
+      }
+      if (c == 0) atomicAdd(&lcnt[cur], run);
+      run = 0;
+    };
+    // a batch: PF rows (row t0 + i clamped into the run, so every load is of
+    // a real token) and their PF label bytes (one 16-byte LDS read)
+    const uint16_t* rbase = vb + 8 * c;
+    auto load = [&](uint4 (&buf)[PF], uint4& lab, int t0) {
+#pragma unroll
+      for (int i = 0; i < PF; ++i) buf[i] = *(const uint4*)(rbase + (int64_t)min(t0 + i, r1 - 1) * sS);
+      lab = *(const uint4*)&lbl[t0 - base];
+    };
+    auto process = [&](const uint4 (&cw)[PF], const uint4& clab, int t0) {
+      const u32 lw[4] = {clab.x, clab.y, clab.z, clab.w};
+#pragma unroll
+      for (int i = 0; i < PF; ++i) {
+        if (t0 + i >= r1) continue;  // (no break: every index stays a constant)
+        const int L = (int)((lw[i >> 2] >> (8 * (i & 3))) & 0xffu);
+        if (L != cur) {
+          if (cur >= 0) flush();
+          cur = L;
+        }
+        const u32 wd[4] = {cw[i].x, cw[i].y, cw[i].z, cw[i].w};
+        u32 mx = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) mx = max(mx, max(wd[q] & 0x7fffu, (wd[q] >> 16) & 0x7fffu));
+        if (mx < 0x4300u) {  // |x| < 128: the exponent shortcut
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[2 * q] += fx24_small(wd[q] & 0xffffu);
+            acc[2 * q + 1] += fx24_small(wd[q] >> 16);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[2 * q] += fx24(bf16_lo(wd[q]));
+            acc[2 * q + 1] += fx24(bf16_hi(wd[q]));
+          }
+        }
+        ++run;
+      }
+    };
+    uint4 wa[PF], wb[PF], la, lb;
+    if (r0 < r1) load(wa, la, r0);
+    for (int t0 = r0; t0 < r1; t0 += 2 * PF) {
+      if (t0 + PF < r1) load(wb, lb, t0 + PF);
+      process(wa, la, t0);
+      if (t0 + 2 * PF < r1) load(wa, la, t0 + 2 * PF);
+      if (t0 + PF < r1) process(wb, lb, t0 + PF);
+    }
+    if (cur >= 0) flush();
   }
   __syncthreads();
   unsigned long long* gs = (unsigned long long*)ws.sums + bh * k * D;
-  for (int e = t; e < k * D; e += 512)
-    if (lcnt[e / D] > 0) atomicAdd(&gs[e], lsum[(e / D) * LD + e % D]);
+  for (int e = t; e < k * D; e += 512) {
+    const int ch = e % D, cc = ch >> 3;  // channel 8 cc + (ch & 7) sits at 8 cc + ((ch + cc / 2) & 7)
+    if (lcnt[e / D] > 0) atomicAdd(&gs[e], lsum[(e / D) * LD + 8 * cc + (((ch & 7) + (cc >> 1)) & 7)]);
+  }
   for (int e = t; e < k; e += 512)
     if (lcnt[e] > 0) atomicAdd((unsigned long long*)&ws.counts[bh * k + e], (unsigned long long)lcnt[e]);
 }
@@ -513,6 +553,7 @@ __global__ __launch_bounds__(512) void kmeans_assign_mx(const uint16_t* __restri
 // Member means (empty clusters keep their centroid), norms, reset sums.
 template <int D>
 __global__ __launch_bounds__(256) void kmeans_update(int k, float* __restrict__ cent, GroupWs ws) {
+  __shared__ float cl[8192];  // the k x D centroids (k D <= 8192)
   const int64_t bh = blockIdx.x;
   const int t = threadIdx.x;
   float* cb = cent + bh * k * D;
@@ -520,13 +561,15 @@ __global__ __launch_bounds__(256) void kmeans_update(int k, float* __restrict__ 
   const long long* nb = ws.counts + bh * k;
   for (int e = t; e < k * D; e += 256) {
     long long n = nb[e / D];
-    if (n > 0) cb[e] = fx24_mean(sb[e], n);
+    const float c = n > 0 ? fx24_mean(sb[e], n) : cb[e];
+    cb[e] = c;
+    cl[e] = c;
     sb[e] = 0;
   }
   __syncthreads();
   for (int c = t; c < k; c += 256) {
     float n2 = 0.0f;
-    for (int d = 0; d < D; ++d) n2 = __builtin_fmaf(cb[c * D + d], cb[c * D + d], n2);
+    for (int d = 0; d < D; ++d) n2 = __builtin_fmaf(cl[c * D + d], cl[c * D + d], n2);
     ws.norms[bh * k + c] = n2;
   }
   __syncthreads();
@@ -816,7 +859,7 @@ hipError_t launch_group_t(const vc_shape& sh, Bshd k, Bshd v, const vc_group_par
   } else {
     group_init<D><<<dim3(H, B), 256, 0, st>>>(v.p, v.sB, v.sS, v.sH, S, H, kc, p.seed,
                                               (p.flags & VC_GROUP_WARM_START) ? 1 : 0, cent, ws);
-    const dim3 ga((S + kAssignTokens - 1) / kAssignTokens, H, B);
+    const dim3 ga(H, (S + kAssignTokens - 1) / kAssignTokens, B);
     const int ncb = kc <= 16 ? 1 : kc <= 32 ? 2 : kc <= 64 ? 4 : 8;  // k <= 8192 / D
     auto assign = ncb == 1 ? kmeans_assign_mx<D, 1> : ncb == 2 ? kmeans_assign_mx<D, 2>
                   : ncb == 4 ? kmeans_assign_mx<D, 4> : kmeans_assign_mx<D, (D == 64 ? 8 : 4)>;
