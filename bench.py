@@ -279,124 +279,172 @@ def cpu_baseline(w, q, k, v, target_s=12.0):
     }
 
 
-def repair_measurement(vc, w, q, k, v, flops, rho=0.005, n=3):
-    """Open-VC's V residual repair on the same inputs, plain path: time of
-    vc_repair_prepare for R = ceil(rho S) rows per head, and of vc_attn_fwd
-    without and with the repair tiles (HIP events, mean of n launches)."""
-    import torch
-
-    qz = vc.vc_quantize(q, k, v, sm_scale=w.sm_scale)
-    R = vc.repair_count(w.S, rho)
-    ws = torch.empty(vc.vc_repair_workspace_size(w.B, w.H, w.S, w.D), dtype=torch.uint8, device=q.device)
-    rp = vc.vc_repair_prepare(k, v, R, workspace=ws)
-    o = torch.empty_like(q)
-    args = (qz["q8"], qz["q_scale"], qz["k8"], qz["k_scale"], qz["v8"], qz["v_scale"], None)
-
-    def timed(fn):
-        fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(n):
-            fn()
-        e1.record()
-        e1.synchronize()
-        return e0.elapsed_time(e1) / n
-
-    t_prep = timed(lambda: vc.vc_repair_prepare(k, v, R, workspace=ws, out=rp))
-    t_plain = timed(lambda: vc.vc_attn_fwd(*args, S=w.S, out=o))
-    t_rep = timed(lambda: vc.vc_attn_fwd(*args, S=w.S, out=o, repair=rp))
-    del qz, rp, ws, o
-    return {"rho": rho, "rows_per_head": R, "prepare_ms": round(t_prep, 3), "attn_plain_ms": round(t_plain, 3),
-            "attn_with_repair_ms": round(t_rep, 3),
-            "tflops_with_repair": round(flops / (t_rep * 1e-3) / 1e12, 1)}
-
-
 FP4_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 matrix-core peak
 HBM_PEAK_GBPS = 8000.0
+ROUNDS = 31                # launches per leg in the interleaved sampling (median of these)
 
 
-def prep_measurement(vc, w, q, k, v, qz, g, ws, clusters, iters, attn_ms, ms_q, ms_g, n=3):
-    """The preparation passes against HBM bandwidth (algorithmic bytes over
-    their timed mean), and the grouping cost amortised over a 50-step
-    schedule ([VC] §3.4 and App. A: grouping on the first ceil(50 / 4) = 13
-    steps, the permutation recomputed at steps 0, 4, 8, 12 and reused in
-    between), as a share of one attention call."""
+class ClockSampler:
+    """The GPU's shader clock (pp_dpm_sclk, the level marked '*') and board
+    power (hwmon power1_input, else power1_average) sampled every few
+    milliseconds on a host thread while a leg runs; each sample is tagged
+    with the leg that was running when it was taken."""
+
+    def __init__(self, torch, period=0.004):
+        import glob
+        import threading
+        p = torch.cuda.get_device_properties(0)
+        bus = "%04x:%02x:%02x" % (getattr(p, "pci_domain_id", 0), getattr(p, "pci_bus_id", 0),
+                                  getattr(p, "pci_device_id", 0))
+        self.sclk = (glob.glob(f"/sys/bus/pci/devices/{bus}*/pp_dpm_sclk") or [None])[0]
+        pw = [c for c in glob.glob(f"/sys/bus/pci/devices/{bus}*/hwmon/hwmon*/power1_*")
+              if c.endswith(("power1_input", "power1_average"))]
+        self.power = sorted(pw, key=lambda c: not c.endswith("input"))[0] if pw else None
+        self.period = period
+        self.tag = None
+        self.samples = []  # (tag, MHz or None, W or None)
+        self._stop = False
+        self._th = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        mhz = watts = None
+        if self.sclk:
+            try:
+                for line in open(self.sclk).read().splitlines():
+                    if line.rstrip().endswith("*"):
+                        mhz = float(line.split(":")[1].strip().lower().split("mhz")[0])
+            except (OSError, ValueError, IndexError):
+                pass
+        if self.power:
+            try:
+                watts = int(open(self.power).read()) / 1e6
+            except (OSError, ValueError):
+                pass
+        return mhz, watts
+
+    def _run(self):
+        while not self._stop:
+            tag = self.tag
+            if tag is not None:
+                mhz, watts = self._read()
+                if tag == self.tag:  # still the same leg
+                    self.samples.append((tag, mhz, watts))
+            time.sleep(self.period)
+
+    def __enter__(self):
+        if self.sclk or self.power:
+            self._th.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop = True
+        if self._th.is_alive():
+            self._th.join()
+
+    def summary(self, tag):
+        mhz = sorted(m for t, m, _ in self.samples if t == tag and m is not None)
+        watts = [x for t, _, x in self.samples if t == tag and x is not None]
+        if not mhz and not watts:
+            return None
+        return {"sclk_mhz_median": mhz[len(mhz) // 2] if mhz else None,
+                "sclk_mhz_min": mhz[0] if mhz else None, "sclk_mhz_max": mhz[-1] if mhz else None,
+                "board_power_w_mean": round(sum(watts) / len(watts), 1) if watts else None,
+                "samples": max(len(mhz), len(watts))}
+
+
+def interleaved(legs, rounds, seed, sampler):
+    """Every leg once per round, in a freshly shuffled order each round (a
+    seeded generator); each launch bracketed by HIP events on the stream it
+    runs on and synchronised before the next, so it runs alone on the GPU.
+    Two untimed launches of each leg first.  Returns name -> list of ms."""
+    import random
+
     import torch
+    names = list(legs)
+    for name in names:
+        for _ in range(2):
+            legs[name]()
+        torch.cuda.synchronize()
+    rng = random.Random(seed)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ms = {name: [] for name in names}
+    for r in range(rounds):
+        order = names[:]
+        rng.shuffle(order)
+        for name in order:
+            sampler.tag = name
+            e0.record()
+            legs[name]()
+            e1.record()
+            e1.synchronize()
+            sampler.tag = None
+            ms[name].append(e0.elapsed_time(e1))
+        if (r + 1) % 10 == 0 or r + 1 == rounds:
+            log(f"interleaved round {r + 1}/{rounds} done")
+    return ms
 
+
+def _stat(xs):
+    ys = sorted(xs)
+    n = len(ys)
+    med = ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
+    return {"median_ms": round(med, 4), "mean_ms": round(sum(ys) / n, 4), "min_ms": round(ys[0], 4),
+            "max_ms": round(ys[-1], 4), "n": n}
+
+
+def group_bytes(w, iters):
+    """Algorithmic HBM bytes of a cold vc_smooth_group call and of a
+    permutation-reuse call: iters k-means reads of V, the K/V gather, the
+    second V' gather of the residual pass, the K' and R writes, labels and
+    pi, the block means."""
     B, H, S, D = w.B, w.H, w.S, w.D
     nb = (S + 127) // 128
     bf = 2 * B * S * H * D            # one bf16 tensor
     f8 = B * H * nb * 128 * D         # one FP8 operand
-    q_bytes = bf + f8 + 4 * B * H * nb
-    apply_bytes = 3 * bf + 2 * f8 + 8 * B * H * S + 6 * B * H * nb * D  # gather K, V; residual pass; K', R; labels, pi; means
-    group_bytes = iters * bf + apply_bytes
-    tq = sum(ms_q) / len(ms_q)
-    tg = sum(ms_g) / len(ms_g)
-    # the reuse step: the permutation of the last grouping, gather + means + residuals only
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    vc.vc_smooth_group(k, v, clusters, iters, w.seed, workspace=ws, out=dict(g), reuse_perm=g["perm"])
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(n):
-        vc.vc_smooth_group(k, v, clusters, iters, w.seed, workspace=ws, out=dict(g), reuse_perm=g["perm"])
-    e1.record()
-    e1.synchronize()
-    tr = e0.elapsed_time(e1) / n
-    steps, window = 50, 13
+    apply_b = 3 * bf + 2 * f8 + 8 * B * H * S + 6 * B * H * nb * D
+    return iters * bf + apply_b, apply_b
+
+
+def quantize_bytes(w, with_kv):
+    """vc_quantize: read Q (and K, V) in bf16, write the FP8 codes and the
+    per-block (per-head for V) scales."""
+    B, H, S, D = w.B, w.H, w.S, w.D
+    nb = (S + 127) // 128
+    bf = 2 * B * S * H * D
+    f8 = B * H * nb * 128 * D
+    one = bf + f8 + 4 * B * H * nb
+    return one * 3 if with_kv else one
+
+
+def amortised(tg, tr, attn_ms, steps=50):
+    """Grouping cost per step over a `steps`-step schedule ([VC] §3.4, App. A:
+    grouping during the first ceil(steps / 4) steps, the permutation computed
+    afresh every 4th of them and reused in between)."""
+    window = -(-steps // 4)
     regroups = sum(1 for s in range(window) if s % 4 == 0)
     per_step = (regroups * tg + (window - regroups) * tr) / steps
-    gb = lambda b, t: round(b / (t * 1e-3) / 1e9, 1)  # noqa: E731
-    return {"vc_quantize_q": {"gb": round(q_bytes / 1e9, 3), "ms": round(tq, 3), "GBps": gb(q_bytes, tq),
-                              "frac_hbm": round(gb(q_bytes, tq) / HBM_PEAK_GBPS, 3)},
-            "vc_smooth_group": {"gb": round(group_bytes / 1e9, 3), "ms": round(tg, 3), "GBps": gb(group_bytes, tg),
-                                "frac_hbm": round(gb(group_bytes, tg) / HBM_PEAK_GBPS, 3)},
-            "vc_smooth_group_reuse_perm": {"gb": round(apply_bytes / 1e9, 3), "ms": round(tr, 3),
-                                           "GBps": gb(apply_bytes, tr),
-                                           "frac_hbm": round(gb(apply_bytes, tr) / HBM_PEAK_GBPS, 3)},
-            "grouping_amortised_50_steps": {"ms_per_step": round(per_step, 3),
-                                            "pct_of_attention": round(100 * per_step / attn_ms, 2)}}
+    return {"steps": steps, "group_steps": window, "regroups": regroups, "ms_per_step": round(per_step, 4),
+            "pct_of_attention": round(100 * per_step / attn_ms, 2)}
 
 
-def mxfp4_measurement(vc, w, q, k, v, g, flops, n=3):
-    """The 4-bit path (V-Smooth without ExpCast, MXFP4) on the same inputs and
-    grouping: vc_quantize4 (Q, and K/V through pi minus the block means) and
-    vc_attn_fwd4, HIP events, mean of n launches after one warm-up."""
-    import torch
-
-    z = vc.vc_quantize4(q, k, v, sm_scale=w.sm_scale, perm=g["perm"], mu_bf16=g["mu_bf16"])
-    o = torch.empty_like(q)
-
-    def timed(fn):
-        fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(n):
-            fn()
-        e1.record()
-        e1.synchronize()
-        return e0.elapsed_time(e1) / n
-
-    tq = timed(lambda: vc.vc_quantize4(q, k, v, sm_scale=w.sm_scale, perm=g["perm"], mu_bf16=g["mu_bf16"], out=z))
-    ta = timed(lambda: vc.vc_attn_fwd4(z["q4"], z["q4_scale"], z["k4"], z["k4_scale"], z["v4"], z["v4_scale"],
-                                       g["mu_bf16"], S=w.S, out=o))
-    tf = flops / (ta * 1e-3) / 1e12
-    del z, o
-    return {"format": "MXFP4 (E2M1, E8M0 per 32)", "vsmooth": True, "quantize4_ms": round(tq, 3),
-            "attn_ms": round(ta, 3), "tflops": round(tf, 1), "frac_fp4_peak": round(tf / FP4_PEAK_TFLOPS, 4)}
+def _gbps(nbytes, ms):
+    g = nbytes / (ms * 1e-3) / 1e9
+    return {"gb": round(nbytes / 1e9, 3), "ms": round(ms, 4), "GBps": round(g, 1),
+            "frac_hbm": round(g / HBM_PEAK_GBPS, 3)}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="wan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-repair", action="store_true", help="skip the Open-VC repair-row measurement")
     ap.add_argument("--no-mxfp4", action="store_true", help="skip the 4-bit (MXFP4) path measurement")
+    ap.add_argument("--no-m-leg", action="store_true", help="skip the H=48, S=84672 grouping legs")
+    ap.add_argument("--rounds", type=int, default=ROUNDS, help="interleaved launches per leg (median)")
     ap.add_argument("--traffic-job", action="store_true",
                     help="one attention launch + calibration copy, for rocprofv3 --pmc runs")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON", "COMMAND"),
@@ -471,6 +519,7 @@ def main():
             e[3].record()
             ev.append(e)
 
+    # ---- the step contract: W untimed steps, then exactly K whole-path steps
     for i in range(args.warmup):
         step()
         torch.cuda.synchronize()
@@ -483,57 +532,132 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     log(f"timed {args.steps} steps in {wall:.3f} s")
-    ms_q = [e[0].elapsed_time(e[1]) for e in evs]
-    ms_g = [e[1].elapsed_time(e[2]) for e in evs]
-    ms_a = [e[2].elapsed_time(e[3]) for e in evs]
-    flops = w.flops()
-    attn_ms = sum(ms_a) / len(ms_a)
-    value = flops / (attn_ms * 1e-3) / 1e12
     ms_per_step = wall * 1e3 / args.steps
+    step_ms = {"vc_quantize": _stat([e[0].elapsed_time(e[1]) for e in evs]),
+               "vc_smooth_group": _stat([e[1].elapsed_time(e[2]) for e in evs]),
+               "vc_attn_fwd": _stat([e[2].elapsed_time(e[3]) for e in evs])}
     assert torch.isfinite(o.float()).all().item(), "non-finite attention output"
+
+    # ---- the legs, sampled interleaved in random order -----------------------
+    head = "fp8_vsmooth" if vs_on else "fp8_plain"
+    legs = {}
+    if vs_on:
+        gr = {kk: vv for kk, vv in g.items() if kk not in ("centroids", "labels")}
+        perm0 = g["perm"].clone()
+        legs["fp8_vsmooth"] = lambda: vc.vc_attn_fwd(qz["q8"], qz["q_scale"], g["k8"], g["k_scale"], g["r8"],
+                                                     g["r_scale"], g["mu_split"], S=w.S, out=o)
+        legs["quantize_q"] = lambda: vc.vc_quantize(q, sm_scale=w.sm_scale, out=qz)
+        legs["group"] = lambda: vc.vc_smooth_group(k, v, clusters, iters, w.seed, workspace=ws, out=g)
+        legs["group_reuse"] = lambda: vc.vc_smooth_group(k, v, clusters, iters, w.seed, workspace=ws, out=gr,
+                                                         reuse_perm=perm0)
+    qp = qz if not vs_on else vc.vc_quantize(q, k, v, sm_scale=w.sm_scale)
+    op = torch.empty_like(q)
+    legs["fp8_plain"] = lambda: vc.vc_attn_fwd(qp["q8"], qp["q_scale"], qp["k8"], qp["k_scale"], qp["v8"],
+                                               qp["v_scale"], None, S=w.S, out=op)
+    legs["quantize_qkv"] = lambda: vc.vc_quantize(q, k, v, sm_scale=w.sm_scale, out=qp)
+    if not args.no_bf16:
+        vt = vc.vc_pack_v_bf16(v)
+        ob = torch.empty_like(q)
+        legs["bf16"] = lambda: vc.vc_attn_fwd_bf16(q, k, vt, out=ob, sm_scale=w.sm_scale)
+    rho = 0.005
+    if not args.no_repair:
+        R = vc.repair_count(w.S, rho)
+        rws = torch.empty(vc.vc_repair_workspace_size(w.B, w.H, w.S, w.D), dtype=torch.uint8, device=dev)
+        rp = vc.vc_repair_prepare(k, v, R, workspace=rws)
+        orp = torch.empty_like(q)
+        legs["repair_prepare"] = lambda: vc.vc_repair_prepare(k, v, R, workspace=rws, out=rp)
+        legs["fp8_plain_repair"] = lambda: vc.vc_attn_fwd(qp["q8"], qp["q_scale"], qp["k8"], qp["k_scale"],
+                                                          qp["v8"], qp["v_scale"], None, S=w.S, out=orp, repair=rp)
+    if not args.no_mxfp4 and vs_on:
+        z4 = vc.vc_quantize4(q, k, v, sm_scale=w.sm_scale, perm=g["perm"], mu_bf16=g["mu_bf16"])
+        o4 = torch.empty_like(q)
+        legs["quantize4"] = lambda: vc.vc_quantize4(q, k, v, sm_scale=w.sm_scale, perm=perm0, mu_bf16=g["mu_bf16"],
+                                                    out=z4)
+        legs["attn4"] = lambda: vc.vc_attn_fwd4(z4["q4"], z4["q4_scale"], z4["k4"], z4["k4_scale"], z4["v4"],
+                                                z4["v4_scale"], g["mu_bf16"], S=w.S, out=o4)
+    # the larger video shape's grouping (its own tensors), with its attention
+    # for the amortised share
+    wm = vcsynth.WORKLOADS["minimax"]
+    m_leg = vs_on and not args.no_m_leg and w.name != wm.name
+    if m_leg:
+        qm, km, vm = vcsynth.make_qkv(wm.name, device=dev)
+        wsm = torch.empty(vc.vc_smooth_group_workspace_size(wm.B, wm.H, wm.S, wm.D, wm.clusters), dtype=torch.uint8,
+                          device=dev)
+        gm = vc.vc_smooth_group(km, vm, wm.clusters, wm.iters, wm.seed, workspace=wsm)
+        grm = {kk: vv for kk, vv in gm.items() if kk not in ("centroids", "labels")}
+        permm = gm["perm"].clone()
+        qzm = vc.vc_quantize(qm, sm_scale=wm.sm_scale)
+        om = torch.empty_like(qm)
+        legs["M_group"] = lambda: vc.vc_smooth_group(km, vm, wm.clusters, wm.iters, wm.seed, workspace=wsm, out=gm)
+        legs["M_group_reuse"] = lambda: vc.vc_smooth_group(km, vm, wm.clusters, wm.iters, wm.seed, workspace=wsm,
+                                                           out=grm, reuse_perm=permm)
+        legs["M_fp8_vsmooth"] = lambda: vc.vc_attn_fwd(qzm["q8"], qzm["q_scale"], gm["k8"], gm["k_scale"], gm["r8"],
+                                                       gm["r_scale"], gm["mu_split"], S=wm.S, out=om)
+    torch.cuda.synchronize()
+    rounds = args.rounds
+    t0 = time.perf_counter()
+    with ClockSampler(torch) as clk:
+        ms = interleaved(legs, rounds, seed=20260, sampler=clk)
+    log(f"interleaved sampling: {len(legs)} legs x {rounds} rounds in {time.perf_counter() - t0:.1f} s")
+    st = {name: _stat(x) for name, x in ms.items()}
+    med = {name: x["median_ms"] for name, x in st.items()}
+    outs = [o, op] + ([om] if m_leg else [])
+    assert all(torch.isfinite(x.float()).all().item() for x in outs), "non-finite attention output"
+    flops = w.flops()
+    attn_ms = med[head]
+    value = flops / (attn_ms * 1e-3) / 1e12
+    clock = {name: clk.summary(name) for name in legs if clk.summary(name)}
+    clock_src = {"sclk": clk.sclk, "power": clk.power}
 
     traffic = traffic_from_profile() if (w.name == "wan" and vs_on) else None
     roof = {"bound": "mfma", "achieved": round(value, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(value / FP8_PEAK_TFLOPS, 4), "traffic": traffic,
             "kernel": "attn_fp8_kernel<128,%s>" % ("true" if vs_on else "false"),
-            "avg_launch_ms": round(attn_ms, 4), "flops_per_launch": flops}
+            "launch_ms_median": attn_ms, "launch_ms_mean": st[head]["mean_ms"], "launches": st[head]["n"],
+            "flops_per_launch": flops}
+    if clock.get(head, {}) and clock[head].get("sclk_mhz_median"):
+        f_obs = clock[head]["sclk_mhz_median"]
+        roof["clock_mhz_observed"] = f_obs
+        roof["frac_of_peak_at_observed_clock"] = round(value / (FP8_PEAK_TFLOPS * f_obs / 2400.0), 4)
 
     bf16 = None
-    if not args.no_bf16:
-        try:
-            vt = vc.vc_pack_v_bf16(v)
-            ob = torch.empty_like(q)
-            for _ in range(2):
-                vc.vc_attn_fwd_bf16(q, k, vt, out=ob, sm_scale=w.sm_scale)
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            n = max(3, args.steps)
-            e0.record()
-            for _ in range(n):
-                vc.vc_attn_fwd_bf16(q, k, vt, out=ob, sm_scale=w.sm_scale)
-            e1.record()
-            e1.synchronize()
-            bms = e0.elapsed_time(e1) / n
-            bt = flops / (bms * 1e-3) / 1e12
-            bf16 = {"ms": round(bms, 3), "tflops": round(bt, 1), "frac_of_bf16_peak": round(bt / BF16_PEAK_TFLOPS, 4),
-                    "speedup_fp8_over_bf16": round(bms / attn_ms, 3)}
-            del vt, ob
-        except vc.VcError as ex:
-            log(f"bf16 baseline unavailable: {ex}")
+    if "bf16" in med:
+        bt = flops / (med["bf16"] * 1e-3) / 1e12
+        bf16 = {"ms": med["bf16"], "tflops": round(bt, 1), "frac_of_bf16_peak": round(bt / BF16_PEAK_TFLOPS, 4),
+                "speedup_fp8_over_bf16": round(med["bf16"] / attn_ms, 3)}
 
     prep = None
     if vs_on:
-        prep = prep_measurement(vc, w, q, k, v, qz, g, ws, clusters, iters, attn_ms, ms_q, ms_g)
+        gb_cold, gb_reuse = group_bytes(w, iters)
+        prep = {"vc_quantize_q": _gbps(quantize_bytes(w, False), med["quantize_q"]),
+                "vc_quantize_qkv": _gbps(quantize_bytes(w, True), med["quantize_qkv"]),
+                "vc_smooth_group": _gbps(gb_cold, med["group"]),
+                "vc_smooth_group_reuse_perm": _gbps(gb_reuse, med["group_reuse"]),
+                "grouping_amortised_50_steps": amortised(med["group"], med["group_reuse"], attn_ms)}
+        if m_leg:
+            gm_cold, gm_reuse = group_bytes(wm, wm.iters)
+            prep["M"] = {"workload": f"{wm.name}: B={wm.B} H={wm.H} S={wm.S} D={wm.D}",
+                         "vc_smooth_group": _gbps(gm_cold, med["M_group"]),
+                         "vc_smooth_group_reuse_perm": _gbps(gm_reuse, med["M_group_reuse"]),
+                         "attn_fp8_vsmooth_ms": med["M_fp8_vsmooth"],
+                         "attn_tflops": round(wm.flops() / (med["M_fp8_vsmooth"] * 1e-3) / 1e12, 1),
+                         "grouping_amortised_50_steps": amortised(med["M_group"], med["M_group_reuse"],
+                                                                  med["M_fp8_vsmooth"])}
         log(f"prep: {prep}")
 
     repair = None
-    if not args.no_repair:
-        repair = repair_measurement(vc, w, q, k, v, flops)
+    if "fp8_plain_repair" in med:
+        repair = {"rho": rho, "rows_per_head": R, "prepare_ms": med["repair_prepare"],
+                  "attn_plain_ms": med["fp8_plain"], "attn_with_repair_ms": med["fp8_plain_repair"],
+                  "overhead_pct": round(100 * (med["fp8_plain_repair"] / med["fp8_plain"] - 1), 2),
+                  "tflops_with_repair": round(flops / (med["fp8_plain_repair"] * 1e-3) / 1e12, 1)}
         log(f"repair rows: {repair}")
 
     mx4 = None
-    if not args.no_mxfp4 and vs_on:
-        mx4 = mxfp4_measurement(vc, w, q, k, v, g, flops)
+    if "attn4" in med:
+        tf = flops / (med["attn4"] * 1e-3) / 1e12
+        mx4 = {"format": "MXFP4 (E2M1, E8M0 per 32)", "vsmooth": True, "quantize4_ms": med["quantize4"],
+               "attn_ms": med["attn4"], "tflops": round(tf, 1), "frac_fp4_peak": round(tf / FP4_PEAK_TFLOPS, 4)}
         log(f"mxfp4 path: {mx4}")
 
     cpu = None
@@ -560,9 +684,12 @@ def main():
                    "vsmooth": vs_on, "clusters": clusters, "kmeans_iters": iters, "window": 2,
                    "sm_scale": w.sm_scale},
         "pct_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
-        "breakdown_ms": {"vc_quantize": round(sum(ms_q) / len(ms_q), 3),
-                         "vc_smooth_group": round(sum(ms_g) / len(ms_g), 3),
-                         "vc_attn_fwd": round(attn_ms, 3)},
+        "timing": {"protocol": (f"{rounds} rounds; every round runs each leg once in a freshly shuffled order "
+                                "(seeded); each launch bracketed by HIP events on its stream and synchronised "
+                                "before the next; value and every leg figure are medians"),
+                   "legs": st},
+        "clock": {"per_leg": clock, "source": clock_src},
+        "step_breakdown_ms": step_ms,
         "path_tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
         "roofline": roof,
         "bf16_baseline": bf16,
