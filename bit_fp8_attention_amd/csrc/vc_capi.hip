@@ -29,6 +29,7 @@ int32_t check_bshd(const vc_bshd* x) {
   if (!aligned16(x->ptr)) return VC_ERR_ALIGN;
   if ((x->sB % 8) || (x->sS % 8) || (x->sH % 8)) return VC_ERR_ALIGN;
   if (x->sB < 0 || x->sS < 0 || x->sH < 0) return VC_ERR_SHAPE;
+  if (x->sS >= ((int64_t)1 << 30)) return VC_ERR_SHAPE;  // token stride below 2^31 bytes
   return VC_OK;
 }
 

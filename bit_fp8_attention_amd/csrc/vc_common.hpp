@@ -13,6 +13,7 @@
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef unsigned int u32;
 typedef u32 v4u __attribute__((ext_vector_type(4)));
 

@@ -16,11 +16,11 @@
 // order-independent; pi is a stable counting sort.
 //
 // Kernels per call: init (Forgy indices by partial Fisher-Yates on
-// SplitMix64, centroids, norms, zeroed accumulators) -> iters x (assign +
-// LDS-accumulate, update) -> label histogram -> scan -> stable scatter ->
-// apply pass 1 (gather K, V by pi; K' per-block codes; block means; residual
-// channel maxima) -> apply pass 2 (residual codes, key-contiguous; scaled
-// means).
+// SplitMix64, centroids, norms, zeroed accumulators) -> iters x (assign and
+// member sums, update; the last assignment also counts each 256-token
+// chunk's labels) -> scan of the counts -> stable scatter -> apply pass 1
+// (gather K, V by pi; K' per-block codes; block means; residual channel
+// maxima) -> apply pass 2 (residual codes, key-contiguous; scaled means).
 #include <algorithm>
 
 #include "vc_common.hpp"
@@ -33,6 +33,7 @@ namespace {
 
 constexpr int kAssignTokens = 2048;  // tokens per assign workgroup
 constexpr int kChunk = 256;          // tokens per histogram / scatter chunk
+constexpr unsigned char kOpen = 0xff;  // label byte of a token not settled yet (k <= 255)
 
 struct GroupWs {
   long long* sums;      // [BH][k][D]
@@ -82,6 +83,11 @@ VC_DEV float fx24_mean(long long s, long long n) {
 // same integer as fx24 -- and converted exactly (|v * 2^24| < 2^31).
 VC_DEV long long fx24_small(u32 b16) {
   return (long long)(int)__builtin_rintf(__uint_as_float((b16 << 16) + (24u << 23)));
+}
+
+// Row t of a token-major tensor: one 32 x 32 -> 64-bit multiply-add.
+VC_DEV const uint16_t* token_row(const uint16_t* base, int t, u32 rowB) {
+  return (const uint16_t*)((const char*)base + (uint64_t)(u32)t * rowB);
 }
 
 // The oracle's assignment rule for one token: one fp32 fmaf chain per
@@ -179,10 +185,21 @@ __global__ __launch_bounds__(256) void group_init(const uint16_t* __restrict__ v
       for (int m = 0; m < NS; ++m) pos[m] = val[m] = -1;
       const int lane = t;
       int n = 0;
-      uint64_t st = seed + 0x9E3779B97F4A7C15ull * (uint64_t)(1 + bh);
+      // the draws need no map: SplitMix64's i-th output depends only on its
+      // counter, so lane i computes draws i and 64 + i (k <= 128) up front
+      const uint64_t st0 = seed + 0x9E3779B97F4A7C15ull * (uint64_t)(1 + bh);
+      int jl[2] = {0, 0};
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int i = 64 * hh + lane;
+        if (i < k) {
+          uint64_t st = st0 + 0x9E3779B97F4A7C15ull * (uint64_t)i;
+          const uint64_t r = splitmix64_next(st);
+          jl[hh] = i + (int)(((r >> 32) * (uint64_t)(unsigned)(S - i)) >> 32);
+        }
+      }
       for (int i = 0; i < k; ++i) {
-        const uint64_t r = splitmix64_next(st);
-        const int j = i + (int)(((r >> 32) * (uint64_t)(unsigned)(S - i)) >> 32);
+        const int j = i < 64 ? __shfl(jl[0], i) : __shfl(jl[1], i - 64);
         int ei = -1, ej = -1, ai = i, aj = j;
 #pragma unroll
         for (int m = 0; m < NS; ++m) {
@@ -220,11 +237,16 @@ __global__ __launch_bounds__(256) void group_init(const uint16_t* __restrict__ v
     }
     __syncthreads();
     const uint16_t* vb = v + b * sB + h * sH;
-    for (int e = t; e < k * D; e += 256) {
-      const int c = e / D, d = e % D;
-      const float x = bf16_to_f32(vb[(int64_t)idx[c] * sS + d]);
-      cb[e] = x;
-      cl[e] = x;
+    constexpr int CPR = D / 8;  // 16-byte chunks per row
+    for (int q = t; q < k * CPR; q += 256) {
+      const int c = q / CPR, u = q % CPR;
+      float x[8];
+      unpack8(*(const uint4*)(vb + (int64_t)idx[c] * sS + 8 * u), x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        cb[c * D + 8 * u + e] = x[e];
+        cl[c * D + 8 * u + e] = x[e];
+      }
     }
   }
   __syncthreads();
@@ -245,18 +267,21 @@ __global__ __launch_bounds__(256) void amax_reset(int D, GroupWs ws) {
 
 // Assignment on the matrix cores, with the exact rule's result.
 //
-// Every centroid c is split exactly into three bf16 parts (hi = bf16(c),
-// mid = bf16(c - hi), lo = c - hi - mid: each difference is exact in fp32 and
-// the last fits in 8 bits), so bf16 products x_d * part are exact and
-// v_mfma_f32_16x16x32_bf16 sums the 3D products of q = x . c in fp32.
-// However the matrix core orders and rounds that sum, it stays within
-// gamma_{3D+12}(2^-23) (1 + 2^-7) S of x . c, S = sum_d |x_d c_d| <= |x| |c|
-// (each addition off by at most 2^-23 relative); the oracle's fmaf chain p
-// stays within gamma_D(2^-24) S.  With a = fl(|c|^2 - 2q) and e the exact
-// rule's fl(|c|^2 - 2p), for D <= 128
-//   |a_c - e_c| <= 1.11e-4 |x| |c| + 2^-23 |a_c| (+ flushed tiny products),
-// and the kernel takes over twice that,
-//   beta_c = |x| |c| 1.0625 2^-12 + |a_c| 2^-22 + 2^-96,
+// Every centroid component c is split into two bf16 parts, hi = bf16(c) and
+// mid = bf16(c - hi) (c - hi is exact in fp32), so |c - hi - mid| <= 2^-16 |c|
+// and bf16 products x_d * part are exact: v_mfma_f32_16x16x32_bf16 sums the
+// 2D products of q ~ x . c in fp32.  However the matrix core orders and
+// rounds that sum, it stays within gamma_{2D+8}(2^-23) (1 + 2^-6) S of
+// x . (hi + mid), S = sum_d |x_d c_d| <= |x| |c| (each addition off by at
+// most 2^-23 relative), and the dropped part adds at most 2^-16 S; the
+// oracle's fmaf chain p stays within gamma_D(2^-24) S of x . c.  With
+// a = fl(|c|^2 - 2q) and e the exact rule's fl(|c|^2 - 2p), for D <= 128
+//   |a_c - e_c| <= 1.10e-4 |x| |c| + 2^-23 |a_c| + 2^-121.5 |x| + 2^-118
+// (the last two terms: mid parts below the smallest normal bf16, 2^-126,
+// and tiny products, should the matrix core flush them: at most
+// 2 sum_d |x_d| 2^-126 <= 2 sqrt(D) |x| 2^-126 and 2D 2^-126), and the
+// kernel takes more than that, twice the first two terms,
+//   beta_c = |x| (|c| 1.0625 2^-12 + 2^-120) + |a_c| 2^-22 + 2^-96,
 // with |x| and |c| rounded up.  The exact argmin c* then has
 // a_c* - beta_c* <= e_c* <= e_c <= a_c + beta_c for every c, so it lies in
 // {c : a_c - beta_c <= min_c' (a_c' + beta_c')}.  A token whose set has one
@@ -266,15 +291,15 @@ __global__ __launch_bounds__(256) void amax_reset(int D, GroupWs ws) {
 // Work: 512 threads, kAssignTokens tokens per workgroup; wave w takes 16 TBW
 // tokens per step; lane (g, lr) loads channels 32 kc + 8 g .. + 7 of token
 // 16 tb + lr (the B operand) and, after the products, holds centroids
-// 16 cb + 4 g + v of that token.  Labels go to LDS; once all are final, the
-// member sums are taken by walking runs of tokens (below).
+// 16 cb + 4 g + v of that token.  Labels go to LDS, and the settled tokens'
+// rows into the member sums (below) in the same step.
 template <int D, int NCB>
 __global__ __launch_bounds__(512) void kmeans_assign_mx(const uint16_t* __restrict__ v, int64_t sB, int64_t sS,
                                                         int64_t sH, int S, int H, int k,
                                                         const float* __restrict__ cent, int32_t* __restrict__ labels,
-                                                        GroupWs ws) {
+                                                        GroupWs ws, int last, int nchunk) {
   constexpr int NKC = D / 32;             // 32-channel chunks
-  constexpr int NF = NCB * NKC * 3;       // A fragments (centroid block, chunk, part)
+  constexpr int NF = NCB * NKC * 2;       // A fragments (centroid block, chunk, part)
   constexpr int TBW = NCB <= 4 ? 4 : 2;   // 16-token blocks per wave step
   constexpr int KP = 16 * NCB;            // centroids, padded
   constexpr int LD = D + 1;               // member-sum row stride (bank spread)
@@ -284,10 +309,15 @@ __global__ __launch_bounds__(512) void kmeans_assign_mx(const uint16_t* __restri
   __shared__ unsigned long long lsum[KP * LD];
   __shared__ int lcnt[KP];
   __shared__ __attribute__((aligned(16))) float lnrm[KP], lbc[KP];
-  __shared__ __attribute__((aligned(16))) unsigned char lbl[kAssignTokens];  // every token's label (k <= 255)
+  // every token's label (k <= 255; kOpen while a token is open)
+  __shared__ __attribute__((aligned(16))) unsigned char lbl[kAssignTokens];
   __shared__ unsigned short otok[kAssignTokens];  // open tokens (offset in the workgroup's range)
   __shared__ u32 omask[kAssignTokens * NW];       // and their candidate sets
   __shared__ unsigned lmisc[2];                   // max |c|^2 (bits), open-list length
+  constexpr int NCH = kAssignTokens / kChunk;
+  static_assert(kAssignTokens % kChunk == 0, "whole histogram chunks per workgroup");
+  __shared__ int hcnt[NCH][KP];                   // last pass: label counts per 256-token chunk
+  __shared__ uint4 stage[8][16 * (D / 8)];        // per wave: one 16-token block of rows
   // heads vary fastest over the grid: the workgroups running at one time
   // read whole [H, D] stripes of the token-major value tensor
   const int h = blockIdx.x, b = blockIdx.z, t = threadIdx.x;
@@ -296,47 +326,98 @@ __global__ __launch_bounds__(512) void kmeans_assign_mx(const uint16_t* __restri
   const int base = blockIdx.y * kAssignTokens;
   const float* __restrict__ cb = cent + bh * k * D;
   for (int e = t; e < KP * LD; e += 512) lsum[e] = 0ull;
+  for (int e = t; e < NCH * KP; e += 512) (&hcnt[0][0])[e] = 0;
   for (int c = t; c < KP; c += 512) {
     lcnt[c] = 0;
     const float n2 = c < k ? ws.norms[bh * k + c] : INFINITY;  // padded centroids never win
     lnrm[c] = n2;
-    lbc[c] = __builtin_sqrtf(n2) * (1.0f + 0x1p-10f) * 0x1.1p-12f;  // >= |c| times the bound's factor
+    // >= |c| times the bound's factor, plus the flush allowance
+    lbc[c] = __builtin_fmaf(__builtin_sqrtf(n2) * (1.0f + 0x1p-10f), 0x1.1p-12f, 0x1p-120f);
   }
   if (t < 2) lmisc[t] = 0u;
   for (int q = t; q < KP * (D / 8); q += 512) {
     const int c = q / (D / 8), u = q % (D / 8);  // centroid c, channels 8u .. 8u + 7
-    u32 pw[3][4];
+    u32 pw[2][4];
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      u32 lo16[3], hi16[3];
+      u32 lo16[2], hi16[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const float x = c < k ? cb[c * D + 8 * u + e + j] : 0.f;
         const uint16_t p0 = f32_to_bf16(x);
-        const float r1 = x - bf16_to_f32(p0);
-        const uint16_t p1 = f32_to_bf16(r1);
-        const uint16_t p2 = f32_to_bf16(r1 - bf16_to_f32(p1));
+        const uint16_t p1 = f32_to_bf16(x - bf16_to_f32(p0));
         (j ? hi16 : lo16)[0] = p0;
         (j ? hi16 : lo16)[1] = p1;
-        (j ? hi16 : lo16)[2] = p2;
       }
 #pragma unroll
-      for (int part = 0; part < 3; ++part) pw[part][e / 2] = lo16[part] | (hi16[part] << 16);
+      for (int part = 0; part < 2; ++part) pw[part][e / 2] = lo16[part] | (hi16[part] << 16);
     }
     const int lane = (u & 3) * 16 + (c & 15);
 #pragma unroll
-    for (int part = 0; part < 3; ++part)
-      cfrag[(((c >> 4) * NKC + (u >> 2)) * 3 + part) * 64 + lane] =
+    for (int part = 0; part < 2; ++part)
+      cfrag[(((c >> 4) * NKC + (u >> 2)) * 2 + part) * 64 + lane] =
           make_uint4(pw[part][0], pw[part][1], pw[part][2], pw[part][3]);
   }
   __syncthreads();
-  float nl[NCB][4];
-#pragma unroll
-  for (int cbk = 0; cbk < NCB; ++cbk)
-#pragma unroll
-    for (int vv = 0; vv < 4; ++vv) nl[cbk][vv] = lnrm[16 * cbk + 4 * g + vv];
   const uint16_t* vb = v + b * sB + h * sH;
+  const u32 rowB = (u32)(2 * sS);  // bytes per token (below 2^31: checked at the boundary)
   const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  // Member sums, taken while the labels are made, from the rows already in
+  // registers (V is read once).  Lanes form groups of D / 8 (lane c of a
+  // group holds channels 8 c .. 8 c + 7 of a token); a group adds its tokens
+  // into 64-bit fixed-point registers and moves them to the cluster's LDS
+  // row only where the label changes.  A 16-token block reaches the groups
+  // through a wave-private LDS stage: chunk q (channels 8 q .. 8 q + 7) of
+  // row r sits at q ^ (r mod D / 8), so both the stage's writes and its
+  // reads hit distinct banks.  In an LDS sum row, channel 8 c + e sits at
+  // 8 c + ((e + c / 2) & 7): the 16 lanes of one flush hit 16 distinct bank
+  // pairs.  Open tokens are added once settled.  Fixed-point sums are exact,
+  // so the order of the additions does not matter.
+  constexpr int LPT = D / 8;     // lanes per token
+  constexpr int GPW = 64 / LPT;  // token groups per wave
+  constexpr int TPG = 16 / GPW;  // tokens of a 16-token block per group
+  const int grp = l / LPT, c = l % LPT;
+  uint4* const stg = &stage[w][0];
+  int cur = -1, run = 0;
+  long long sacc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sacc[e] = 0;
+  auto flush = [&]() {
+    unsigned long long* ls = lsum + cur * LD + 8 * c;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      atomicAdd(&ls[(e + (c >> 1)) & 7], (unsigned long long)sacc[e]);
+      sacc[e] = 0;
+    }
+    if (c == 0) atomicAdd(&lcnt[cur], run);
+    run = 0;
+  };
+  // one token's 8 channels of this lane, labelled L
+  auto add_row = [&](const uint4& row, int L) {
+    if (L != cur) {
+      if (cur >= 0) flush();
+      cur = L;
+    }
+    const u32 wd[4] = {row.x, row.y, row.z, row.w};
+    u32 mx = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) mx = max(mx, max(wd[q] & 0x7fffu, (wd[q] >> 16) & 0x7fffu));
+    if (mx < 0x4300u) {  // |x| < 128: the exponent shortcut
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        sacc[2 * q] += fx24_small(wd[q] & 0xffffu);
+        sacc[2 * q + 1] += fx24_small(wd[q] >> 16);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        sacc[2 * q] += fx24(bf16_lo(wd[q]));
+        sacc[2 * q + 1] += fx24(bf16_hi(wd[q]));
+      }
+    }
+    ++run;
+  };
 
   for (int it = 0; it < NIT; ++it) {
     const int t0 = base + (it * 8 + w) * 16 * TBW;
@@ -344,7 +425,7 @@ __global__ __launch_bounds__(512) void kmeans_assign_mx(const uint16_t* __restri
     uint4 xw[TBW][NKC];
 #pragma unroll
     for (int tb = 0; tb < TBW; ++tb) {
-      const uint16_t* row = vb + (int64_t)min(t0 + 16 * tb + lr, S - 1) * sS;  // rows past S: discarded
+      const uint16_t* row = token_row(vb, min(t0 + 16 * tb + lr, S - 1), rowB);  // rows past S: discarded
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) xw[tb][kc] = *(const uint4*)(row + 32 * kc + 8 * g);
     }
@@ -354,8 +435,8 @@ __global__ __launch_bounds__(512) void kmeans_assign_mx(const uint16_t* __restri
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
-        for (int part = 0; part < 3; ++part) {
-          const v8bf af = __builtin_bit_cast(v8bf, cfrag[((cbk * NKC + kc) * 3 + part) * 64 + l]);
+        for (int part = 0; part < 2; ++part) {
+          const v8bf af = __builtin_bit_cast(v8bf, cfrag[((cbk * NKC + kc) * 2 + part) * 64 + l]);
 #pragma unroll
           for (int tb = 0; tb < TBW; ++tb)
             acc[cbk][tb] = mfma_bf16(af, __builtin_bit_cast(v8bf, xw[tb][kc]),
@@ -363,30 +444,33 @@ __global__ __launch_bounds__(512) void kmeans_assign_mx(const uint16_t* __restri
         }
 #pragma unroll
     for (int tb = 0; tb < TBW; ++tb) {
-      // |x|^2
+      // |x|^2 straight from the packed pairs (v_dot2c_f32_bf16: exact bf16
+      // products, within a relative 2^-19 of the square norm over the 16
+      // accumulations; the factor 1 + 2^-10 below covers it, and 2^-59 any
+      // squares below the smallest normal that the instruction may flush)
       float x2 = 0.f;
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
         const u32 wd[4] = {xw[tb][kc].x, xw[tb][kc].y, xw[tb][kc].z, xw[tb][kc].w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          x2 = __builtin_fmaf(bf16_lo(wd[q]), bf16_lo(wd[q]), x2);
-          x2 = __builtin_fmaf(bf16_hi(wd[q]), bf16_hi(wd[q]), x2);
-        }
+        for (int q = 0; q < 4; ++q)
+          x2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, wd[q]), __builtin_bit_cast(v2bf, wd[q]), x2,
+                                               false);
       }
       x2 = __uint_as_float(over_groups(__float_as_uint(x2), [](u32 x, u32 y) {
         return __float_as_uint(__uint_as_float(x) + __uint_as_float(y));
       }));
-      const float xn = __builtin_sqrtf(x2) * (1.0f + 0x1p-10f);  // >= |x| (a sum of squares, a sqrt)
+      const float xn = __builtin_fmaf(__builtin_sqrtf(x2), 1.0f + 0x1p-10f, 0x1p-59f);  // >= |x|
       float a[NCB][4], lo[NCB][4];
       float hmin = INFINITY;
 #pragma unroll
       for (int cbk = 0; cbk < NCB; ++cbk) {
         const float4 bc = *(const float4*)&lbc[16 * cbk + 4 * g];
-        const float bcv[4] = {bc.x, bc.y, bc.z, bc.w};
+        const float4 nc = *(const float4*)&lnrm[16 * cbk + 4 * g];
+        const float bcv[4] = {bc.x, bc.y, bc.z, bc.w}, ncv[4] = {nc.x, nc.y, nc.z, nc.w};
 #pragma unroll
         for (int vv = 0; vv < 4; ++vv) {
-          a[cbk][vv] = __builtin_fmaf(-2.0f, acc[cbk][tb][vv], nl[cbk][vv]);
+          a[cbk][vv] = __builtin_fmaf(-2.0f, acc[cbk][tb][vv], ncv[vv]);
           const float beta = __builtin_fmaf(fabsf(a[cbk][vv]), 0x1p-22f, __builtin_fmaf(xn, bcv[vv], 0x1p-96f));
           lo[cbk][vv] = a[cbk][vv] - beta;  // NaN for padded centroids: never a candidate
           hmin = fminf(hmin, a[cbk][vv] + beta);
@@ -421,11 +505,26 @@ __global__ __launch_bounds__(512) void kmeans_assign_mx(const uint16_t* __restri
           labels[bh * S + tok] = idx;
           lbl[tok - base] = (unsigned char)idx;
         } else {
+          lbl[tok - base] = kOpen;
           const unsigned slot = atomicAdd(&lmisc[1], 1u);
           otok[slot] = (unsigned short)(tok - base);
 #pragma unroll
           for (int q = 0; q < NW; ++q) omask[slot * NW + q] = cm[q];
         }
+      }
+      // the block's settled tokens into the member sums, through the stage
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) stg[lr * LPT + ((4 * kc + g) ^ (lr & (LPT - 1)))] = xw[tb][kc];
+      // all of this group's labels (one LDS read) and rows first, then the sums
+      const int r0 = TPG * grp, tk0 = t0 + 16 * tb + r0;
+      const u32 lw = TPG == 4 ? *(const u32*)&lbl[tk0 - base] : (u32)*(const uint16_t*)&lbl[tk0 - base];
+      uint4 rows[TPG];
+#pragma unroll
+      for (int j = 0; j < TPG; ++j) rows[j] = stg[(r0 + j) * LPT + (c ^ ((r0 + j) & (LPT - 1)))];
+#pragma unroll
+      for (int j = 0; j < TPG; ++j) {
+        const int L = (int)((lw >> (8 * j)) & 0xffu);
+        if (L != kOpen && tk0 + j < S) add_row(rows[j], L);  // not open, not past S
       }
     }
   }
@@ -461,85 +560,16 @@ __global__ __launch_bounds__(512) void kmeans_assign_mx(const uint16_t* __restri
     lbl[tok - base] = (unsigned char)best;
   }
   __syncthreads();
-  // member sums and counts.  Every label is known now: each group of D / 8
-  // lanes walks its own run of consecutive tokens, lane c adding channels
-  // 8 c .. 8 c + 7 of each token into 64-bit registers, and adds them to
-  // the cluster's LDS sums only where the label changes (tokens in raster
-  // order come in long runs of one label).  Rows come 16 at a time, each
-  // batch added while the next one loads.  In an LDS sum row, channel
-  // 8 c + e sits at position 8 c + ((e + c / 2) & 7): the 16 lanes of one
-  // flush instruction then hit 16 distinct bank pairs.  Fixed-point sums are
-  // exact, so the order does not matter.
-  {
-    constexpr int LPT = D / 8;                       // lanes per token
-    constexpr int GPW = 64 / LPT;                    // token groups per wave
-    constexpr int SPAN = kAssignTokens / (8 * GPW);  // tokens per group (a multiple of 16)
-    constexpr int PF = 16;                           // rows per batch
-    const int grp = l / LPT, c = l % LPT;
-    const int r0 = base + (w * GPW + grp) * SPAN;
-    const int r1 = min(r0 + SPAN, S);
-    int cur = -1, run = 0;
-    long long acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0;
-    auto flush = [&]() {
-      unsigned long long* ls = lsum + cur * LD + 8 * c;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        atomicAdd(&ls[(e + (c >> 1)) & 7], (unsigned long long)acc[e]);
-        acc[e] = 0;
-      }
-      if (c == 0) atomicAdd(&lcnt[cur], run);
-      run = 0;
-    };
-    // a batch: PF rows (row t0 + i clamped into the run, so every load is of
-    // a real token) and their PF label bytes (one 16-byte LDS read)
-    const uint16_t* rbase = vb + 8 * c;
-    auto load = [&](uint4 (&buf)[PF], uint4& lab, int t0) {
-#pragma unroll
-      for (int i = 0; i < PF; ++i) buf[i] = *(const uint4*)(rbase + (int64_t)min(t0 + i, r1 - 1) * sS);
-      lab = *(const uint4*)&lbl[t0 - base];
-    };
-    auto process = [&](const uint4 (&cw)[PF], const uint4& clab, int t0) {
-      const u32 lw[4] = {clab.x, clab.y, clab.z, clab.w};
-#pragma unroll
-      for (int i = 0; i < PF; ++i) {
-        if (t0 + i >= r1) continue;  // (no break: every index stays a constant)
-        const int L = (int)((lw[i >> 2] >> (8 * (i & 3))) & 0xffu);
-        if (L != cur) {
-          if (cur >= 0) flush();
-          cur = L;
-        }
-        const u32 wd[4] = {cw[i].x, cw[i].y, cw[i].z, cw[i].w};
-        u32 mx = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) mx = max(mx, max(wd[q] & 0x7fffu, (wd[q] >> 16) & 0x7fffu));
-        if (mx < 0x4300u) {  // |x| < 128: the exponent shortcut
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            acc[2 * q] += fx24_small(wd[q] & 0xffffu);
-            acc[2 * q + 1] += fx24_small(wd[q] >> 16);
-          }
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            acc[2 * q] += fx24(bf16_lo(wd[q]));
-            acc[2 * q + 1] += fx24(bf16_hi(wd[q]));
-          }
-        }
-        ++run;
-      }
-    };
-    uint4 wa[PF], wb[PF], la, lb;
-    if (r0 < r1) load(wa, la, r0);
-    for (int t0 = r0; t0 < r1; t0 += 2 * PF) {
-      if (t0 + PF < r1) load(wb, lb, t0 + PF);
-      process(wa, la, t0);
-      if (t0 + 2 * PF < r1) load(wa, la, t0 + 2 * PF);
-      if (t0 + PF < r1) process(wb, lb, t0 + PF);
-    }
-    if (cur >= 0) flush();
+  // last pass: the label histogram of each 256-token chunk (the counting
+  // sort's first step), written out after the next barrier
+  if (last)
+    for (int i = t; i < kAssignTokens && base + i < S; i += 512) atomicAdd(&hcnt[i / kChunk][lbl[i]], 1);
+  // the open tokens' rows, now that their labels are settled
+  for (int i = w * GPW + grp; i < nopen; i += 8 * GPW) {
+    const int off = otok[i];
+    add_row(*(const uint4*)token_row(vb + 8 * c, base + off, rowB), lbl[off]);
   }
+  if (cur >= 0) flush();
   __syncthreads();
   unsigned long long* gs = (unsigned long long*)ws.sums + bh * k * D;
   for (int e = t; e < k * D; e += 512) {
@@ -548,76 +578,104 @@ __global__ __launch_bounds__(512) void kmeans_assign_mx(const uint16_t* __restri
   }
   for (int e = t; e < k; e += 512)
     if (lcnt[e] > 0) atomicAdd((unsigned long long*)&ws.counts[bh * k + e], (unsigned long long)lcnt[e]);
+  if (last)
+    for (int e = t; e < NCH * k; e += 512) {
+      const int i = e / k, c = e % k, ch = blockIdx.y * NCH + i;
+      if (ch < nchunk) ws.hist[(bh * k + c) * nchunk + ch] = hcnt[i][c];
+    }
 }
 
-// Member means (empty clusters keep their centroid), norms, reset sums.
+// Member means (empty clusters keep their centroid), norms, reset sums and
+// counts: CPW centroids per workgroup, every element's loads issued at once.
+constexpr int kUpdCentroids = 8;
 template <int D>
 __global__ __launch_bounds__(256) void kmeans_update(int k, float* __restrict__ cent, GroupWs ws) {
-  __shared__ float cl[8192];  // the k x D centroids (k D <= 8192)
-  const int64_t bh = blockIdx.x;
-  const int t = threadIdx.x;
-  float* cb = cent + bh * k * D;
-  long long* sb = ws.sums + bh * k * D;
-  const long long* nb = ws.counts + bh * k;
-  for (int e = t; e < k * D; e += 256) {
-    long long n = nb[e / D];
-    const float c = n > 0 ? fx24_mean(sb[e], n) : cb[e];
-    cb[e] = c;
-    cl[e] = c;
-    sb[e] = 0;
+  constexpr int CPW = kUpdCentroids, PER = CPW * D / 256;
+  __shared__ float cl[CPW * D];
+  const int64_t bh = blockIdx.y;
+  const int c0 = blockIdx.x * CPW, t = threadIdx.x;
+  const int nc = min(CPW, k - c0);
+  float* cb = cent + (bh * k + c0) * D;
+  long long* sb = ws.sums + (bh * k + c0) * D;
+  long long* nb = ws.counts + bh * k + c0;
+  long long n[PER], sv[PER];
+  float old[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = t + 256 * i;
+    const bool in = e < nc * D;
+    n[i] = in ? nb[e / D] : 0;
+    sv[i] = in ? sb[e] : 0;
+    old[i] = in ? cb[e] : 0.0f;
   }
-  __syncthreads();
-  for (int c = t; c < k; c += 256) {
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = t + 256 * i;
+    if (e < nc * D) {
+      const float c = n[i] > 0 ? fx24_mean(sv[i], n[i]) : old[i];
+      cb[e] = c;
+      cl[e] = c;
+      sb[e] = 0;
+    }
+  }
+  __syncthreads();  // every count of this workgroup's centroids has been read
+  if (t < nc) {
     float n2 = 0.0f;
-    for (int d = 0; d < D; ++d) n2 = __builtin_fmaf(cl[c * D + d], cl[c * D + d], n2);
-    ws.norms[bh * k + c] = n2;
+    for (int d = 0; d < D; ++d) n2 = __builtin_fmaf(cl[t * D + d], cl[t * D + d], n2);
+    ws.norms[bh * k + c0 + t] = n2;
+    nb[t] = 0;
   }
-  __syncthreads();
-  for (int c = t; c < k; c += 256) ws.counts[bh * k + c] = 0;
 }
 
-// Per-chunk label counts: hist[bh][c][chunk].
-__global__ __launch_bounds__(256) void label_hist(const int32_t* __restrict__ labels, int S, int H, int k,
-                                                  int nchunk, GroupWs ws) {
-  __shared__ int cnt[256];
-  const int h = blockIdx.y, b = blockIdx.z, t = threadIdx.x, ch = blockIdx.x;
-  const int64_t bh = (int64_t)b * H + h;
-  if (t < k) cnt[t] = 0;
-  __syncthreads();
-  const int tok = ch * kChunk + t;
-  if (tok < S) atomicAdd(&cnt[labels[bh * S + tok]], 1);
-  __syncthreads();
-  if (t < k) ws.hist[(bh * k + t) * nchunk + ch] = cnt[t];
-}
-
-// Exclusive scan of hist[bh] in (label, chunk) order, in place.
+// Exclusive scan of hist[bh] in (label, chunk) order, in place: tiles of
+// 8192 counts go through LDS with coalesced loads and stores; each thread
+// scans 8 consecutive counts, the 1024 partial sums are scanned in LDS, and
+// the running total carries to the next tile.
 __global__ __launch_bounds__(1024) void hist_scan(int k, int nchunk, GroupWs ws) {
+  constexpr int PER = 8, TILE = 1024 * PER;
+  __shared__ int tile[TILE];
   __shared__ int part[1024];
   const int64_t bh = blockIdx.x;
   const int t = threadIdx.x;
   int* hb = ws.hist + bh * k * nchunk;
   const int E = k * nchunk;
-  const int per = (E + 1023) / 1024;
-  const int e0 = t * per, e1 = min(E, e0 + per);
-  int s = 0;
-  for (int e = e0; e < e1; ++e) s += hb[e];
-  part[t] = s;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    int x = t >= o ? part[t - o] : 0;
+  int carry = 0;
+  for (int b0 = 0; b0 < E; b0 += TILE) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = b0 + t + 1024 * i;
+      tile[t + 1024 * i] = e < E ? hb[e] : 0;
+    }
     __syncthreads();
-    part[t] += x;
+    int s = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) s += tile[PER * t + j];
+    part[t] = s;
     __syncthreads();
-  }
-  int run = part[t] - s;  // exclusive prefix of this segment
-  for (int e = e0; e < e1; ++e) {
-    int c = hb[e];
-    hb[e] = run;
-    run += c;
+    for (int o = 1; o < 1024; o <<= 1) {
+      const int x = t >= o ? part[t - o] : 0;
+      __syncthreads();
+      part[t] += x;
+      __syncthreads();
+    }
+    int run = carry + part[t] - s;  // exclusive prefix of this thread's 8 counts
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int c = tile[PER * t + j];
+      tile[PER * t + j] = run;
+      run += c;
+    }
+    carry += part[1023];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = b0 + t + 1024 * i;
+      if (e < E) hb[e] = tile[t + 1024 * i];
+    }
+    __syncthreads();  // the tile is reused
   }
 }
 
-// Stable scatter: perm[offset(label, chunk) + rank within chunk] = token.
 __global__ __launch_bounds__(256) void label_scatter(const int32_t* __restrict__ labels, int S, int H, int k,
                                                      int nchunk, GroupWs ws, int32_t* __restrict__ perm) {
   __shared__ int wcnt[4][256];
@@ -863,11 +921,13 @@ hipError_t launch_group_t(const vc_shape& sh, Bshd k, Bshd v, const vc_group_par
     const int ncb = kc <= 16 ? 1 : kc <= 32 ? 2 : kc <= 64 ? 4 : 8;  // k <= 8192 / D
     auto assign = ncb == 1 ? kmeans_assign_mx<D, 1> : ncb == 2 ? kmeans_assign_mx<D, 2>
                   : ncb == 4 ? kmeans_assign_mx<D, 4> : kmeans_assign_mx<D, (D == 64 ? 8 : 4)>;
+    const dim3 gu((kc + kUpdCentroids - 1) / kUpdCentroids, BH);
     for (int it = 0; it < p.iters; ++it) {
-      assign<<<ga, 512, 0, st>>>(v.p, v.sB, v.sS, v.sH, S, H, kc, cent, labels, ws);
-      kmeans_update<D><<<BH, 256, 0, st>>>(kc, cent, ws);
+      // the last pass also counts each 256-token chunk's labels
+      assign<<<ga, 512, 0, st>>>(v.p, v.sB, v.sS, v.sH, S, H, kc, cent, labels, ws, it == p.iters - 1 ? 1 : 0,
+                                 nchunk);
+      kmeans_update<D><<<gu, 256, 0, st>>>(kc, cent, ws);
     }
-    label_hist<<<dim3(nchunk, H, B), 256, 0, st>>>(labels, S, H, kc, nchunk, ws);
     hist_scan<<<BH, 1024, 0, st>>>(kc, nchunk, ws);
     label_scatter<<<dim3(nchunk, H, B), 256, 0, st>>>(labels, S, H, kc, nchunk, ws, perm);
   }

@@ -19,7 +19,8 @@
  *    nblk = ceil(S / 128) key/query blocks, S_pad = 128 * nblk.
  *  - bf16 activations are described by vc_bshd: element (b, s, h, d) lives at
  *    ptr + b*sB + s*sS + h*sH + d (strides in elements, d contiguous).  The
- *    base and all three strides must be multiples of 8 elements (16 bytes).
+ *    base and all three strides must be multiples of 8 elements (16 bytes),
+ *    and the token stride sS below 2^30 elements (2 GiB; VC_ERR_SHAPE).
  *  - FP8 data is OCP E4M3 (E4M3FN: bias 7, max 448, no infinities), the
  *    format gfx950's matrix cores consume.
  *  - Packed FP8 operand layouts.  K and V (and K', R) are stored tile-major

@@ -121,6 +121,14 @@ def test_smooth_group_validation(vc):
     assert call_ptrs(m.vc_group_params(64, 4, 0, 1), [None] + [FAKE] * 8) == 1  # warm start needs centroids
     assert call(m.vc_group_params(64, 4, 0, 0), wsb=ws - 1) == 5
     assert call(m.vc_group_params(64, 4, 0, 0), ws_ptr=FAKE + 16) == 3
+    # a token stride of 2^30 elements or more (the kernels' 32-bit row offsets)
+    huge = m.vc_bshd(FAKE, 1 << 31, 1 << 30, 128)
+    assert L.vc_smooth_group(ctypes.byref(sh), ctypes.byref(huge), ctypes.byref(ok),
+                             ctypes.byref(m.vc_group_params(64, 4, 0, 0)), None, *[P(FAKE)] * 9, P(FAKE), ws, st) == 2
+    near = m.vc_bshd(FAKE, 1 << 31, (1 << 30) - 8, 128)
+    assert L.vc_smooth_group(ctypes.byref(sh), ctypes.byref(near), ctypes.byref(ok),
+                             ctypes.byref(m.vc_group_params(64, 4, 0, 0)), None, *[P(FAKE)] * 9, P(FAKE), ws - 1,
+                             st) == 5  # the stride passes; the workspace size is what fails
     small = m.vc_shape(1, 1, 10, 128)
     assert L.vc_smooth_group(ctypes.byref(small), ctypes.byref(ok), ctypes.byref(ok),
                              ctypes.byref(m.vc_group_params(11, 1, 0, 0)), None, *[P(FAKE)] * 9, P(FAKE), ws,
