@@ -110,10 +110,11 @@ VC_DEV v8i vfrag(const uint8_t* vt, int m, const FragBase<D>& fb) {
 //   V(j): VALU -- running max, rescale, ExpCast codes P_j.
 // Half B runs one phase behind half A (one extra barrier at the start, A one
 // at the end), so on every SIMD one wave's matrix-core chain runs while the
-// other wave computes codes.  K and V tiles go through two 3-stage LDS rings;
-// half B issues all copies, in its V phase (it reads no LDS there): at V(j)
-// it loads K_{j+3} into K_j's stage and V_{j+2} into V_{j-1}'s stage, both
-// read for the last time in M(j).  A copy has four phases to land.
+// other wave computes codes.  K and V tiles go through two 4-stage LDS rings
+// (tile i in stage i mod 4), filled in the V phases: at V(j) the mean row
+// j + 2, K_{j+3} and V_{j+2} go into the stages of K_{j-1} and V_{j-2},
+// read for the last time in half B's M(j-1), one slot earlier; half A issues
+// them all with V-Smooth, and on the plain path half B issues V_{j+2}.
 // ---------------------------------------------------------------------------
 
 template <int D, bool VS>
@@ -126,13 +127,15 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
   constexpr int NM = D / 16;             // channel blocks of the output
   constexpr int TB = kBlk * D;           // bytes of one K or V tile
   constexpr int NI = TB / 1024 / 4;      // 1 KB copies per issuing wave per tile
-  // six separate LDS objects, so the compiler can tell every stage apart
+  // eight separate LDS objects, so the compiler can tell every stage apart
   __shared__ __attribute__((aligned(1024))) uint8_t kst0[TB];
   __shared__ __attribute__((aligned(1024))) uint8_t kst1[TB];
   __shared__ __attribute__((aligned(1024))) uint8_t kst2[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t kst3[TB];
   __shared__ __attribute__((aligned(1024))) uint8_t vst0[TB];
   __shared__ __attribute__((aligned(1024))) uint8_t vst1[TB];
   __shared__ __attribute__((aligned(1024))) uint8_t vst2[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t vst3[TB];
   // V-Smooth: ring of the scaled block-mean rows (bf16 hi | lo << 16 per
   // channel) of the last 16 visited tiles (one 8-tile restoration window
   // plus the rows in flight)
@@ -179,7 +182,16 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
   auto kscale = [&](int i) { return repair_visit(i) ? rksb[i - nblk] : ksb[tile_at(i)]; };
 
   const unsigned loff = (unsigned)l * 16u;
-  // copies of half B, wave wq: 1 KB blocks 4r + wq of a tile; with V-Smooth
+  // the stages of visit i (i mod 4; picked at run time)
+  auto kst_of = [&](int i) -> uint8_t* {
+    const int c = i & 3;
+    return c == 0 ? kst0 : (c == 1 ? kst1 : (c == 2 ? kst2 : kst3));
+  };
+  auto vst_of = [&](int i) -> uint8_t* {
+    const int c = i & 3;
+    return c == 0 ? vst0 : (c == 1 ? vst1 : (c == 2 ? vst2 : vst3));
+  };
+  // copies of half A, wave wq: 1 KB blocks 4r + wq of a tile; with V-Smooth
   // also bytes [wq D, (wq + 1) D) of the tile's mean row (D / 16 lanes),
   // issued first in a group, so that a read of the ring waits for no tile
   auto issue_mu = [&](int i) {
@@ -204,7 +216,7 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
       lds_dma16_raw(src + base + loff, dst + base);
     }
   };
-  constexpr int GRP = 2 * NI + (VS ? 1 : 0);  // copies per wave per full group
+  constexpr int GRP_A = VS ? 2 * NI + 1 : NI;  // copies per half-A wave per V phase
 
   const FragBase<D> fb(lr, g);
   // visit of the ragged last key tile: first when the order starts there,
@@ -216,17 +228,20 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
     for (int e = tid; e < MR * D; e += 512) mz[e] = 0u;
     __syncthreads();
   }
-  // prologue: mean row 0, K_0, V_0, K_1; K_0 must have landed before M(0)
-  if (hb) {
+  // prologue (half A): mean row 0, K_0, V_0, K_1, then group -1 (mean row 1,
+  // K_2, V_1); K_0 must have landed before M(0)
+  if (!hb) {
     issue_mu(0);
     issue_k(kst0, 0);
     issue_v(vst0, 0);
-    if (n > 1) {
-      issue_k(kst1, 1);
-      wait_vm_n<2 * NI>();
-    } else {
+    if (n > 1) issue_k(kst1, 1);
+    if (1 < n) issue_mu(1);
+    if (2 < n) issue_k(kst2, 2);
+    if (1 < n) issue_v(vst1, 1);
+    if (n >= 3)
+      wait_vm_n<4 * NI + (VS ? 1 : 0)>();
+    else
       wait_vm();
-    }
   }
 
   v8i qf[2];
@@ -392,7 +407,7 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
 
   // ---- V phase: running max, rescale, codes of tile j; half B then issues
   // the copies of K_{j+3} and V_{j+2} into the stages M(j) last read ----
-  auto vphase = [&](int j, uint8_t* Kdst, uint8_t* Vdst, bool tail, auto pm_tag) {
+  auto vphase = [&](int j, bool tail, auto pm_tag) {
     constexpr bool PM = decltype(pm_tag)::value;
     const int t = tile_at(j);
     if (tail) {
@@ -470,51 +485,57 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
     }
     // the next tile's key scale, a whole phase before it is needed
     if (j + 1 < n) skv = e8m0_of_pow2(kscale(j + 1));
-    if (hb) {
+    // The copies of V(j): mean row j + 2, K_{j+3}, V_{j+2}.  Half A issues
+    // its share and then waits until only those of V(j - 1) and V(j) are in
+    // flight, so the barrier ending this slot publishes the tiles read from
+    // the next slot on (K_{j+1}, and V_j when half A copies V).  With
+    // V-Smooth half A issues all of them; on the plain path half B copies
+    // V_{j+2} (into V_{j-2}'s stage) and waits for it at the end of M(j + 1)
+    // (the balance that measured fastest for each path: the issuing wave
+    // stalls for several hundred cycles, and the mean flush lengthens the M
+    // phases)
+    if (!hb) {
       if (j + 2 < n) issue_mu(j + 2);
-      if (j + 3 < n) issue_k(Kdst, j + 3);
-      if (j + 2 < n) issue_v(Vdst, j + 2);
+      if (j + 3 < n) issue_k(kst_of(j + 3), j + 3);
+      if (VS && j + 2 < n) issue_v(vst_of(j + 2), j + 2);
+      if (j + 3 < n)
+        wait_vm_n<2 * GRP_A>();
+      else
+        wait_vm();
+    } else if (!VS) {
+      if (j + 2 < n) issue_v(vst_of(j + 2), j + 2);
     }
   };
 
-  // end of an M phase in half B: the copies issued one V phase earlier may
-  // stay in flight, every older copy must have landed (the next phase of
-  // half A reads it)
+  // end of an M phase M(j) in half B (plain path): the V copies it issued
+  // in V(j - 1) may stay in flight, V_j (issued in V(j - 2)) must have
+  // landed (half A's next phase reads it)
   auto mwait = [&](int j) {
-    if (hb) {
-      if (j + 2 < n)
-        wait_vm_n<GRP>();
+    if (!VS && hb) {
+      if (j + 1 < n)
+        wait_vm_n<NI>();
       else
         wait_vm();
     }
   };
 
   phase_sync();  // prologue copies visible
-  // half B: one phase behind; it issues K_2 and V_1 in this slot
-  if (hb) {
-    if (1 < n) issue_mu(1);
-    if (2 < n) issue_k(kst2, 2);
-    if (1 < n) issue_v(vst1, 1);
-    phase_sync();
-  }
+  if (hb) phase_sync();  // half B: one phase behind
 
   // j = 0 (may be the ragged tile; no P.V yet)
-  mphase(0, kst0, vst2, std::false_type{}, std::true_type{}, std::false_type{});
+  mphase(0, kst0, vst3, std::false_type{}, std::true_type{}, std::false_type{});
   mwait(0);
   phase_sync();
-  vphase(0, kst0, vst2, tail_visit == 0, std::false_type{});
+  vphase(0, tail_visit == 0, std::false_type{});
   phase_sync();
 
-  // steady state, rolled: stages picked at run time (j mod 3)
+  // steady state, rolled: stages picked at run time (j mod 4)
   {
-    int ck = 1, cv = 0;
     auto steady = [&](int j, auto mask_tag) {
-      uint8_t* const Kc = ck == 0 ? kst0 : (ck == 1 ? kst1 : kst2);
-      uint8_t* const Vc = cv == 0 ? vst0 : (cv == 1 ? vst1 : vst2);
-      mphase(j, Kc, Vc, std::true_type{}, std::true_type{}, std::true_type{});
+      mphase(j, kst_of(j), vst_of(j - 1), std::true_type{}, std::true_type{}, std::true_type{});
       mwait(j);
       phase_sync();
-      vphase(j, Kc, Vc, false, std::true_type{});
+      vphase(j, false, std::true_type{});
       // plain path with repair tiles: the ragged tile may fall in here.  The
       // running max above then covered its pad keys, harmless because
       // vc_quantize makes them copies of the last key; their codes are
@@ -530,8 +551,6 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
         }
       }
       phase_sync();
-      ck = ck == 2 ? 0 : ck + 1;
-      cv = cv == 2 ? 0 : cv + 1;
     };
     // the loop with that check only where it can matter, so the common loop
     // carries no test
@@ -542,21 +561,17 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
     }
   }
   // j = n - 1 (may be the ragged tile); stages chosen at run time
-  const int cl = (n - 1) % 3;
-  uint8_t* const Kl = cl == 0 ? kst0 : (cl == 1 ? kst1 : kst2);
-  uint8_t* const Vp = cl == 0 ? vst2 : (cl == 1 ? vst0 : vst1);  // V_{n-2}
-  uint8_t* const Vl = cl == 0 ? vst0 : (cl == 1 ? vst1 : vst2);  // V_{n-1}
   if (n >= 2) {
-    mphase(n - 1, Kl, Vp, std::true_type{}, std::true_type{}, std::false_type{});
+    mphase(n - 1, kst_of(n - 1), vst_of(n - 2), std::true_type{}, std::true_type{}, std::false_type{});
     mwait(n - 1);
     phase_sync();
-    vphase(n - 1, Kl, Vp, tail_visit == n - 1, std::false_type{});
+    vphase(n - 1, tail_visit == n - 1, std::false_type{});
     phase_sync();
   }
   // M(n): the last P.V
-  mphase(n, nullptr, Vl, std::true_type{}, std::false_type{}, std::false_type{});
+  mphase(n, nullptr, vst_of(n - 1), std::true_type{}, std::false_type{}, std::false_type{});
   if (!hb) phase_sync();  // half A's extra barrier, matching half B's first
-  if (hb) wait_vm();      // no copy may outlive the workgroup's LDS
+  wait_vm();              // no copy may outlive the workgroup's LDS
 
   // ---- epilogue: O = (A / l) * s_V, bf16, original query order -----------
   if (!live) return;
