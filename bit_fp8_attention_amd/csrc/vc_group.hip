@@ -716,8 +716,10 @@ struct ApplyMap {
 };
 
 // Pass 1: gather K and V by pi; K' per-block codes; block means; residual
-// per-channel maxima.
-template <int D>
+// per-channel maxima.  PREP: the key preprocessing is on.  Without it every
+// K and V row of the tile is loaded up front, raw, in one round trip; with
+// it the keys are transformed in fp32 first and V follows.
+template <int D, bool PREP>
 __global__ __launch_bounds__(256) void group_apply1(const uint16_t* __restrict__ kx, int64_t kB, int64_t kS,
                                                     int64_t kH, const uint16_t* __restrict__ vx, int64_t vB,
                                                     int64_t vS, int64_t vH, int S, int H, int nblk,
@@ -725,8 +727,13 @@ __global__ __launch_bounds__(256) void group_apply1(const uint16_t* __restrict__
                                                     float* __restrict__ k_scale, uint16_t* __restrict__ mu_bf16,
                                                     GroupWs ws, PrepArgs pp) {
   using Mp = ApplyMap<D>;
-  __shared__ long long psum[Mp::RG][D];
-  __shared__ float pmax[Mp::RG][D];
+  // partial sums and maxima, row group x channel; a lane's 8 channels sit
+  // 16 apart (slot e * CPR + ch for channel 8 ch + e) so that the lanes of a
+  // row group write consecutive words, and the rows are padded so that the
+  // row groups of one wave start in different banks
+  constexpr int PW = D + 16;
+  __shared__ long long psum[Mp::RG][PW];
+  __shared__ float pmax[Mp::RG][PW];
   __shared__ float red[4];
   __shared__ float mu_l[D];
   const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
@@ -735,32 +742,76 @@ __global__ __launch_bounds__(256) void group_apply1(const uint16_t* __restrict__
   const int nvalid = min(kBlk, S - j * kBlk);
   // perm may be the caller's (VC_GROUP_REUSE_PERM): every gathered index is
   // clamped into [0, S), so a malformed permutation gives wrong codes, never
-  // an access outside K, V or the RoPE tables
+  // an access outside K, V or the RoPE tables.  Rows past the end of a
+  // ragged last tile load the tile's last row and count as zero.
   int tok[Mp::RPT];
+  bool ok[Mp::RPT];
 #pragma unroll
   for (int r = 0; r < Mp::RPT; ++r) {
-    int row = rg * Mp::RPT + r;
-    tok[r] = row < nvalid ? clamp_tok(perm[bh * S + j * kBlk + row], S) : -1;
+    const int row = rg * Mp::RPT + r;
+    ok[r] = row < nvalid;
+    tok[r] = clamp_tok(perm[bh * S + j * kBlk + min(row, nvalid - 1)], S);
   }
+  const uint16_t* kb = kx + b * kB + h * kH;
+  const uint16_t* vb = vx + b * vB + h * vH;
+  uint4 vr[Mp::RPT];
   // ---- K' = K[pi], per-block E4M3 ----
   // With preprocessing ([VC] App. B: centring statistics, RoPE, gather,
   // Hadamard, mean subtraction), each gathered key is rotated at its original
   // position, centred by the head's channel mean and transformed, as in
   // vc_quantize's K path, before the block scale is taken.
   {
-    const uint16_t* kb = kx + b * kB + h * kH;
-    float kv[Mp::RPT][8];
-    float cm[8];
-    if (pp.flags & kPrepCenter) {
+    uint8_t* kd = k8 + (bh * nblk * kBlk + (int64_t)j * kBlk) * D;
+    auto store_codes = [&](int r, const float (&x)[8], float inv) {
+      uint2 c;
+      c.x = cvt4_fp8(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
+      c.y = cvt4_fp8(x[4] * inv, x[5] * inv, x[6] * inv, x[7] * inv);
+      *(uint2*)(kd + kpack_off<D>(rg * Mp::RPT + r, ch >> 1) + (ch & 1) * 8) = c;
+    };
+    auto block_scale = [&](float m) {
+      m = wave_max(m);
+      if ((t & 63) == 0) red[t >> 6] = m;
+      __syncthreads();
+      m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+      // power-of-two block scale, as for vc_quantize's K
+      const int e = pow2_block_exp(m);
+      if (t == 0) k_scale[bh * nblk + j] = ldexpf(1.0f, e);
+      return ldexpf(1.0f, -e);
+    };
+    if constexpr (!PREP) {
+      uint4 kr[Mp::RPT];
 #pragma unroll
-      for (int e2 = 0; e2 < 8; ++e2) cm[e2] = fx24_mean_of(pp.ksum[bh * D + ch * 8 + e2], S);
-    }
-    float m = 0.0f;
+      for (int r = 0; r < Mp::RPT; ++r) kr[r] = *(const uint4*)(kb + (int64_t)tok[r] * kS + ch * 8);
 #pragma unroll
-    for (int r = 0; r < Mp::RPT; ++r) {
-      unpack8(tok[r] >= 0 ? *(const uint4*)(kb + (int64_t)tok[r] * kS + ch * 8) : make_uint4(0, 0, 0, 0), kv[r]);
-      if (pp.flags) {
-        if (tok[r] >= 0) {
+      for (int r = 0; r < Mp::RPT; ++r) vr[r] = *(const uint4*)(vb + (int64_t)tok[r] * vS + ch * 8);
+      float m = 0.0f;
+#pragma unroll
+      for (int r = 0; r < Mp::RPT; ++r) {
+        if (!ok[r]) kr[r] = make_uint4(0, 0, 0, 0);
+        float x[8];
+        unpack8(kr[r], x);
+#pragma unroll
+        for (int e2 = 0; e2 < 8; ++e2) m = fmaxf(m, fabsf(x[e2]));
+      }
+      const float inv = block_scale(m);
+#pragma unroll
+      for (int r = 0; r < Mp::RPT; ++r) {
+        float x[8];
+        unpack8(kr[r], x);
+        store_codes(r, x, inv);
+      }
+    } else {
+      float kv[Mp::RPT][8];
+      float cm[8];
+      if (pp.flags & kPrepCenter) {
+#pragma unroll
+        for (int e2 = 0; e2 < 8; ++e2) cm[e2] = fx24_mean_of(pp.ksum[bh * D + ch * 8 + e2], S);
+      }
+      float m = 0.0f;
+#pragma unroll
+      for (int r = 0; r < Mp::RPT; ++r) {
+        unpack8(ok[r] ? *(const uint4*)(kb + (int64_t)tok[r] * kS + ch * 8) : make_uint4(0, 0, 0, 0), kv[r]);
+        if (ok[r]) {
           if (pp.flags & kPrepRope)
             rope8(kv[r], pp.cs + (int64_t)tok[r] * (D / 2) + ch * 4, pp.sn + (int64_t)tok[r] * (D / 2) + ch * 4);
           if (pp.flags & kPrepCenter)
@@ -768,52 +819,60 @@ __global__ __launch_bounds__(256) void group_apply1(const uint16_t* __restrict__
             for (int e2 = 0; e2 < 8; ++e2) kv[r][e2] -= cm[e2];
         }
         if (pp.flags & kPrepHadamard) fwht_row8<Mp::CPR>(kv[r], ch);  // every lane of the row takes part
+#pragma unroll
+        for (int e2 = 0; e2 < 8; ++e2) m = fmaxf(m, fabsf(kv[r][e2]));
       }
+      const float inv = block_scale(m);
 #pragma unroll
-      for (int e2 = 0; e2 < 8; ++e2) m = fmaxf(m, fabsf(kv[r][e2]));
-    }
-    m = wave_max(m);
-    if ((t & 63) == 0) red[t >> 6] = m;
-    __syncthreads();
-    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    // power-of-two block scale, as for vc_quantize's K
-    const int e = pow2_block_exp(m);
-    const float inv = ldexpf(1.0f, -e);
-    if (t == 0) k_scale[bh * nblk + j] = ldexpf(1.0f, e);
-    uint8_t* kd = k8 + (bh * nblk * kBlk + (int64_t)j * kBlk) * D;
+      for (int r = 0; r < Mp::RPT; ++r) store_codes(r, kv[r], inv);
 #pragma unroll
-    for (int r = 0; r < Mp::RPT; ++r) {
-      uint2 c;
-      c.x = cvt4_fp8(kv[r][0] * inv, kv[r][1] * inv, kv[r][2] * inv, kv[r][3] * inv);
-      c.y = cvt4_fp8(kv[r][4] * inv, kv[r][5] * inv, kv[r][6] * inv, kv[r][7] * inv);
-      *(uint2*)(kd + kpack_off<D>(rg * Mp::RPT + r, ch >> 1) + (ch & 1) * 8) = c;
+      for (int r = 0; r < Mp::RPT; ++r) vr[r] = *(const uint4*)(vb + (int64_t)tok[r] * vS + ch * 8);
     }
   }
   // ---- V' block mean ----
-  const uint16_t* vb = vx + b * vB + h * vH;
-  float xv[Mp::RPT][8];
+#pragma unroll
+  for (int r = 0; r < Mp::RPT; ++r)
+    if (!ok[r]) vr[r] = make_uint4(0, 0, 0, 0);
   {
     long long ps[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    u32 mx = 0;
 #pragma unroll
     for (int r = 0; r < Mp::RPT; ++r) {
-      uint4 w = tok[r] >= 0 ? *(const uint4*)(vb + (int64_t)tok[r] * vS + ch * 8) : make_uint4(0, 0, 0, 0);
-      xv[r][0] = bf16_lo(w.x); xv[r][1] = bf16_hi(w.x);
-      xv[r][2] = bf16_lo(w.y); xv[r][3] = bf16_hi(w.y);
-      xv[r][4] = bf16_lo(w.z); xv[r][5] = bf16_hi(w.z);
-      xv[r][6] = bf16_lo(w.w); xv[r][7] = bf16_hi(w.w);
+      const u32 wd[4] = {vr[r].x, vr[r].y, vr[r].z, vr[r].w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ps[e] += fx24(xv[r][e]);
+      for (int q = 0; q < 4; ++q) mx = max(mx, max(wd[q] & 0x7fffu, (wd[q] >> 16) & 0x7fffu));
+    }
+    if (mx < 0x4300u) {  // every |x| < 128: the exponent shortcut
+#pragma unroll
+      for (int r = 0; r < Mp::RPT; ++r) {
+        const u32 wd[4] = {vr[r].x, vr[r].y, vr[r].z, vr[r].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          ps[2 * q] += fx24_small(wd[q] & 0xffffu);
+          ps[2 * q + 1] += fx24_small(wd[q] >> 16);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < Mp::RPT; ++r) {
+        float x[8];
+        unpack8(vr[r], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ps[e] += fx24(x[e]);
+      }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) psum[rg][ch * 8 + e] = ps[e];
+    for (int e = 0; e < 8; ++e) psum[rg][e * Mp::CPR + ch] = ps[e];
   }
   __syncthreads();
   if (t < D) {
+    // thread t sums slot t: channel 8 (t % CPR) + t / CPR
+    const int c = (t % Mp::CPR) * 8 + t / Mp::CPR;
     long long s = 0;
     for (int q = 0; q < Mp::RG; ++q) s += psum[q][t];
     uint16_t mb = f32_to_bf16(fx24_mean(s, nvalid));
-    mu_bf16[(bh * nblk + j) * D + t] = mb;
-    mu_l[t] = bf16_to_f32(mb);
+    mu_bf16[(bh * nblk + j) * D + c] = mb;
+    mu_l[c] = bf16_to_f32(mb);
   }
   __syncthreads();
   // ---- residual channel maxima ----
@@ -821,17 +880,21 @@ __global__ __launch_bounds__(256) void group_apply1(const uint16_t* __restrict__
     float pm[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int r = 0; r < Mp::RPT; ++r)
-      if (tok[r] >= 0)
+      if (ok[r]) {
+        float x[8];
+        unpack8(vr[r], x);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pm[e] = fmaxf(pm[e], fabsf(xv[r][e] - mu_l[ch * 8 + e]));
+        for (int e = 0; e < 8; ++e) pm[e] = fmaxf(pm[e], fabsf(x[e] - mu_l[ch * 8 + e]));
+      }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pmax[rg][ch * 8 + e] = pm[e];
+    for (int e = 0; e < 8; ++e) pmax[rg][e * Mp::CPR + ch] = pm[e];
   }
   __syncthreads();
   if (t < D) {
+    const int c = (t % Mp::CPR) * 8 + t / Mp::CPR;
     float m = 0.0f;
     for (int q = 0; q < Mp::RG; ++q) m = fmaxf(m, pmax[q][t]);
-    atomicMax(&ws.r_amax[bh * D + t], __float_as_uint(m));
+    atomicMax(&ws.r_amax[bh * D + c], __float_as_uint(m));
   }
 }
 
@@ -846,20 +909,42 @@ __global__ __launch_bounds__(256) void group_apply2(const uint16_t* __restrict__
                                                     uint8_t* __restrict__ r8, float* __restrict__ r_scale,
                                                     u32* __restrict__ mu_split) {
   using Mp = ApplyMap<D>;
-  constexpr int LD = D + 4;
-  __shared__ uint8_t tile[kBlk * LD];
+  // the packed tile in LDS, channel-major: channel d's 128 codes in V tile
+  // position order at tile[d * LP ...] (rows 16-byte aligned)
+  constexpr int LP = kBlk + 16;
+  __shared__ __align__(16) uint8_t tile[D * LP];
   __shared__ float inv_l[D], mu_l[D];
   const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
   const int64_t bh = (int64_t)b * H + h;
+  const int ch = t % Mp::CPR, rg = t / Mp::CPR;
+  const int nvalid = min(kBlk, S - j * kBlk);
+  // every row of the tile in one round trip: indices clamped as in pass 1,
+  // rows past the end of a ragged last tile load the tile's last row.  The
+  // per-channel loads come first (every lane issues them, so that the wait
+  // for them leaves the row loads in flight).
+  const int tc = t & (D - 1);
+  const u32 amax_bits = ws.r_amax[bh * D + tc];
+  const uint16_t mu_bits = mu_bf16[(bh * nblk + j) * D + tc];
+  const uint16_t* vb = vx + b * vB + h * vH;
+  uint4 w[Mp::RPT];
+  {
+    int tok[Mp::RPT];
+#pragma unroll
+    for (int r = 0; r < Mp::RPT; ++r)
+      tok[r] = clamp_tok(perm[bh * S + j * kBlk + min(rg * Mp::RPT + r, nvalid - 1)], S);
+#pragma unroll
+    for (int r = 0; r < Mp::RPT; ++r) w[r] = *(const uint4*)(vb + (int64_t)tok[r] * vS + ch * 8);
+  }
+  asm volatile("" ::"v"(amax_bits), "v"(mu_bits));  // keeps the two loads ahead of the row loads
   if (t < D) {
-    float m = __uint_as_float(ws.r_amax[bh * D + t]);
+    const float m = __uint_as_float(amax_bits);
     float s = 1.0f, inv = 1.0f;
     if (m > 0.0f) {
       s = m / 448.0f;
       inv = 448.0f / m;
     }
     inv_l[t] = inv;
-    float mu = bf16_to_f32(mu_bf16[(bh * nblk + j) * D + t]);
+    const float mu = bf16_to_f32(mu_bits);
     mu_l[t] = mu;
     const float ms = mu * inv;
     const uint16_t hi = f32_to_bf16(ms);
@@ -868,39 +953,44 @@ __global__ __launch_bounds__(256) void group_apply2(const uint16_t* __restrict__
     if (j == 0) r_scale[bh * D + t] = s;
   }
   __syncthreads();
-  const int ch = t % Mp::CPR, rg = t / Mp::CPR;
-  const int nvalid = min(kBlk, S - j * kBlk);
-  const uint16_t* vb = vx + b * vB + h * vH;
+  // codes of this lane's rows (keys 8 rg + r) and channels (8 ch + e):
+  // cw[r][0] holds channels 0..3 (byte e = channel e), cw[r][1] channels 4..7
+  u32 cw[Mp::RPT][2];
 #pragma unroll
   for (int r = 0; r < Mp::RPT; ++r) {
-    const int row = rg * Mp::RPT + r;
-    u32 c0 = 0, c1 = 0;
-    if (row < nvalid) {
-      const int tk = clamp_tok(perm[bh * S + j * kBlk + row], S);  // as in pass 1
-      uint4 w = *(const uint4*)(vb + (int64_t)tk * vS + ch * 8);
-      const float* mu = mu_l + ch * 8;
-      const float* iv = inv_l + ch * 8;
-      c0 = cvt4_fp8((bf16_lo(w.x) - mu[0]) * iv[0], (bf16_hi(w.x) - mu[1]) * iv[1], (bf16_lo(w.y) - mu[2]) * iv[2],
-                    (bf16_hi(w.y) - mu[3]) * iv[3]);
-      c1 = cvt4_fp8((bf16_lo(w.z) - mu[4]) * iv[4], (bf16_hi(w.z) - mu[5]) * iv[5], (bf16_lo(w.w) - mu[6]) * iv[6],
-                    (bf16_hi(w.w) - mu[7]) * iv[7]);
+    const float* mu = mu_l + ch * 8;
+    const float* iv = inv_l + ch * 8;
+    cw[r][0] = cvt4_fp8((bf16_lo(w[r].x) - mu[0]) * iv[0], (bf16_hi(w[r].x) - mu[1]) * iv[1],
+                        (bf16_lo(w[r].y) - mu[2]) * iv[2], (bf16_hi(w[r].y) - mu[3]) * iv[3]);
+    cw[r][1] = cvt4_fp8((bf16_lo(w[r].z) - mu[4]) * iv[4], (bf16_hi(w[r].z) - mu[5]) * iv[5],
+                        (bf16_lo(w[r].w) - mu[6]) * iv[6], (bf16_hi(w[r].w) - mu[7]) * iv[7]);
+    if (rg * Mp::RPT + r >= nvalid) cw[r][0] = cw[r][1] = 0;
+  }
+  // 4 x 4 byte transposes: four rows' words (byte = channel) into four
+  // channels' words (byte = row); keys k0 .. k0 + 3 (k0 a multiple of 4)
+  // sit at the 4 consecutive tile positions starting at the position of k0
+#pragma unroll
+  for (int rq = 0; rq < Mp::RPT / 4; ++rq) {
+    const int k0 = rg * Mp::RPT + 4 * rq;
+    const int p0 = vkey_of_pos(k0);  // the key <-> position swap is its own inverse
+#pragma unroll
+    for (int cq = 0; cq < 2; ++cq) {
+      const u32 x0 = cw[4 * rq][cq], x1 = cw[4 * rq + 1][cq], x2 = cw[4 * rq + 2][cq], x3 = cw[4 * rq + 3][cq];
+      const u32 a_lo = __builtin_amdgcn_perm(x1, x0, 0x05010400u), a_hi = __builtin_amdgcn_perm(x1, x0, 0x07030602u);
+      const u32 b_lo = __builtin_amdgcn_perm(x3, x2, 0x05010400u), b_hi = __builtin_amdgcn_perm(x3, x2, 0x07030602u);
+      const u32 y[4] = {__builtin_amdgcn_perm(b_lo, a_lo, 0x05040100u), __builtin_amdgcn_perm(b_lo, a_lo, 0x07060302u),
+                        __builtin_amdgcn_perm(b_hi, a_hi, 0x05040100u), __builtin_amdgcn_perm(b_hi, a_hi, 0x07060302u)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) *(u32*)(tile + (ch * 8 + 4 * cq + e) * LP + p0) = y[e];
     }
-    *(u32*)(tile + row * LD + ch * 8) = c0;
-    *(u32*)(tile + row * LD + ch * 8 + 4) = c1;
   }
   __syncthreads();
   uint8_t* ob = r8 + (bh * nblk + j) * (int64_t)D * kBlk;  // packed V tile j
   constexpr int TASKS = D * (kBlk / 16);
 #pragma unroll
   for (int i = 0; i < TASKS / 256; ++i) {
-    int task = t + 256 * i, d = task / (kBlk / 16), c = task % (kBlk / 16), k0 = c * 16;
-    u32 wv[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      wv[q] = (u32)tile[vkey_of_pos(k0 + 4 * q) * LD + d] | ((u32)tile[vkey_of_pos(k0 + 4 * q + 1) * LD + d] << 8) |
-             ((u32)tile[vkey_of_pos(k0 + 4 * q + 2) * LD + d] << 16) |
-             ((u32)tile[vkey_of_pos(k0 + 4 * q + 3) * LD + d] << 24);
-    *(uint4*)(ob + vpack_off(d, c)) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    const int task = t + 256 * i, d = task / (kBlk / 16), c = task % (kBlk / 16);
+    *(uint4*)(ob + vpack_off(d, c)) = *(const uint4*)(tile + d * LP + 16 * c);
   }
 }
 
@@ -931,8 +1021,9 @@ hipError_t launch_group_t(const vc_shape& sh, Bshd k, Bshd v, const vc_group_par
     hist_scan<<<BH, 1024, 0, st>>>(kc, nchunk, ws);
     label_scatter<<<dim3(nchunk, H, B), 256, 0, st>>>(labels, S, H, kc, nchunk, ws, perm);
   }
-  group_apply1<D><<<dim3(nblk, H, B), 256, 0, st>>>(k.p, k.sB, k.sS, k.sH, v.p, v.sB, v.sS, v.sH, S, H, nblk, perm,
-                                                    k8, k_scale, mu_bf16, ws, pp);
+  auto apply1 = pp.flags ? group_apply1<D, true> : group_apply1<D, false>;
+  apply1<<<dim3(nblk, H, B), 256, 0, st>>>(k.p, k.sB, k.sS, k.sH, v.p, v.sB, v.sS, v.sH, S, H, nblk, perm, k8, k_scale,
+                                           mu_bf16, ws, pp);
   group_apply2<D><<<dim3(nblk, H, B), 256, 0, st>>>(v.p, v.sB, v.sS, v.sH, S, H, nblk, perm, mu_bf16, ws, r8,
                                                     r_scale, mu_split);
   return hipGetLastError();
