@@ -366,7 +366,8 @@ hipError_t launch_v_amax(const vc_shape& sh, Bshd v, float* out, int stride, hip
 
 hipError_t launch_v_quant(const vc_shape& sh, Bshd v, uint8_t* v8, float* v_scale, hipStream_t st) {
   int nblk = (sh.S + kBlk - 1) / kBlk;
-  launch_v_amax(sh, v, v_scale, sh.D, st);
+  const hipError_t e = launch_v_amax(sh, v, v_scale, sh.D, st);
+  if (e != hipSuccess) return e;
   dim3 g2(nblk, sh.H, sh.B);
   if (sh.D == 128)
     v_convert<128><<<g2, 256, 0, st>>>(v.p, v.sB, v.sS, v.sH, sh.S, sh.H, nblk, v_scale, v8);

@@ -246,6 +246,22 @@ def test_smooth_group_ties_bitexact(vc, D, kc):
     _group_case(vc, k, v, kc, 3, 17)
 
 
+@pytest.mark.parametrize("D,kc,frac", [(128, 64, 0.1), (64, 64, 0.1), (128, 64, 0.3), (64, 128, 0.3)])
+def test_smooth_group_partial_ties_bitexact(vc, D, kc, frac):
+    # a fraction of the tokens repeat one value row, the rest are random: the
+    # Forgy draw takes about kc * frac copies of that row, so 150 to 450
+    # tokens per head are open, each tied between that many candidates (7 to
+    # 40), beside the random tokens settled by the matrix-core bound
+    print(f"case group partial ties D={D} k={kc} frac={frac}", flush=True)
+    S, H = 1500, 2
+    q, k, v = vcsynth.random_qkv(1, S, H, D, seed=37, v_kind="t3")
+    g = torch.Generator().manual_seed(8)
+    row = torch.randn((1, 1, H, D), generator=g).to(torch.bfloat16)
+    tied = (torch.rand((1, S, 1, 1), generator=g) < frac)
+    v = torch.where(tied, row.expand(1, S, H, D), v)
+    _group_case(vc, k, v, kc, 3, 29)
+
+
 def test_smooth_group_large_values_bitexact(vc):
     # a quarter of the tokens scaled x400 (|v| in the thousands): the slow
     # fixed-point conversion and a wide candidate margin
