@@ -352,11 +352,30 @@ class ClockSampler:
                 "samples": max(len(mhz), len(watts))}
 
 
+SPIN_MS = 0.5  # GPU spin ahead of each timed launch
+
+
+def spin_cycles(ms_target):
+    """Argument of torch.cuda._sleep that keeps the GPU busy for about
+    ms_target (measured once with events)."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1000)
+    e0.record()
+    torch.cuda._sleep(1_000_000)
+    e1.record()
+    e1.synchronize()
+    return max(1000, int(1_000_000 * ms_target / max(e0.elapsed_time(e1), 1e-3)))
+
+
 def interleaved(legs, rounds, seed, sampler):
     """Every leg once per round, in a freshly shuffled order each round (a
     seeded generator); each launch bracketed by HIP events on the stream it
     runs on and synchronised before the next, so it runs alone on the GPU.
-    Two untimed launches of each leg first.  Returns name -> list of ms."""
+    A short GPU spin is enqueued ahead of the start event, so that a call
+    made of several kernel launches is fully queued when its bracket opens
+    (its host-side enqueue time is not counted).  Two untimed launches of
+    each leg first.  Returns name -> list of ms."""
     import random
 
     import torch
@@ -365,6 +384,7 @@ def interleaved(legs, rounds, seed, sampler):
         for _ in range(2):
             legs[name]()
         torch.cuda.synchronize()
+    spin = spin_cycles(SPIN_MS)
     rng = random.Random(seed)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ms = {name: [] for name in names}
@@ -373,6 +393,7 @@ def interleaved(legs, rounds, seed, sampler):
         rng.shuffle(order)
         for name in order:
             sampler.tag = name
+            torch.cuda._sleep(spin)
             e0.record()
             legs[name]()
             e1.record()
@@ -686,7 +707,8 @@ def main():
         "pct_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
         "timing": {"protocol": (f"{rounds} rounds; every round runs each leg once in a freshly shuffled order "
                                 "(seeded); each launch bracketed by HIP events on its stream and synchronised "
-                                "before the next; value and every leg figure are medians"),
+                                f"before the next, behind a {SPIN_MS} ms GPU spin so that its kernels are all "
+                                "queued when the bracket opens; value and every leg figure are medians"),
                    "legs": st},
         "clock": {"per_leg": clock, "source": clock_src},
         "step_breakdown_ms": step_ms,
