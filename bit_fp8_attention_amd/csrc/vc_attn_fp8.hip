@@ -191,31 +191,18 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
     const int c = i & 3;
     return c == 0 ? vst0 : (c == 1 ? vst1 : (c == 2 ? vst2 : vst3));
   };
-  // copies of half A, wave wq: 1 KB blocks 4r + wq of a tile; with V-Smooth
-  // also bytes [wq D, (wq + 1) D) of the tile's mean row (D / 16 lanes),
-  // issued first in a group, so that a read of the ring waits for no tile
+  // copies of an issuing wave wq: the tile's NI consecutive 1 KB blocks from
+  // wq NI KB on, under one M0; with V-Smooth (half A) also bytes
+  // [wq D, (wq + 1) D) of the tile's mean row (D / 16 lanes), issued first
+  // in a group, so that a read of the ring waits for no tile
   auto issue_mu = [&](int i) {
     if (VS) {
       const uint8_t* msrc = (const uint8_t*)(mu + ((int64_t)bh * nblk + tile_at(i)) * D) + wq * D;
       if (l < D / 16) lds_dma16_raw(msrc + loff, (uint8_t*)&mring[i & (MR - 1)][0] + wq * D);
     }
   };
-  auto issue_k = [&](uint8_t* dst, int i) {
-    const uint8_t* src = ksrc(i);
-#pragma unroll
-    for (int r = 0; r < NI; ++r) {
-      const int base = (r * 4 + wq) * 1024;
-      lds_dma16_raw(src + base + loff, dst + base);
-    }
-  };
-  auto issue_v = [&](uint8_t* dst, int i) {
-    const uint8_t* src = vsrc(i);
-#pragma unroll
-    for (int r = 0; r < NI; ++r) {
-      const int base = (r * 4 + wq) * 1024;
-      lds_dma16_raw(src + base + loff, dst + base);
-    }
-  };
+  auto issue_k = [&](uint8_t* dst, int i) { lds_dma16_kb<NI>(ksrc(i) + wq * NI * 1024 + loff, dst + wq * NI * 1024); };
+  auto issue_v = [&](uint8_t* dst, int i) { lds_dma16_kb<NI>(vsrc(i) + wq * NI * 1024 + loff, dst + wq * NI * 1024); };
   constexpr int GRP_A = VS ? 2 * NI + 1 : NI;  // copies per half-A wave per V phase
 
   const FragBase<D> fb(lr, g);

@@ -139,6 +139,28 @@ VC_DEV void lds_dma16_raw(const void* g, void* lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
 }
 
+// NB consecutive 1 KB copies under one M0: lane i of copy r reads
+// g + 1024 r and lands at lds_base + 1024 r + 16 i.  The instruction's
+// immediate offset moves the global and the LDS address alike, so the
+// copies need one M0 write between them (a wave's copies issue about a
+// quarter faster than with an M0 write before each, measured).
+template <int NB>
+VC_DEV void lds_dma16_kb(const void* g, void* lds_base) {
+  static_assert(NB == 2 || NB == 4, "2 or 4 KB per call");
+  const unsigned lds = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)LDS_PTR(lds_base));
+  if constexpr (NB == 4)
+    asm volatile(
+        "s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off\n\tglobal_load_lds_dwordx4 %0, off offset:1024\n\t"
+        "global_load_lds_dwordx4 %0, off offset:2048\n\tglobal_load_lds_dwordx4 %0, off offset:3072" ::"v"(g),
+        "s"(lds)
+        : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off\n\tglobal_load_lds_dwordx4 %0, off offset:1024" ::"v"(
+                     g),
+                 "s"(lds)
+                 : "memory", "m0");
+}
+
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
 template <int B, int E, class F>
 VC_DEV void static_for(F&& f) {
