@@ -86,11 +86,10 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
       lds_dma16_raw(kbp + (int64_t)key * kS + kcol[r], dst + (r * 4 + wq) * 1024);
     }
   };
+  // V half-tiles are contiguous: the wave's NI consecutive 1 KB blocks under one M0
   auto issue_v = [&](uint8_t* dst, int j) {
     const uint8_t* vsrc = vb + ((int64_t)tile_at(j >> 1) * 2 + (j & 1)) * TB;
-#pragma unroll
-    for (int r = 0; r < NI; ++r)
-      lds_dma16_raw(vsrc + (r * 4 + wq) * 1024 + l * 16, dst + (r * 4 + wq) * 1024);
+    lds_dma16_kb<NI>(vsrc + wq * NI * 1024 + l * 16, dst + wq * NI * 1024);
   };
   constexpr int GRP = 2 * NI;
 

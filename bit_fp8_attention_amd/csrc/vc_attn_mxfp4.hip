@@ -298,11 +298,16 @@ __global__ __launch_bounds__(256, 2) void attn4_kernel(
     const int64_t t = (int64_t)bh * nblk + tile_at(i);
     const uint8_t* ks = k4 + t * TB + w * CW;
     const uint8_t* vs = v4 + t * TB + w * CW;
+    if constexpr (CW == 2048) {  // two 1 KB blocks under one M0 each
+      lds_dma16_kb<2>(ks + loff, &kst[st][w * CW]);
+      lds_dma16_kb<2>(vs + loff, &vst[st][w * CW]);
+    } else {
 #pragma unroll
-    for (int r = 0; r < (CW + 1023) / 1024; ++r) {
-      if (l * 16 < CW - 1024 * r) {
-        lds_dma16_raw(ks + 1024 * r + loff, &kst[st][w * CW + 1024 * r]);
-        lds_dma16_raw(vs + 1024 * r + loff, &vst[st][w * CW + 1024 * r]);
+      for (int r = 0; r < (CW + 1023) / 1024; ++r) {
+        if (l * 16 < CW - 1024 * r) {
+          lds_dma16_raw(ks + 1024 * r + loff, &kst[st][w * CW + 1024 * r]);
+          lds_dma16_raw(vs + 1024 * r + loff, &vst[st][w * CW + 1024 * r]);
+        }
       }
     }
     if (VS && w == 0 && l < D / 8) lds_dma16_raw((const uint8_t*)(mu + t * D) + loff, &mring[i & (MR - 1)][0]);
