@@ -164,6 +164,29 @@ def prep_job(w):
     log("prep job done")
 
 
+def attn4_job(w):
+    """The 4-bit path once on the workload: the grouping it reuses (pi and
+    the block means), vc_quantize4, one V-Smooth vc_attn_fwd4 launch, then
+    one plain device copy of COPY_BYTES as the very last dispatch (the
+    FETCH_SIZE / WRITE_SIZE calibration of --counter-summary)."""
+    import torch
+
+    import bit_fp8_attention_amd as vc
+    import vcsynth
+    q, k, v = vcsynth.make_qkv(w.name, device="cuda")
+    g = vc.vc_smooth_group(k, v, w.clusters or 64, w.iters or 4, w.seed)
+    z = vc.vc_quantize4(q, k, v, sm_scale=w.sm_scale, perm=g["perm"], mu_bf16=g["mu_bf16"])
+    o = torch.empty_like(q)
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    vc.vc_attn_fwd4(z["q4"], z["q4_scale"], z["k4"], z["k4_scale"], z["v4"], z["v4_scale"], g["mu_bf16"], S=w.S,
+                    out=o)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    log("attn4 job done")
+
+
 def counter_summary(out_path, title, dirs, command):
     """Per-kernel table of every counter found under the rocprofv3 --pmc
     output directories: value per dispatch (averaged over the kernel's
@@ -470,6 +493,8 @@ def main():
                     help="one attention launch + calibration copy, for rocprofv3 --pmc runs")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON", "COMMAND"),
                     help="write the per-launch traffic record from the two counter runs")
+    ap.add_argument("--attn4-job", action="store_true",
+                    help="one 4-bit V-Smooth launch, then a 1 GiB device copy (for rocprofv3 --pmc runs)")
     ap.add_argument("--prep-job", action="store_true",
                     help="the preparation passes once + calibration copy, for rocprofv3 --pmc runs")
     ap.add_argument("--counter-summary", nargs="+", metavar="ARG",
@@ -500,6 +525,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.traffic_job:
         traffic_job(w)
+        return
+    if args.attn4_job:
+        attn4_job(w)
         return
     if args.prep_job:
         prep_job(w)
