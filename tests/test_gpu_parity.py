@@ -262,6 +262,14 @@ def test_smooth_group_partial_ties_bitexact(vc, D, kc, frac):
     _group_case(vc, k, v, kc, 3, 29)
 
 
+def test_smooth_group_batch2_bitexact(vc):
+    # two batch entries of two heads, a ragged last tile: every (b, h) runs
+    # its own k-means, sort and apply passes
+    print("case group B=2 H=2 S=700 D=128 k=16", flush=True)
+    q, k, v = vcsynth.random_qkv(2, 700, 2, 128, seed=53, v_kind="t3")
+    _group_case(vc, k, v, 16, 3, 19)
+
+
 def test_smooth_group_large_values_bitexact(vc):
     # a quarter of the tokens scaled x400 (|v| in the thousands): the slow
     # fixed-point conversion and a wide candidate margin
@@ -402,6 +410,15 @@ def test_attn_vsmooth_ragged_parity(vc):
     print("case attn vsmooth ragged S=1000 D=128", flush=True)
     q, k, v = vcsynth.random_qkv(1, 1000, 2, 128, seed=11, v_kind="t3")
     err, _, _ = _vsmooth_case(vc, q, k, v, 16, 3, 5, 2 / math.sqrt(128))
+    assert err <= REL_L2_TOL, err
+
+
+def test_attn_vsmooth_batch2_parity(vc):
+    # B = 2 at D = 128: the V-Smooth kernel's (b, h) bases, an odd tile count
+    # (a dead half in the last pair) and a ragged tile
+    print("case attn vsmooth B=2 H=2 S=600 D=128", flush=True)
+    q, k, v = vcsynth.random_qkv(2, 600, 2, 128, seed=59, v_kind="t3")
+    err, _, _ = _vsmooth_case(vc, q, k, v, 16, 3, 7, 1 / math.sqrt(128))
     assert err <= REL_L2_TOL, err
 
 
