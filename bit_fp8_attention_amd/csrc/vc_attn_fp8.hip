@@ -38,8 +38,9 @@
 //  - K and V are stored tile-major and pre-swizzled (the packed layouts of
 //    vc_attn.h), so each 16 KB tile streams HBM -> LDS as one straight copy
 //    with global_load_lds_dwordx4 (no VGPR staging, no per-tile address
-//    arithmetic) into 3-stage rings, and the 32-byte fragment reads from LDS
-//    are bank-conflict free;
+//    arithmetic; each issuing wave copies a contiguous quarter under one M0)
+//    into 4-stage rings, and the 32-byte fragment reads from LDS are
+//    bank-conflict free;
 //  - workgroup ids are remapped so each XCD works on a contiguous range of
 //    query tiles of one head, whose mid-window sweeps hit the same K/V in that
 //    XCD's L2.
