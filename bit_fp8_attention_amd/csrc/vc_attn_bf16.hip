@@ -3,7 +3,8 @@
 // two 128-query tiles of one (b, h) that share one K/V stream; the two
 // 4-wave halves alternate a matrix-core phase and a VALU phase one phase
 // apart (barrier ping-pong); K/V stream HBM -> LDS with global_load_lds into
-// 3-stage rings issued by half B; fragments are read two MFMA pairs ahead;
+// 4-stage rings, issued by half A in its VALU phase; fragments are read two
+// MFMA pairs ahead;
 // S^T = K Q^T; the output is accumulated transposed (V^T P^T) so rescales
 // stay in the lane; row sums come from a matrix-core product against ones;
 // the same mid-window key order and epilogue.
@@ -13,7 +14,7 @@
 // (v_mfma_f32_16x16x32_bf16), and per score an fp32 exponential
 // p = exp2(acc * scale * log2 e - m) followed by a cast to bf16.  A step is
 // a 64-key half-tile, so the bf16 K and V stages (16 KB each) fill the same
-// 96 KB of rings as the FP8 kernel's 128-key tiles.
+// 128 KB of rings as the FP8 kernel's 128-key tiles.
 #include "vc_common.hpp"
 #include "vc_launch.hpp"
 
@@ -46,9 +47,11 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
   __shared__ __attribute__((aligned(1024))) uint8_t kst0[TB];
   __shared__ __attribute__((aligned(1024))) uint8_t kst1[TB];
   __shared__ __attribute__((aligned(1024))) uint8_t kst2[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t kst3[TB];
   __shared__ __attribute__((aligned(1024))) uint8_t vst0[TB];
   __shared__ __attribute__((aligned(1024))) uint8_t vst1[TB];
   __shared__ __attribute__((aligned(1024))) uint8_t vst2[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t vst3[TB];
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int pr = __builtin_amdgcn_readfirstlane(lin % npair);
@@ -56,7 +59,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
   const int b = bh / H, h = bh % H;
   const int tid = threadIdx.x, l = tid & 63, lr = l & 15, g = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool hb = w >= 4;  // half B: one phase behind, issues the copies
+  const bool hb = w >= 4;  // half B: one phase behind
   const int wq = w & 3;
   const bool live = 2 * pr + (hb ? 1 : 0) < nblk;
   const int qt = __builtin_amdgcn_readfirstlane(live ? 2 * pr + (hb ? 1 : 0) : nblk - 1);
@@ -91,18 +94,32 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
     const uint8_t* vsrc = vb + ((int64_t)tile_at(j >> 1) * 2 + (j & 1)) * TB;
     lds_dma16_kb<NI>(vsrc + wq * NI * 1024 + l * 16, dst + wq * NI * 1024);
   };
-  constexpr int GRP = 2 * NI;
+  constexpr int GRP = 2 * NI;  // copies per half-A wave per step
+  // the stages of step i (i mod 4; picked at run time)
+  auto kst_of = [&](int i) -> uint8_t* {
+    const int c = i & 3;
+    return c == 0 ? kst0 : (c == 1 ? kst1 : (c == 2 ? kst2 : kst3));
+  };
+  auto vst_of = [&](int i) -> uint8_t* {
+    const int c = i & 3;
+    return c == 0 ? vst0 : (c == 1 ? vst1 : (c == 2 ? vst2 : vst3));
+  };
 
   // the ragged last tile is steps 0, 1 or steps n - 2, n - 1
   const bool ragged = (S % kBlk) != 0;
   const bool tail_first = ragged && tile_at(0) == nblk - 1;
   const bool tail_last = ragged && !tail_first;
 
-  if (hb) {  // prologue: K_0, V_0, K_1
+  if (!hb) {  // prologue (half A): K_0, V_0, K_1, then K_2, V_1; K_0 must have landed before M(0)
     issue_k(kst0, 0);
     issue_v(vst0, 0);
-    issue_k(kst1, 1);
-    wait_vm_n<2 * NI>();
+    if (1 < n) issue_k(kst1, 1);
+    if (2 < n) issue_k(kst2, 2);
+    if (1 < n) issue_v(vst1, 1);
+    if (n >= 3)
+      wait_vm_n<4 * NI>();
+    else
+      wait_vm();
   }
 
   // Q^T fragments: sub-tile s, d chunk kc: lane holds query lr, d = 32 kc + 8 g .. + 7
@@ -195,9 +212,9 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
     (void)j;
   };
 
-  // ---- V phase: running max, rescale, probabilities of step j; half B
-  // then copies K_{j+3} and V_{j+2} into the stages M(j) read last ----
-  auto vphase = [&](int j, uint8_t* Kdst, uint8_t* Vdst, bool tail) {
+  // ---- V phase: running max, rescale, probabilities of step j; half A
+  // then copies K_{j+3} and V_{j+2} ----
+  auto vphase = [&](int j, bool tail) {
     if (tail) {
       const int lim = S - (tile_at(j >> 1) * kBlk + (j & 1) * kHalf);
 #pragma unroll
@@ -233,50 +250,40 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
           for (int v = 0; v < 4; ++v)
             P[s][p][4 * hb2 + v] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(Sc[s][2 * p + hb2][v], c1, nm));
     }
-    if (hb) {
-      if (j + 3 < n) issue_k(Kdst, j + 3);
-      if (j + 2 < n) issue_v(Vdst, j + 2);
-    }
-  };
-  auto mwait = [&](int j) {
-    if (hb) {
-      if (j + 2 < n)
-        wait_vm_n<GRP>();
+    // half A: K_{j+3} and V_{j+2} into the stages of K_{j-1} and V_{j-2}
+    // (read for the last time in half B's M(j - 1), one slot earlier), then
+    // wait until only these and the previous step's copies are in flight,
+    // so the barrier ending this slot publishes K_{j+1} and V_j
+    if (!hb) {
+      if (j + 3 < n) issue_k(kst_of(j + 3), j + 3);
+      if (j + 2 < n) issue_v(vst_of(j + 2), j + 2);
+      if (j + 3 < n)
+        wait_vm_n<2 * GRP>();
       else
         wait_vm();
     }
   };
 
   phase_sync();
-  if (hb) {
-    if (2 < n) issue_k(kst2, 2);
-    issue_v(vst1, 1);
-    phase_sync();
-  }
+  if (hb) phase_sync();  // half B: one phase behind
   const std::true_type T{};
   const std::false_type F{};
   // steps 0 and 1 (the ragged tile's halves when it is visited first)
-  mphase(0, kst0, vst2, F, T);
-  mwait(0);
+  mphase(0, kst0, vst3, F, T);
   phase_sync();
-  vphase(0, kst0, vst2, tail_first);
+  vphase(0, tail_first);
   phase_sync();
   mphase(1, kst1, vst0, T, T);
-  mwait(1);
   phase_sync();
-  vphase(1, kst1, vst0, tail_first);
+  vphase(1, tail_first);
   phase_sync();
   // steady state, steps 2 .. n - 3.  The loop stays rolled with the stages
-  // picked at run time (j mod 3): unrolled copies each kept the output
+  // picked at run time (j mod 4): unrolled copies each kept the output
   // accumulators in registers of their own and spilled.
   for (int j = 2; j < n - 2; ++j) {
-    const int c = j % 3;
-    uint8_t* const Kc = c == 0 ? kst0 : (c == 1 ? kst1 : kst2);
-    uint8_t* const Vp = c == 0 ? vst2 : (c == 1 ? vst0 : vst1);
-    mphase(j, Kc, Vp, T, T);
-    mwait(j);
+    mphase(j, kst_of(j), vst_of(j - 1), T, T);
     phase_sync();
-    vphase(j, Kc, Vp, false);
+    vphase(j, false);
     phase_sync();
   }
   // steps n - 2 and n - 1 (n >= 2 always; when n == 2 they are steps 0, 1 above)
@@ -284,23 +291,15 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int jj = n - 2 + e;
-      const int c = jj % 3;
-      uint8_t* const Kc = c == 0 ? kst0 : (c == 1 ? kst1 : kst2);
-      uint8_t* const Vp = c == 0 ? vst2 : (c == 1 ? vst0 : vst1);
-      mphase(jj, Kc, Vp, T, T);
-      mwait(jj);
+      mphase(jj, kst_of(jj), vst_of(jj - 1), T, T);
       phase_sync();
-      vphase(jj, Kc, Vp, tail_last);
+      vphase(jj, tail_last);
       phase_sync();
     }
   }
-  {
-    const int c = (n - 1) % 3;
-    const uint8_t* Vl = c == 0 ? vst0 : (c == 1 ? vst1 : vst2);  // V_{n-1}
-    mphase(n, nullptr, Vl, T, F);
-  }
+  mphase(n, nullptr, vst_of(n - 1), T, F);  // the last P.V (V_{n-1})
   if (!hb) phase_sync();  // half A's extra barrier, matching half B's first
-  if (hb) wait_vm();
+  wait_vm();              // no copy may outlive the workgroup's LDS
 
   if (!live) return;
   uint16_t* ob = o + b * oB + h * oH;
