@@ -31,7 +31,7 @@ VC_OK = 0
 VC_ATTN_SEQUENTIAL = 1
 VC_GROUP_WARM_START = 1
 VC_GROUP_REUSE_PERM = 2
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 
 class VcError(RuntimeError):

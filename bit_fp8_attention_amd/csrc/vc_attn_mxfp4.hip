@@ -3,7 +3,7 @@
 // ExpCast-FP8": P is kept in a microscaled 4-bit format, for which no affine
 // log-to-code map exists).  The pages' format is NVFP4; gfx950's matrix
 // cores take OCP MXFP4: E2M1 elements with one E8M0 (power-of-two) scale per
-// 32, applied by v_mfma_scale_f32_16x16x128_f8f6f4 from a per-lane byte.
+// 32, applied by v_mfma_scale_f32_32x32x64_f8f6f4 from a per-lane byte.
 //
 // Block scale of 32 elements: the smallest 2^e (e >= -127) with
 // amax <= 6 * 2^e (2^0 for zeros); elements E2M1_rne(x / 2^e)
@@ -14,18 +14,22 @@
 // Layouts (per (b, h); nblk = ceil(S / 128) tiles of 128 keys):
 //  - q4: row-major [S_pad][D/2] bytes, byte c = channels 2c (low nibble) and
 //    2c + 1; q4_scale [S_pad][D/32] E8M0 bytes.
-//  - k4: per tile 128 rows of D/2 bytes; tile row 16 t + 4 g + v holds key
-//    32 g + 4 t + v of the tile, so that the S^T accumulator of MFMA block t,
-//    register v, in lane group g holds key 32 g + 4 t + v: lane group g then
-//    holds keys [32 g, 32 g + 32), one P block, in its own registers.  The
-//    16-byte chunk c of row r sits at chunk c ^ k4swz(r), so that the 16 rows
-//    a fragment read touches spread over all LDS banks.
-//    k4_scale per tile 512 bytes [g][lr][t] (the scale of tile row 16 t + lr,
-//    channel block g; 127 where g >= D/32).
+//  - k4: per tile 128 rows of D/2 bytes; tile row 64 c + 32 b + 8 j + 4 h + v
+//    holds key 64 c + 32 h + 16 b + 4 j + v of the tile, so that the S^T
+//    accumulator of key block kb = 2 c + b, register 4 j + v, in lane half h
+//    holds key 64 c + 32 h + 16 b + 4 j + v: lane half h then holds keys
+//    [64 c + 32 h, 64 c + 32 h + 32), one P block, in its own registers, in
+//    the order the P operand takes them.  The 16-byte chunk c of row r sits
+//    at chunk c ^ k4swz(r), so that the 16 rows a fragment read touches
+//    spread over all LDS banks.
+//    k4_scale per tile 512 bytes [h][n][kb][c] (the scale of tile row
+//    32 kb + n, channel block 2 c + h; 127 where 2 c + h >= D/32).
 //  - v4: per tile D channel rows of 64 bytes (keys 0..127 of the tile,
 //    key 2c in the low nibble of byte c; 16-byte chunk c of row d at chunk
-//    c ^ ((d >> 2) & 3)); v4_scale per tile 512 bytes
-//    [g][lr][m] (the scale of channel 16 m + lr, keys [32 g, 32 g + 32)).
+//    c ^ ((d >> 2) & 3)); v4_scale per tile 512 bytes [h][n][cb][c] (the
+//    scale of channel 32 cb + n, keys [64 c + 32 h, 64 c + 32 h + 32)).
+//  The bytes of one lane (h = lane / 32, n = lane % 32) are its 8 scale
+//  operands of a tile, read as one 8-byte load.
 #include "vc_common.hpp"
 #include "vc_launch.hpp"
 
@@ -59,8 +63,9 @@ VC_DEV u32 cvt8_fp4(const float (&x)[8], float scale) {
   return w;
 }
 
-// tile row holding key k of the tile (inverse of the row -> key map above)
-VC_DEV int k4_row_of_key(int k) { return 16 * ((k & 31) >> 2) + 4 * (k >> 5) + (k & 3); }
+// tile row holding key k of the tile (inverse of the row -> key map above):
+// key 64 c + 32 h + 16 b + 4 j + v sits in row 64 c + 32 b + 8 j + 4 h + v
+VC_DEV int k4_row_of_key(int k) { return (k & 64) | ((k & 28) << 1) | ((k >> 3) & 4) | (k & 3); }
 // chunk swizzles: 4 rows of 64 bytes (2 of 32 at D = 64) fill the 256-byte
 // bank width, so rows r and r + 4 (r + 8) would collide without them
 template <int D>
@@ -177,10 +182,11 @@ __global__ __launch_bounds__(256) void kv4_tile_kernel(const uint16_t* __restric
     }
     const int row = k4_row_of_key(key);
     *(uint4*)(kt + row * (D / 2) + 16 * (blk ^ k4swz<D>(row))) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-    kts[(16 * blk + (row & 15)) * 8 + (row >> 4)] = (uint8_t)(e + 127);
+    kts[(32 * (blk & 1) + (row & 31)) * 8 + 2 * (row >> 5) + (blk >> 1)] = (uint8_t)(e + 127);
   }
-  // channel blocks the head dimension does not fill: scale 2^0
-  for (int item = tid; item < (4 - NB) * 16 * 8; item += 256) kts[NB * 128 + item] = 127;
+  // D = 64 has one 64-channel chunk: the second chunk's bytes hold 2^0
+  if (D == 64)
+    for (int item = tid; item < 256; item += 256) kts[2 * item + 1] = 127;
   // V: rows into LDS (fp32, minus the block mean), then one thread per
   // (channel, 32-key block)
   for (int item = tid; item < kBlk * (D / 8); item += 256) {
@@ -224,9 +230,9 @@ __global__ __launch_bounds__(256) void kv4_tile_kernel(const uint16_t* __restric
       wd[c] = cvt8_fp4(tt, sc);
     }
     *(uint4*)(vtp + d * 64 + 16 * (g ^ v4swz(d))) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-    vts[(16 * g + (d & 15)) * 8 + (d >> 4)] = (uint8_t)(e + 127);
+    vts[(32 * (g & 1) + (d & 31)) * 8 + 2 * (d >> 5) + (g >> 1)] = (uint8_t)(e + 127);
   }
-  for (int item = tid; item < 64 * 8; item += 256)  // channel blocks past D / 16: scale 2^0
+  for (int item = tid; item < 64 * 8; item += 256)  // channel blocks past D / 32: scale 2^0
     if ((item & 7) >= D / 16) vts[item] = 127;
 }
 
@@ -234,18 +240,34 @@ __global__ __launch_bounds__(256) void kv4_tile_kernel(const uint16_t* __restric
 //
 // One workgroup = one 128-query tile of one (b, h) (4 waves x 32 queries),
 // two workgroups per CU: their barriers are independent, so one
-// workgroup's VALU work overlaps the other's matrix-core work on each SIMD
-// (with both tiles in one 8-wave workgroup the shared per-tile barrier kept
-// the two waves of a SIMD in the same phase: 8-9% slower).  K/V tiles come
-// in the mid-window order through a 2-stage LDS ring that the 4 waves fill
-// with global_load_lds_dwordx4.  Per tile and 16-query sub-tile:
-// S^T = K Q^T (scores in log2 units), the running max on the true scores,
-// p = 2^(s - M) (v_exp_f32), one E8M0 block scale per lane (its 32 keys),
-// E2M1 codes, row sum (ones x P^T) and A^T += V^T P^T on the block-scaled
-// matrix cores, and with V-Smooth the block mean restored as A += r mu.
+// workgroup's VALU work overlaps the other's matrix-core work on each SIMD.
+// K/V tiles come in the mid-window order through a 2-stage LDS ring that the
+// 4 waves fill with global_load_lds_dwordx4.  The products are
+// v_mfma_scale_f32_32x32x64_f8f6f4 (FP4 operands): a wave's 32 queries are
+// one product's 32 columns, so lane l holds query l % 32 in both halves
+// (h = l / 32) and each half carries 32 of a product's 64 K values.  Every
+// product holds the SIMD's VALU issue for about the same few cycles
+// whatever its size, so the 32x32 products, each twice the work of a
+// 16x16x128 one, take half as many of those cycles.  Per tile:
+// S^T = K Q^T (scores in log2 units; tile row 32 kb + 8 j + 4 h + v of key
+// block kb lands in register 4 j + v of lane half h), the running max on
+// the true scores, p = 2^(s - M) (v_exp_f32), one E8M0 scale per lane and
+// 64-key chunk (its 32 keys: one P block), E2M1 codes, then the row sum
+// (ones x P^T) and A^T += V^T P^T on the block-scaled matrix cores, and with
+// V-Smooth the block mean restored as A += r mu.
 
-VC_DEV v4f mfma_fp4(v8i a, v8i b, v4f c, int sa, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+VC_DEV v16f mfma32_fp4(v8i a, v8i b, v16f c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
+}
+VC_DEV v16f mfma32_bf16(v8bf a, v8bf b, v16f c) { return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0); }
+
+// max over the two 32-lane halves (lanes l and l ^ 32 hold the same query)
+VC_DEV float max_over_halves(float x) {
+  const int xi = __float_as_int(x);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  return __builtin_fmaxf(__int_as_float(p32[0]), __int_as_float(p32[1]));
 }
 
 template <int D, bool VS>
@@ -254,7 +276,8 @@ __global__ __launch_bounds__(256, 2) void attn4_kernel(
     const uint8_t* __restrict__ k4s, const uint8_t* __restrict__ v4, const uint8_t* __restrict__ v4s,
     const uint16_t* __restrict__ mu, uint16_t* __restrict__ o, int64_t oB, int64_t oS, int64_t oH, int S, int H,
     int nblk, int npair, int window, int sequential) {
-  constexpr int NM = D / 16;
+  constexpr int NC = D / 64;        // 64-channel chunks of the score product
+  constexpr int NO = D / 32;        // 32-channel blocks of the output
   constexpr int TB = kBlk * D / 2;  // bytes of a K or V tile
   constexpr int NB = D / 32;
   __shared__ __attribute__((aligned(1024))) uint8_t kst[2][TB];
@@ -266,32 +289,29 @@ __global__ __launch_bounds__(256, 2) void attn4_kernel(
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int pr = __builtin_amdgcn_readfirstlane(lin % npair);
   const int bh = __builtin_amdgcn_readfirstlane(lin / npair);
-  const int tid = threadIdx.x, l = tid & 63, lr = l & 15, g = l >> 4;
+  const int tid = threadIdx.x, l = tid & 63, n = l & 31, hh = l >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wq = w & 3;
-  const bool live = true;
   const int qt = pr;  // one query tile per workgroup
   const int64_t S_pad = (int64_t)nblk * kBlk;
   const int start = __builtin_amdgcn_readfirstlane(sequential ? 0 : min((qt | 1) + window, nblk - 1));
   auto tile_at = [&](int i) -> int { return sequential ? i : (i <= start ? start - i : i); };
 
-  // Q fragments and scales of the wave's two 16-query sub-tiles
-  v8i qf[2];
-  int qsc[2];
+  // Q fragments of the wave's 32 queries: chunk c, lane half hh holds
+  // channels 64 c + 32 hh .. + 31 of query n, with their scale
+  v8i qf[NC];
+  int qsc[NC];
+  {
+    const int64_t qrow = (int64_t)bh * S_pad + qt * kBlk + 32 * wq + n;
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int64_t qrow = (int64_t)bh * S_pad + qt * kBlk + 32 * wq + 16 * s + lr;
-    uint4 qv = make_uint4(0, 0, 0, 0);
-    int sc = 127;
-    if (g < NB) {
-      qv = *(const uint4*)(q4 + qrow * (D / 2) + 16 * g);
-      sc = q4s[qrow * NB + g];
+    for (int c = 0; c < NC; ++c) {
+      const uint4 qv = *(const uint4*)(q4 + qrow * (D / 2) + 32 * c + 16 * hh);
+      qf[c] = v8i{(int)qv.x, (int)qv.y, (int)qv.z, (int)qv.w, 0, 0, 0, 0};
+      qsc[c] = q4s[qrow * NB + 2 * c + hh];
     }
-    qf[s] = v8i{(int)qv.x, (int)qv.y, (int)qv.z, (int)qv.w, 0, 0, 0, 0};
-    qsc[s] = sc;
   }
 
-  // copies of tile i into stage st: each wave 1/8 of the K and of the V tile
+  // copies of tile i into stage st: each wave a quarter of the K and of the V tile
   constexpr int CW = TB / 4;  // bytes per wave (2 KB at D = 128)
   const unsigned loff = (unsigned)l * 16u;
   auto issue = [&](int i, int st) {
@@ -312,7 +332,7 @@ __global__ __launch_bounds__(256, 2) void attn4_kernel(
     }
     if (VS && w == 0 && l < D / 8) lds_dma16_raw((const uint8_t*)(mu + t * D) + loff, &mring[i & (MR - 1)][0]);
   };
-  // per-lane scale bytes of tile i: 8 K scales (blocks t8) and 8 V scales (blocks m)
+  // per-lane scale bytes of tile i: K byte 2 kb + c, V byte 2 cb + c
   auto load_scales = [&](int i, uint2& ks, uint2& vs) {
     const int64_t t = (int64_t)bh * nblk + tile_at(i);
     ks = *(const uint2*)(k4s + t * 512 + l * 8);
@@ -321,25 +341,25 @@ __global__ __launch_bounds__(256, 2) void attn4_kernel(
   auto sbyte = [](const uint2& s, int k) -> int { return (int)(((k < 4 ? s.x : s.y) >> (8 * (k & 3))) & 0xffu); };
 
   const v8i ones = {0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};  // E2M1 1.0
-  const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
-  // M: running max of the sub-tile's query (log2 units); the score product
-  // starts its accumulator at -M, so it emits s - M directly (0 before the
-  // first tile, which always sets M)
-  float M[2] = {0.f, 0.f};
-  v4f cinit[2] = {zero4, zero4};
-  float L[2] = {0.f, 0.f};
-  v4f O[2][NM];
+  v16f zero16;
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
+  for (int e = 0; e < 16; ++e) zero16[e] = 0.f;
+  // M: running max of query n (log2 units); the score product starts its
+  // accumulator at -M, so it emits s - M directly (0 before the first tile,
+  // which always sets M)
+  float M = 0.f;
+  v16f cinit = zero16;
+  float L = 0.f;
+  v16f O[NO];  // A^T: lane half hh holds channels 32 cb + 8 j + 4 hh + v of query n
 #pragma unroll
-    for (int m = 0; m < NM; ++m) O[s][m] = zero4;
+  for (int cb = 0; cb < NO; ++cb) O[cb] = zero16;
 
-  // V-Smooth: row sums of the window slots 2g, 2g + 1 (lane group g), restored
-  // every 8 tiles on the bf16 matrix cores as A += r mu^T: lane group g
-  // carries its two slots in K slots 8g .. 8g + 7 as
-  //   mean side: (mu0, 0, mu1, 0, mu0, 0, mu1, 0)   (mu is exact in bf16)
-  //   sum side:  (r0.hi, r0.hi, r1.hi, r1.hi, r0.lo, 0, r1.lo, 0)
-  float rb[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+  // V-Smooth: row sums of window slots 4 hh .. 4 hh + 3 (lane half hh),
+  // restored every 8 tiles on the bf16 matrix cores as A += r mu^T: element
+  // 2q / 2q + 1 of lane half hh carries slot 4 hh + q as
+  //   mean side: (mu, mu)   (mu is exact in bf16)
+  //   sum side:  (r.hi, r.lo)
+  float rb[4] = {0.f, 0.f, 0.f, 0.f};
   if (VS) {  // rows never written must read as finite zeros
     for (int e2 = tid; e2 < MR * D; e2 += 256) (&mring[0][0])[e2] = 0;
     __syncthreads();
@@ -359,156 +379,141 @@ __global__ __launch_bounds__(256, 2) void attn4_kernel(
     }
     const uint8_t* Kt = kst[st];
     const uint8_t* Vt = vst[st];
-    // S^T = K Q^T: block t8 is tile rows 16 t8 + lr, channel block g
-    v4f Sc[2][8];
-    uint4 kv[8];
+    // S^T = K Q^T: key block kb is tile rows 32 kb + n (A operand), chunk c
+    v16f Sc[4];
 #pragma unroll
-    for (int t8 = 0; t8 < 8; ++t8) {
-      const int r = 16 * t8 + lr;
-      kv[t8] = g < NB ? *(const uint4*)(Kt + r * (D / 2) + 16 * (g ^ k4swz<D>(r))) : make_uint4(0, 0, 0, 0);
+    for (int kb = 0; kb < 4; ++kb) {
+      const int r = 32 * kb + n;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const uint4 kv = *(const uint4*)(Kt + r * (D / 2) + 16 * ((2 * c + hh) ^ k4swz<D>(r)));
+        const v8i kf = {(int)kv.x, (int)kv.y, (int)kv.z, (int)kv.w, 0, 0, 0, 0};
+        Sc[kb] = mfma32_fp4(kf, qf[c], c == 0 ? cinit : Sc[kb], sbyte(ksc, 2 * kb + c), qsc[c]);
+      }
     }
+    // V fragments of both chunks, read now so that their latency hides
+    // behind the max and the probabilities: channel block cb is row
+    // 32 cb + n, keys 64 cp + 32 hh .. + 31
+    uint4 vf[2][NO];
+#pragma unroll
+    for (int cp = 0; cp < 2; ++cp)
+#pragma unroll
+      for (int cb = 0; cb < NO; ++cb) {
+        const int d = 32 * cb + n;
+        vf[cp][cb] = *(const uint4*)(Vt + d * 64 + 16 * ((2 * cp + hh) ^ v4swz(d)));
+      }
     const int t = tile_at(i);
-    const bool ragged = t == nblk - 1 && (S % kBlk) != 0;  // keys past S: no probability
+    if (t == nblk - 1 && (S % kBlk) != 0) {  // keys past S: no probability
+      // opaque to the compiler, so the compares stay in this branch instead
+      // of being hoisted out of the loop as 64 live lane masks
+      int lim = S - t * kBlk;
+      asm volatile("" : "+s"(lim));
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)  // register e of block kb is key 64 (kb / 2) + 32 hh + 16 (kb % 2) + e
+          if (64 * (kb >> 1) + 32 * hh + 16 * (kb & 1) + e >= lim) Sc[kb][e] = -INFINITY;
+    }
+    // the lane's max over each 64-key chunk (its 32 keys: one P block), the
+    // row's max over both halves, and the rescale on an increase
+    float lm[2];
+#pragma unroll
+    for (int cp = 0; cp < 2; ++cp) {
+      float m = __builtin_fmaxf(Sc[2 * cp][0], Sc[2 * cp][1]);
+#pragma unroll
+      for (int e = 2; e < 32; e += 2)
+        m = __builtin_fmaxf(__builtin_fmaxf(m, Sc[2 * cp + (e >> 4)][e & 15]), Sc[2 * cp + (e >> 4)][(e & 15) + 1]);
+      lm[cp] = m;
+    }
+    const float rm = max_over_halves(__builtin_fmaxf(lm[0], lm[1]));  // the row's max of s - M
+    const bool rise = i == 0 || rm > 0.0f;
+    if (__any(rise)) {
+      const float delta = rise ? -rm : 0.0f;  // M - M'
+      if (i != 0) {
+        const float alpha = __builtin_amdgcn_exp2f(delta);
+        L *= alpha;
+        if (VS) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) rb[q] *= alpha;
+        }
+#pragma unroll
+        for (int cb = 0; cb < NO; ++cb) O[cb] = O[cb] * alpha;
+      }
+      M -= delta;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) cinit[e] = -M;
+      lm[0] += delta;
+      lm[1] += delta;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) Sc[kb] = Sc[kb] + delta;
+    }
+    // probabilities and codes of chunk cp: element 8 q + e of the lane's P
+    // operand is key 64 cp + 32 hh + 8 q + e, register 8 (q % 2) + e of
+    // key block 2 cp + q / 2
     v8i P[2];
     int pe[2];
-    float lmx[2], rr[2];
-    // one sub-tile (16 query rows) at a time: scores; running max and
-    // rescale; probabilities and their codes; row sum and P.V.  Sub-tile 1's
-    // scores come after sub-tile 0's rescale, and sub-tile 0's P.V after
-    // sub-tile 1's, so each stretch between the rescale branches pairs one
-    // sub-tile's matrix-core work with the other's VALU work
-    auto qk = [&](int s) {
-#pragma unroll
-      for (int t8 = 0; t8 < 8; ++t8) {
-        const v8i kf = {(int)kv[t8].x, (int)kv[t8].y, (int)kv[t8].z, (int)kv[t8].w, 0, 0, 0, 0};
-        Sc[s][t8] = mfma_fp4(kf, qf[s], cinit[s], sbyte(ksc, t8), qsc[s]);
-      }
-    };
-    auto mask = [&](int s) {
-      if (ragged) {
-        const int lim = S - t * kBlk;
-#pragma unroll
-        for (int t8 = 0; t8 < 8; ++t8)
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (32 * g + 4 * t8 + v >= lim) Sc[s][t8][v] = -INFINITY;
-      }
-    };
-    auto rescale = [&](int s) {
-      float lm = -INFINITY;  // the lane's max (its 32 keys: one P block)
-#pragma unroll
-      for (int t8 = 0; t8 < 8; ++t8)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) lm = fmaxf(lm, Sc[s][t8][v]);
-      const float rm = max_over_groups(lm);  // the row's max of s - M
-      const bool rise = i == 0 || rm > 0.0f;
-      if (__any(rise)) {
-        const float delta = rise ? -rm : 0.0f;  // M - M'
-        if (i != 0) {
-          const float alpha = __builtin_amdgcn_exp2f(delta);
-          L[s] *= alpha;
-          if (VS) {
-            rb[s][0] *= alpha;
-            rb[s][1] *= alpha;
-          }
-#pragma unroll
-          for (int m = 0; m < NM; ++m) O[s][m] = O[s][m] * alpha;
-        }
-        M[s] -= delta;
-        cinit[s] = v4f{-M[s], -M[s], -M[s], -M[s]};
-        lm += delta;
-#pragma unroll
-        for (int t8 = 0; t8 < 8; ++t8) Sc[s][t8] = Sc[s][t8] + delta;
-      }
-      lmx[s] = lm;
-    };
-    auto probs = [&](int s) {
-      const float pmax = __builtin_amdgcn_exp2f(lmx[s]);  // in [0, 1]: lmx <= 0
+    auto probs = [&](int cp) {
+      const float pmax = __builtin_amdgcn_exp2f(lm[cp]);  // in [0, 1]: lm <= 0
       const int e = mx_block_exp_prob(pmax);
       const float sc = ldexpf(1.0f, e);
-      pe[s] = e + 127;
-      // key 32 g + 4 t8 + v is nibble 4 t8 + v of the lane's P operand
+      pe[cp] = e + 127;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float p8[8];
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) p8[4 * u + v] = __builtin_amdgcn_exp2f(Sc[s][2 * q + u][v]);
-        P[s][q] = (int)cvt8_fp4(p8, sc);
+        for (int x = 0; x < 8; ++x) p8[x] = __builtin_amdgcn_exp2f(Sc[2 * cp + (q >> 1)][8 * (q & 1) + x]);
+        P[cp][q] = (int)cvt8_fp4(p8, sc);
       }
-      P[s][4] = P[s][5] = P[s][6] = P[s][7] = 0;
+      P[cp][4] = P[cp][5] = P[cp][6] = P[cp][7] = 0;
     };
-    // V's fragments, read once for both sub-tiles
-    v8i vf[NM];
-    auto pv = [&](int s) {
-      // row sum and A^T += V^T P^T
-      rr[s] = mfma_fp4(ones, P[s], zero4, 127, pe[s])[0];
-      L[s] += rr[s];
+    // row sum over both chunks and A^T += V^T P^T for chunk cp
+    v16f rs;
+    auto pv = [&](int cp) {
+      rs = mfma32_fp4(ones, P[cp], cp == 0 ? zero16 : rs, 127, pe[cp]);
 #pragma unroll
-      for (int m = 0; m < NM; ++m) O[s][m] = mfma_fp4(vf[m], P[s], O[s][m], sbyte(vsc, m), pe[s]);
+      for (int cb = 0; cb < NO; ++cb) {
+        const uint4 vv = vf[cp][cb];
+        const v8i a = {(int)vv.x, (int)vv.y, (int)vv.z, (int)vv.w, 0, 0, 0, 0};
+        O[cb] = mfma32_fp4(a, P[cp], O[cb], sbyte(vsc, 2 * cb + cp), pe[cp]);
+      }
     };
-    qk(0);
-    mask(0);
-    rescale(0);
-    qk(1);
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      const int d = 16 * m + lr;
-      const uint4 vv = *(const uint4*)(Vt + d * 64 + 16 * (g ^ v4swz(d)));
-      vf[m] = v8i{(int)vv.x, (int)vv.y, (int)vv.z, (int)vv.w, 0, 0, 0, 0};
-    }
     probs(0);
-    // sub-tile 0's codes stay ahead of sub-tile 1's branches, and its
-    // conversion work is spread between sub-tile 1's score products
+    // chunk 0's codes stay ahead of chunk 1's conversions, so its products
+    // can run beside them (the compiler's own placement of the products
+    // measured faster than a fixed interleave)
     asm volatile("" ::"v"(P[0][0]), "v"(P[0][1]), "v"(P[0][2]), "v"(P[0][3]), "v"(pe[0]));
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
-    }
-    mask(1);
-    rescale(1);
     pv(0);
     probs(1);
-    // and sub-tile 1's between sub-tile 0's row sum and P.V products
-#pragma unroll
-    for (int k = 0; k < 9; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
-    }
     pv(1);
+    const float rr = rs[0];
+    L += rr;
     if (VS) {
       const int slot = i & 7;
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        if (slot == 2 * g) rb[s2][0] = rr[s2];
-        if (slot == 2 * g + 1) rb[s2][1] = rr[s2];
-      }
+      for (int q = 0; q < 4; ++q)
+        if (slot == 4 * hh + q) rb[q] = rr;
       if (slot == 7 || i == nblk - 1) {
-        v8bf Ar[2];
+        v8bf Br;
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            const __bf16 hi = (__bf16)rb[s2][jj];
-            const __bf16 lo = (__bf16)(rb[s2][jj] - (float)hi);
-            Ar[s2][2 * jj + 0] = hi;
-            Ar[s2][2 * jj + 1] = hi;
-            Ar[s2][4 + 2 * jj + 0] = lo;
-            Ar[s2][4 + 2 * jj + 1] = (__bf16)0.0f;
-            rb[s2][jj] = 0.f;
-          }
+        for (int q = 0; q < 4; ++q) {
+          const __bf16 hi = (__bf16)rb[q];
+          Br[2 * q] = hi;
+          Br[2 * q + 1] = (__bf16)(rb[q] - (float)hi);
+          rb[q] = 0.f;
         }
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
-          // window slot 2g + jj is visit i - slot + 2g + jj; slots past i hold
-          // zero row sums, so whatever finite row the ring holds there adds nothing
-          const u32 m0 = mring[(i - slot + 2 * g) & (MR - 1)][16 * m + lr];
-          const u32 m1 = mring[(i - slot + 2 * g + 1) & (MR - 1)][16 * m + lr];
-          const v8bf Bm = __builtin_bit_cast(v8bf, (v4u){m0, m1, m0, m1});
-          O[0][m] = mfma_bf16(Bm, Ar[0], O[0][m]);
-          O[1][m] = mfma_bf16(Bm, Ar[1], O[1][m]);
+        for (int cb = 0; cb < NO; ++cb) {
+          // window slot 4 hh + q is visit i - slot + 4 hh + q; slots past i
+          // hold zero row sums, so whatever finite row the ring holds there
+          // adds nothing
+          v8bf Am;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const __bf16 m = __builtin_bit_cast(__bf16, mring[(i - slot + 4 * hh + q) & (MR - 1)][32 * cb + n]);
+            Am[2 * q] = m;
+            Am[2 * q + 1] = m;
+          }
+          O[cb] = mfma32_bf16(Am, Br, O[cb]);
         }
       }
     }
@@ -518,19 +523,25 @@ __global__ __launch_bounds__(256, 2) void attn4_kernel(
     __syncthreads();  // every wave is done with stage st and sees stage st ^ 1
   }
 
-  if (!live) return;
+  // the last products feed the stores below, which some lanes skip: use
+  // every accumulator before that branch, so no product moves into it
+  asm volatile("" ::"v"(L));
+#pragma unroll
+  for (int cb = 0; cb < NO; ++cb)
+#pragma unroll
+    for (int e = 0; e < 16; e += 4) asm volatile("" ::"v"(O[cb][e]), "v"(O[cb][e + 1]), "v"(O[cb][e + 2]), "v"(O[cb][e + 3]));
   const int b = bh / H, h = bh % H;
   uint16_t* ob = o + b * oB + h * oH;
+  const int q = qt * kBlk + 32 * wq + n;
+  if (q >= S) return;
+  const float inv = 1.0f / L;
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int q = qt * kBlk + 32 * wq + 16 * s + lr;
-    if (q >= S) continue;
-    const float inv = 1.0f / L[s];
+  for (int cb = 0; cb < NO; ++cb) {
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      const int d = 16 * m + 4 * g;
-      const u32 lo = (u32)f32_to_bf16(O[s][m][0] * inv) | ((u32)f32_to_bf16(O[s][m][1] * inv) << 16);
-      const u32 hi = (u32)f32_to_bf16(O[s][m][2] * inv) | ((u32)f32_to_bf16(O[s][m][3] * inv) << 16);
+    for (int j = 0; j < 4; ++j) {
+      const int d = 32 * cb + 8 * j + 4 * hh;
+      const u32 lo = (u32)f32_to_bf16(O[cb][4 * j] * inv) | ((u32)f32_to_bf16(O[cb][4 * j + 1] * inv) << 16);
+      const u32 hi = (u32)f32_to_bf16(O[cb][4 * j + 2] * inv) | ((u32)f32_to_bf16(O[cb][4 * j + 3] * inv) << 16);
       *(uint2*)(ob + (int64_t)q * oS + d) = make_uint2(lo, hi);
     }
   }

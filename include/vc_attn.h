@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define VC_ABI_VERSION 6
+#define VC_ABI_VERSION 7
 
 typedef enum vc_status {
   VC_OK = 0,
@@ -385,19 +385,20 @@ int32_t vc_attn_fwd(const vc_shape* shape, const vc_attn_params* p, const uint8_
  * Layouts, per (b, h), nblk = ceil(S / 128), S_pad = 128 nblk:
  *   q4       uint8 [S_pad][D/2]: byte c = channels 2c (low nibble), 2c + 1;
  *   q4_scale uint8 [S_pad][D/32]: one E8M0 byte per 32 channels of a row;
- *   k4       per tile t, 64 D bytes: tile row 16 a + 4 g + v (a < 8, g < 4,
- *            v < 4), D/2 bytes as q4, holds key 128 t + 32 g + 4 a + v,
- *            its 16-byte chunk c at chunk c ^ sw4(r), sw4(r) = (r >> 2) & 3
- *            for D = 128, (r >> 3) & 1 for D = 64;
- *   k4_scale per tile 512 bytes: byte (16 c + (r & 15)) * 8 + (r >> 4) is
- *            the scale of tile row r, channels [32 c, 32 c + 32) (127 for
- *            c >= D/32);
+ *   k4       per tile t, 64 D bytes: tile row 64 c + 32 b + 8 j + 4 h + v
+ *            (c, b, h < 2, j, v < 4), D/2 bytes as q4, holds key
+ *            128 t + 64 c + 32 h + 16 b + 4 j + v, its 16-byte chunk x at
+ *            chunk x ^ sw4(r), sw4(r) = (r >> 2) & 3 for D = 128,
+ *            (r >> 3) & 1 for D = 64;
+ *   k4_scale per tile 512 bytes: byte (32 (x & 1) + (r & 31)) * 8
+ *            + 2 (r >> 5) + (x >> 1) is the scale of tile row r, channels
+ *            [32 x, 32 x + 32) (127 for x >= D/32);
  *   v4       per tile, D channel rows of 64 bytes: logical byte c of row d
  *            holds keys 128 t + 2c (low nibble) and 128 t + 2c + 1; the
  *            16-byte chunk c of row d sits at chunk c ^ ((d >> 2) & 3);
- *   v4_scale per tile 512 bytes: byte (16 g + (d & 15)) * 8 + (d >> 4) is
- *            the scale of channel d, keys [128 t + 32 g, 128 t + 32 g + 32)
- *            (127 for d >= D);
+ *   v4_scale per tile 512 bytes: byte (32 (g & 1) + (d & 31)) * 8
+ *            + 2 (d >> 5) + (g >> 1) is the scale of channel d, keys
+ *            [128 t + 32 g, 128 t + 32 g + 32) (127 for d >= D);
  * rows / keys >= S are zero codes and do not enter any block maximum.
  * q4, k4, v4 16-byte aligned; k4_scale, v4_scale 8-byte; mu_bf16 16-byte.
  */

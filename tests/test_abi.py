@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(vc):
 
 
 def test_abi_version_and_status_strings(vc):
-    assert vc.vc_abi_version() == vc.ABI_VERSION == 6
+    assert vc.vc_abi_version() == vc.ABI_VERSION == 7
     assert vc.vc_status_str(0) == "VC_OK"
     for s in range(1, 8):
         assert vc.vc_status_str(s).startswith("VC_ERR_")

@@ -45,8 +45,10 @@ def nibbles(b):
 
 
 def k4_row_of_key(k):
+    """Key 64 c + 32 h + 16 b + 4 j + v of a tile sits in tile row 64 c + 32 b + 8 j + 4 h + v."""
     k = np.asarray(k)
-    return 16 * ((k & 31) >> 2) + 4 * (k >> 5) + (k & 3)
+    c, h, b, j, v = k >> 6, (k >> 5) & 1, (k >> 4) & 1, (k >> 2) & 3, k & 3
+    return 64 * c + 32 * b + 8 * j + 4 * h + v
 
 
 def unswizzle(t, sw):
@@ -71,7 +73,7 @@ def unpack_k4(k4, k4s, D):
     codes = nibbles(unswizzle(k4, sw))[:, rows, :].reshape(nblk * 128, D)
     exps = np.zeros((nblk * 128, D // 32), np.int32)
     for c in range(D // 32):
-        idx = (16 * c + (rows & 15)) * 8 + (rows >> 4)
+        idx = (32 * (c & 1) + (rows & 31)) * 8 + 2 * (rows >> 5) + (c >> 1)
         exps[:, c] = (k4s[:, idx].astype(np.int32) - 127).reshape(-1)
     return codes, exps
 
@@ -84,7 +86,7 @@ def unpack_v4(v4, v4s, D):
     d = np.arange(D)
     exps = np.zeros((D, nblk * 4), np.int32)
     for g in range(4):
-        idx = (16 * g + (d & 15)) * 8 + (d >> 4)
+        idx = (32 * (g & 1) + (d & 31)) * 8 + 2 * (d >> 5) + (g >> 1)
         exps[:, g::4] = (v4s[:, idx].astype(np.int32) - 127).T
     return codes, exps
 
