@@ -19,14 +19,15 @@
 //    accumulator of key block kb = 2 c + b, register 4 j + v, in lane half h
 //    holds key 64 c + 32 h + 16 b + 4 j + v: lane half h then holds keys
 //    [64 c + 32 h, 64 c + 32 h + 32), one P block, in its own registers, in
-//    the order the P operand takes them.  The 16-byte chunk c of row r sits
-//    at chunk c ^ k4swz(r), so that the 16 rows a fragment read touches
+//    the order the P operand takes them.  The 16-byte chunk x of row r sits
+//    at chunk x ^ k4swz(r), so that the 16 rows a fragment read touches
 //    spread over all LDS banks.
-//    k4_scale per tile 512 bytes [h][n][kb][c] (the scale of tile row
-//    32 kb + n, channel block 2 c + h; 127 where 2 c + h >= D/32).
+//    k4_scale per tile 512 bytes [h][n][kb][cc] (the scale of tile row
+//    32 kb + n, channels [64 cc + 32 h, 64 cc + 32 h + 32); 127 where that
+//    block lies past D).
 //  - v4: per tile D channel rows of 64 bytes (keys 0..127 of the tile,
-//    key 2c in the low nibble of byte c; 16-byte chunk c of row d at chunk
-//    c ^ ((d >> 2) & 3)); v4_scale per tile 512 bytes [h][n][cb][c] (the
+//    key 2y in the low nibble of byte y; 16-byte chunk x of row d at chunk
+//    x ^ ((d >> 2) & 3)); v4_scale per tile 512 bytes [h][n][cb][c] (the
 //    scale of channel 32 cb + n, keys [64 c + 32 h, 64 c + 32 h + 32)).
 //  The bytes of one lane (h = lane / 32, n = lane % 32) are its 8 scale
 //  operands of a tile, read as one 8-byte load.
