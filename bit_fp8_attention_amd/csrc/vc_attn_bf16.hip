@@ -44,14 +44,14 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
   constexpr int NKC = D / 32;          // 32-wide d chunks of QK^T
   constexpr int TB = kHalf * D * 2;    // bytes of one K or V half-tile
   constexpr int NI = TB / 1024 / 4;    // 1 KB copies per issuing wave per half-tile
-  __shared__ __attribute__((aligned(1024))) uint8_t kst0[TB];
-  __shared__ __attribute__((aligned(1024))) uint8_t kst1[TB];
-  __shared__ __attribute__((aligned(1024))) uint8_t kst2[TB];
-  __shared__ __attribute__((aligned(1024))) uint8_t kst3[TB];
-  __shared__ __attribute__((aligned(1024))) uint8_t vst0[TB];
-  __shared__ __attribute__((aligned(1024))) uint8_t vst1[TB];
-  __shared__ __attribute__((aligned(1024))) uint8_t vst2[TB];
-  __shared__ __attribute__((aligned(1024))) uint8_t vst3[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t kring[4][TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t vring[4][TB];
+  uint8_t* const kst0 = kring[0];
+  uint8_t* const kst1 = kring[1];
+  uint8_t* const kst2 = kring[2];
+  uint8_t* const vst0 = vring[0];
+  uint8_t* const vst1 = vring[1];
+  uint8_t* const vst3 = vring[3];
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int pr = __builtin_amdgcn_readfirstlane(lin % npair);
@@ -95,15 +95,11 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
     lds_dma16_kb<NI>(vsrc + wq * NI * 1024 + l * 16, dst + wq * NI * 1024);
   };
   constexpr int GRP = 2 * NI;  // copies per half-A wave per step
-  // the stages of step i (i mod 4; picked at run time)
-  auto kst_of = [&](int i) -> uint8_t* {
-    const int c = i & 3;
-    return c == 0 ? kst0 : (c == 1 ? kst1 : (c == 2 ? kst2 : kst3));
-  };
-  auto vst_of = [&](int i) -> uint8_t* {
-    const int c = i & 3;
-    return c == 0 ? vst0 : (c == 1 ? vst1 : (c == 2 ? vst2 : vst3));
-  };
+  // the stages of step i (i mod 4; picked at run time): a shift, as one
+  // array per ring
+  auto kst_of = [&](int i) -> uint8_t* { return kring[i & 3]; };
+  auto vst_of = [&](int i) -> uint8_t* { return vring[i & 3]; };
+
 
   // the ragged last tile is steps 0, 1 or steps n - 2, n - 1
   const bool ragged = (S % kBlk) != 0;
