@@ -158,3 +158,33 @@ def test_attn4_parity(vc, S, D, vsmooth, seq):
         print(f"  head {h}: rel-L2 {err:.2e}, row max {row.max():.2e}", flush=True)
         assert err <= REL_L2_TOL, (h, err)
         assert row.max() <= REL_L2_TOL, (h, row.max())  # no row outside the bar either
+
+
+@pytest.mark.parametrize("S,window,vsmooth", [(1000, 0, False), (1000, 5, True), (700, 0, True)])
+def test_attn4_parity_windows(vc, S, window, vsmooth):
+    """Other mid-window widths: the visit order starts at tile min((qt | 1) + W, nblk - 1)."""
+    print(f"case attn4 S={S} window={window} vsmooth={vsmooth}", flush=True)
+    B, H, D = 1, 2, 128
+    q, k, v = vcsynth.random_qkv(B, S, H, D, seed=11 * S + window, v_kind="t3")
+    q = (q.float() * 2).to(torch.bfloat16)
+    sm = float(np.float32(1 / math.sqrt(D)))
+    kw, mu = {}, None
+    if vsmooth:
+        g = vc.vc_smooth_group(k.cuda(), v.cuda(), 16, 3, 11)
+        kw = dict(perm=g["perm"], mu_bf16=g["mu_bf16"])
+        mu = g["mu_bf16"]
+    z = vc.vc_quantize4(q.cuda(), k.cuda(), v.cuda(), sm_scale=sm, **kw)
+    o = vc.vc_attn_fwd4(z["q4"], z["q4_scale"], z["k4"], z["k4_scale"], z["v4"], z["v4_scale"], mu, S=S,
+                        window=window)
+    torch.cuda.synchronize()
+    og = o.float().cpu().numpy()
+    qb, kb, vb = (vcsynth.bf16_bits(x) for x in (q, k, v))
+    for h in range(H):
+        res = oracle.pipeline4_head(qb, kb, vb, 0, h, vsmooth=vsmooth, nclust=16, iters=3, seed=11, sm_scale=sm,
+                                    window=window)
+        emu = oracle.bf16_bits_to_f32(res["out_bf16"])
+        err = np.linalg.norm(og[0, :, h] - emu) / np.linalg.norm(emu)
+        row = np.linalg.norm(og[0, :, h] - emu, axis=1) / np.maximum(np.linalg.norm(emu, axis=1), 1e-30)
+        print(f"  head {h}: rel-L2 {err:.2e}, row max {row.max():.2e}", flush=True)
+        assert err <= REL_L2_TOL, (h, err)
+        assert row.max() <= REL_L2_TOL, (h, row.max())
