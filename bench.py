@@ -707,6 +707,8 @@ def main():
         tf = flops / (med["attn4"] * 1e-3) / 1e12
         mx4 = {"format": "MXFP4 (E2M1, E8M0 per 32)", "vsmooth": True, "quantize4_ms": med["quantize4"],
                "attn_ms": med["attn4"], "tflops": round(tf, 1), "frac_fp4_peak": round(tf / FP4_PEAK_TFLOPS, 4)}
+        if "bf16" in med:  # the comparison the pages make for their 4-bit path
+            mx4["speedup_over_bf16"] = round(med["bf16"] / med["attn4"], 3)
         log(f"mxfp4 path: {mx4}")
 
     cpu = None
