@@ -32,9 +32,9 @@
 //    other wave's codes;
 //  - S^T = K Q^T on v_mfma_f32_16x16x128_f8f6f4 (K = D = 128): the output
 //    puts one query and 4 keys in each lane; the packed V tile stores its keys
-//    in exactly the order in which those accumulators hand them to the P.V
-//    product's A operand, so codes go from the accumulator to the PV operand
-//    without any shuffle;
+//    in exactly the order in which those accumulators hand them, as codes, to
+//    the P.V product's B operand, so codes go from the accumulator to the PV
+//    operand without any shuffle;
 //  - K and V are stored tile-major and pre-swizzled (the packed layouts of
 //    vc_attn.h), so each 16 KB tile streams HBM -> LDS as one straight copy
 //    with global_load_lds_dwordx4 (no VGPR staging, no per-tile address
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
   constexpr int NM = D / 16;             // channel blocks of the output
   constexpr int TB = kBlk * D;           // bytes of one K or V tile
   constexpr int NI = TB / 1024 / 4;      // 1 KB copies per issuing wave per tile
-  // eight separate LDS objects, so the compiler can tell every stage apart
+  // the K and V rings: four 16 KB stages each
   __shared__ __attribute__((aligned(1024))) uint8_t kring[4][TB];
   __shared__ __attribute__((aligned(1024))) uint8_t vring[4][TB];
   uint8_t* const kst0 = kring[0];
