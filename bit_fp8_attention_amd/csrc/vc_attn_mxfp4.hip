@@ -382,16 +382,24 @@ __global__ __launch_bounds__(256, 2) void attn4_kernel(
     const uint8_t* Vt = vst[st];
     // S^T = K Q^T: key block kb is tile rows 32 kb + n (A operand), chunk c
     v16f Sc[4];
+    uint4 kv[4][NC];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int r = 32 * kb + n;
 #pragma unroll
+      for (int c = 0; c < NC; ++c) kv[kb][c] = *(const uint4*)(Kt + r * (D / 2) + 16 * ((2 * c + hh) ^ k4swz<D>(r)));
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const uint4 kv = *(const uint4*)(Kt + r * (D / 2) + 16 * ((2 * c + hh) ^ k4swz<D>(r)));
-        const v8i kf = {(int)kv.x, (int)kv.y, (int)kv.z, (int)kv.w, 0, 0, 0, 0};
+        const v8i kf = {(int)kv[kb][c].x, (int)kv[kb][c].y, (int)kv[kb][c].z, (int)kv[kb][c].w, 0, 0, 0, 0};
         Sc[kb] = mfma32_fp4(kf, qf[c], c == 0 ? cinit : Sc[kb], sbyte(ksc, 2 * kb + c), qsc[c]);
       }
     }
+    // every K fragment read goes out before the first score product
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 * NC, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * NC, 0);
     // V fragments of both chunks, read now so that their latency hides
     // behind the max and the probabilities: channel block cb is row
     // 32 cb + n, keys 64 cp + 32 hh .. + 31
