@@ -262,6 +262,18 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 VC_DEV v16f mfma32_fp4(v8i a, v8i b, v16f c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
 }
+// the same product with the A operand's E8M0 scale taken as byte k of the
+// 8 scale bytes s: the product's own byte select picks it out of its dword,
+// so no instruction extracts it (k is a constant once the loops unroll)
+VC_DEV v16f mfma32_fp4_sa(v8i a, v8i b, v16f c, const uint2& s, int k, int sb) {
+  const int w = (int)(k < 4 ? s.x : s.y);
+  switch (k & 3) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 0, w, 0, sb);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 1, w, 0, sb);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 2, w, 0, sb);
+    default: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 3, w, 0, sb);
+  }
+}
 VC_DEV v16f mfma32_bf16(v8bf a, v8bf b, v16f c) { return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0); }
 
 // max over the two 32-lane halves (lanes l and l ^ 32 hold the same query)
@@ -339,7 +351,6 @@ __global__ __launch_bounds__(256, 2) void attn4_kernel(
     ks = *(const uint2*)(k4s + t * 512 + l * 8);
     vs = *(const uint2*)(v4s + t * 512 + l * 8);
   };
-  auto sbyte = [](const uint2& s, int k) -> int { return (int)(((k < 4 ? s.x : s.y) >> (8 * (k & 3))) & 0xffu); };
 
   const v8i ones = {0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};  // E2M1 1.0
   v16f zero16;
@@ -394,7 +405,7 @@ __global__ __launch_bounds__(256, 2) void attn4_kernel(
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const v8i kf = {(int)kv[kb][c].x, (int)kv[kb][c].y, (int)kv[kb][c].z, (int)kv[kb][c].w, 0, 0, 0, 0};
-        Sc[kb] = mfma32_fp4(kf, qf[c], c == 0 ? cinit : Sc[kb], sbyte(ksc, 2 * kb + c), qsc[c]);
+        Sc[kb] = mfma32_fp4_sa(kf, qf[c], c == 0 ? cinit : Sc[kb], ksc, 2 * kb + c, qsc[c]);
       }
     }
     // every K fragment read goes out before the first score product
@@ -483,7 +494,7 @@ __global__ __launch_bounds__(256, 2) void attn4_kernel(
       for (int cb = 0; cb < NO; ++cb) {
         const uint4 vv = vf[cp][cb];
         const v8i a = {(int)vv.x, (int)vv.y, (int)vv.z, (int)vv.w, 0, 0, 0, 0};
-        O[cb] = mfma32_fp4(a, P[cp], O[cb], sbyte(vsc, 2 * cb + cp), pe[cp]);
+        O[cb] = mfma32_fp4_sa(a, P[cp], O[cb], vsc, 2 * cb + cp, pe[cp]);
       }
     };
     probs(0);
