@@ -251,13 +251,18 @@ __global__ __launch_bounds__(256) void kv4_tile_kernel(const uint16_t* __restric
 // whatever its size, so the 32x32 products, each twice the work of a
 // 16x16x128 one, take half as many of those cycles.  Per tile:
 // S^T = K Q^T (scores in log2 units; tile row 32 kb + 8 j + 4 h + v of key
-// block kb lands in register 4 j + v of lane half h), the running max on
-// the true scores, p = 2^(s - M) (v_exp_f32), one E8M0 scale per lane and
+// block kb lands in register 4 j + v of lane half h), the running max as
+// an integer (rises within a headroom left unapplied), p = 2^(s - M)
+// (v_exp_f32), one E8M0 scale per lane and
 // 64-key chunk (its 32 keys: one P block), E2M1 codes, then the row sum
 // (ones x P^T) and A^T += V^T P^T on the block-scaled matrix cores, and with
 // V-Smooth the block mean restored as A += r mu.
 
 typedef float v16f __attribute__((ext_vector_type(16)));
+
+// how far a tile's max may exceed the running max before it is applied
+// (log2 units)
+constexpr float kHeadroom4 = 8.0f;
 
 VC_DEV v16f mfma32_fp4(v8i a, v8i b, v16f c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
@@ -356,9 +361,9 @@ __global__ __launch_bounds__(256, 2) void attn4_kernel(
   v16f zero16;
 #pragma unroll
   for (int e = 0; e < 16; ++e) zero16[e] = 0.f;
-  // M: running max of query n (log2 units); the score product starts its
-  // accumulator at -M, so it emits s - M directly (0 before the first tile,
-  // which always sets M)
+  // M: running max of query n (log2 units, an integer); the score product
+  // starts its accumulator at -M, so it emits s - M directly (0 before the
+  // first tile, which always sets M)
   float M = 0.f;
   v16f cinit = zero16;
   float L = 0.f;
@@ -445,12 +450,18 @@ __global__ __launch_bounds__(256, 2) void attn4_kernel(
         m = __builtin_fmaxf(__builtin_fmaxf(m, Sc[2 * cp + (e >> 4)][e & 15]), Sc[2 * cp + (e >> 4)][(e & 15) + 1]);
       lm[cp] = m;
     }
+    // M is an integer (log2 units), the ceiling of the scores' max: a
+    // rescale is then an exact power of two, and moving M by an integer n
+    // moves each P block's exponent by n and none of its codes.  So a rise
+    // of at most kHeadroom4 is left unapplied (p then stays below 2^9): the
+    // output is the same, and most tiles skip the rescale ([OVC] "Mid-window
+    // key traversal": without ExpCast a stale maximum has headroom)
     const float rm = max_over_halves(__builtin_fmaxf(lm[0], lm[1]));  // the row's max of s - M
-    const bool rise = i == 0 || rm > 0.0f;
+    const bool rise = i == 0 || rm > kHeadroom4;
     if (__any(rise)) {
-      const float delta = rise ? -rm : 0.0f;  // M - M'
+      const float delta = rise ? -__builtin_ceilf(rm) : 0.0f;  // M - M', an integer
       if (i != 0) {
-        const float alpha = __builtin_amdgcn_exp2f(delta);
+        const float alpha = __builtin_ldexpf(1.0f, (int)delta);
         L *= alpha;
         if (VS) {
 #pragma unroll

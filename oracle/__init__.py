@@ -32,6 +32,7 @@ _lib = None
 
 SEQUENTIAL = 1
 EXACT_EXP = 2
+DEFER4 = 4  # 4-bit path: rises within the headroom of 8 left unapplied
 
 # preprocessing flags (vco_prep_rows)
 PREP_ROPE = 1

@@ -587,6 +587,12 @@ EXPORT void vco_tile_order(int32_t qt, int32_t nblk, int32_t window, int32_t seq
 
 #define VCO_SEQUENTIAL 1
 #define VCO_EXACT_EXP 2
+/* 4-bit path: a tile whose maximum exceeds the running max M by at most
+ * VCO_HEADROOM4 leaves M as it is (the headroom a path without ExpCast has,
+ * [OVC] "Mid-window key traversal"); with an integer M this changes no
+ * output (vco_attn4_emulate_rows) */
+#define VCO_DEFER4 4
+#define VCO_HEADROOM4 8.0f
 
 /*
  * q_codes [S_pad][D] with q_scale [nblk] (query rows in token order),
@@ -695,8 +701,9 @@ EXPORT void vco_attn_emulate_rows(const uint8_t* q_codes, const float* q_scale, 
 /* reached with that scale); Q/K blocks are 32 channels of a row (Q first   */
 /* multiplied by fl(sm_scale * log2 e), so scores come out in log2 units);  */
 /* V (or V-Smooth's residual) and P blocks are 32 consecutive keys of a     */
-/* 128-key tile, per channel and per query row; p = fl32(2^fl32(s - M))     */
-/* with the running max M over the true scores, every increase applied;    */
+/* 128-key tile, per channel and per query row; p = fl32(2^(s - M)) with    */
+/* M the running max rounded up to an integer (log2 units; s - M is then   */
+/* exact), every increase of that integer applied;                          */
 /* the row sum adds the dequantised P; the block mean is restored per tile  */
 /* as A += r mu ([VC] §3.2 Eq. 6).                                           */
 /* ------------------------------------------------------------------------ */
@@ -765,6 +772,11 @@ EXPORT void vco_mxfp4_cols(const float* x, int32_t S, int32_t D, uint8_t* codes_
 
 /*
  * 4-bit attention, one query row at a time (rows in token order).
+ * The running max is kept as an integer M (log2 units): a rescale is then an
+ * exact power of two, and moving M by an integer n moves each P block's
+ * exponent by n and leaves its codes as they are.  So whether a rise is
+ * applied at once or later (VCO_DEFER4) does not change the output, which is
+ * what lets the kernel skip the rescale of most rises.
  * q_codes [S_pad][D] / q_exps [S_pad][D/32] (Q carrying fl(sm log2 e)),
  * k_codes, k_exps likewise, v_codes_t [D][S_pad] / v_exps [D][S_pad/32],
  * mu [nblk][D] fp32 block means or NULL (plain).  Key blocks in the order
@@ -800,8 +812,9 @@ EXPORT void vco_attn4_emulate_rows(const uint8_t* q_codes, const int32_t* q_exps
         acc[kk - k0] = (float)s;
         mx = fmaxf(mx, acc[kk - k0]);
       }
-      const float Mn = fmaxf(M, mx);
-      if (Mn > M) {
+      const float Mn = fmaxf(M, ceilf(mx));
+      const int defer = (flags & VCO_DEFER4) && M != -INFINITY && mx - M <= VCO_HEADROOM4;
+      if (Mn > M && !defer) {
         if (M != -INFINITY) {
           const double alpha = exp2((double)M - (double)Mn);
           for (int32_t d = 0; d < D; ++d) A[d] *= alpha;
@@ -810,7 +823,7 @@ EXPORT void vco_attn4_emulate_rows(const uint8_t* q_codes, const int32_t* q_exps
         }
         M = Mn;
       }
-      for (int32_t kk = k0; kk < k1; ++kk) p[kk - k0] = (float)exp2((double)(acc[kk - k0] - M));
+      for (int32_t kk = k0; kk < k1; ++kk) p[kk - k0] = (float)exp2((double)acc[kk - k0] - (double)M);
       double r = 0.0;
       for (int32_t b0 = k0; b0 < k1; b0 += 32) { /* P's blocks of 32 keys */
         const int32_t b1 = b0 + 32 < k1 ? b0 + 32 : k1;

@@ -160,6 +160,40 @@ def test_attn4_parity(vc, S, D, vsmooth, seq):
         assert row.max() <= REL_L2_TOL, (h, row.max())  # no row outside the bar either
 
 
+@pytest.mark.parametrize("vsmooth,seq", [(False, True), (True, False), (False, False)])
+def test_attn4_parity_large_rises(vc, vsmooth, seq):
+    """Keys of tile t scaled by 1 + 3 t: the running max rises past the
+    kernel's headroom after the first tile, so the applied-rescale path runs.
+    The oracle follows the kernel's rule here (DEFER4: rises within the
+    headroom unapplied), which the CPU pins show gives the same output as
+    applying every rise of the integer max, and counts the applied rises."""
+    from test_oracle_mxfp4 import rising_keys
+    print(f"case attn4 large rises vsmooth={vsmooth} seq={seq}", flush=True)
+    B, H, S, D = 1, 2, 1000, 128
+    q, k, v = vcsynth.random_qkv(B, S, H, D, seed=5 + seq, v_kind="t3")
+    k = rising_keys(k, 3)
+    sm = float(np.float32(1 / math.sqrt(D)))
+    kw, mu = {}, None
+    if vsmooth:
+        g = vc.vc_smooth_group(k.cuda(), v.cuda(), 16, 3, 11)
+        kw = dict(perm=g["perm"], mu_bf16=g["mu_bf16"])
+        mu = g["mu_bf16"]
+    z = vc.vc_quantize4(q.cuda(), k.cuda(), v.cuda(), sm_scale=sm, **kw)
+    o = vc.vc_attn_fwd4(z["q4"], z["q4_scale"], z["k4"], z["k4_scale"], z["v4"], z["v4_scale"], mu, S=S,
+                        sequential=seq)
+    torch.cuda.synchronize()
+    og = o.float().cpu().numpy()
+    qb, kb, vb = (vcsynth.bf16_bits(x) for x in (q, k, v))
+    for h in range(H):
+        res = oracle.pipeline4_head(qb, kb, vb, 0, h, vsmooth=vsmooth, nclust=16, iters=3, seed=11, sm_scale=sm,
+                                    flags=(oracle.SEQUENTIAL if seq else 0) | oracle.DEFER4)
+        assert (res["stats"][:, 0] >= 1).mean() > 0.5  # most rows apply a rise after tile 0
+        emu = oracle.bf16_bits_to_f32(res["out_bf16"])
+        row = np.linalg.norm(og[0, :, h] - emu, axis=1) / np.maximum(np.linalg.norm(emu, axis=1), 1e-30)
+        print(f"  head {h}: row max rel-L2 {row.max():.2e}", flush=True)
+        assert row.max() <= REL_L2_TOL, (h, row.max())
+
+
 @pytest.mark.parametrize("S,window,vsmooth", [(1000, 0, False), (1000, 5, True), (700, 0, True)])
 def test_attn4_parity_windows(vc, S, window, vsmooth):
     """Other mid-window widths: the visit order starts at tile min((qt | 1) + W, nblk - 1)."""

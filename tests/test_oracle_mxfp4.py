@@ -174,3 +174,60 @@ def test_pipeline4_tracks_exact_attention():
         res = oracle.pipeline4_head(qb, kb, vb, 0, 0, vsmooth=vs, nclust=8, iters=3, seed=1, sm_scale=sm)
         err = np.linalg.norm(res["out_f32"] - ref) / np.linalg.norm(ref)
         assert 0.1 < err < 0.35, (vs, err)
+
+
+def _scores_of(res, row):
+    """The row's log2 scores from the emulation's own codes, recomputed in
+    float64 (products of E2M1 values and powers of two are exact)."""
+    qd = oracle.e2m1_decode(res["q_codes"][row]) * np.exp2(np.repeat(res["q_exps"][row], 32))
+    kd = oracle.e2m1_decode(res["k_codes"]) * np.exp2(np.repeat(res["k_exps"], 32, axis=1))
+    return (kd @ qd).astype(np.float32)
+
+
+@pytest.mark.parametrize("vs", [False, True])
+def test_attn4_running_max_is_the_integer_ceiling(vs):
+    # the running max is an integer: the ceiling of the row's largest score
+    import vcsynth
+    S, D = 700, 64
+    q, k, v = vcsynth.random_qkv(1, S, 1, D, seed=11)
+    qb, kb, vb = (vcsynth.bf16_bits(x) for x in (q, k, v))
+    rows = np.array([0, 1, 130, 311, 699])
+    res = oracle.pipeline4_head(qb, kb, vb, 0, 0, vsmooth=vs, nclust=8, iters=2, seed=2, rows=rows)
+    for j, r in enumerate(rows):
+        s = _scores_of(res, r)[:S]
+        assert res["stats"][j, 1] == math.ceil(float(s.max()))
+        assert res["stats"][j, 1] == int(res["stats"][j, 1])
+
+
+def rising_keys(k, step):
+    """Keys of tile t scaled by 1 + step t (bf16 [B,S,H,D]), so that in key
+    order each tile's scores reach well past the last one's: rises beyond
+    any headroom."""
+    import torch
+    t = torch.arange(k.shape[1]) // 128
+    return (k.float() * (1 + step * t).float()[None, :, None, None]).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("vs,flags,rising", [(False, 0, False), (True, 0, False), (True, oracle.SEQUENTIAL, False),
+                                             (False, oracle.SEQUENTIAL, False), (False, oracle.SEQUENTIAL, True),
+                                             (True, 0, True)])
+def test_attn4_deferred_rises_change_no_output(vs, flags, rising):
+    # with an integer running max, a rise left unapplied (within the headroom
+    # of 8) moves every P block's exponent by an integer and no code: the
+    # output is the same, bit for bit, with far fewer rescales.  A max kept
+    # fractional (the true max) would fail this.
+    import vcsynth
+    S, D = 1000, 64
+    q, k, v = vcsynth.random_qkv(1, S, 1, D, seed=12)
+    if rising:
+        k = rising_keys(k, 2)
+    qb, kb, vb = (vcsynth.bf16_bits(x) for x in (q, k, v))
+    rows = np.arange(0, S, 3)
+    kw = dict(vsmooth=vs, nclust=8, iters=2, seed=4, rows=rows, sm_scale=0.3)
+    eager = oracle.pipeline4_head(qb, kb, vb, 0, 0, flags=flags, **kw)
+    lazy = oracle.pipeline4_head(qb, kb, vb, 0, 0, flags=flags | oracle.DEFER4, **kw)
+    assert np.array_equal(eager["out_f32"], lazy["out_f32"])
+    if rising:  # rises past the headroom are applied, after the first tile too
+        assert (lazy["stats"][:, 0] >= 1).mean() > 0.5
+    else:
+        assert eager["stats"][:, 0].sum() > 2 * lazy["stats"][:, 0].sum()
