@@ -12,7 +12,11 @@
 // What differs is the arithmetic the pages contrast with ExpCast ([VC] §3.1
 // Eq. 1, §3.3; [OVC] opening paragraph): BF16 matrix-core products
 // (v_mfma_f32_16x16x32_bf16), and per score an fp32 exponential
-// p = exp2(acc * scale * log2 e - m) followed by a cast to bf16.  A step is
+// p = exp2(acc * scale * log2 e - m) followed by a cast to bf16.  As in a
+// BF16 FlashAttention-4 kernel, a rise of the running max m of at most
+// kHeadroom is left unapplied ([OVC] "Mid-window key traversal": without
+// ExpCast a stale maximum has headroom; the probabilities then stay below
+// 2^9, where bf16 keeps the same relative precision).  A step is
 // a 64-key half-tile, so the bf16 K and V stages (16 KB each) fill the same
 // 128 KB of rings as the FP8 kernel's 128-key tiles.
 #include "vc_common.hpp"
@@ -23,6 +27,9 @@ namespace vc {
 namespace {
 
 constexpr int kHalf = 64;  // keys per step
+// how far a step's max may exceed the running max before it is applied
+// (log2 units)
+constexpr float kHeadroom = 8.0f;
 
 // K half-tile in LDS: 64 rows x 2D bytes; 16-byte chunk c of row r sits at
 // chunk c ^ swb(r) (rows read together by a fragment differ in bits 0,1,3,4).
@@ -229,7 +236,8 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
       for (int e = 2; e < 16; e += 2)
         mx = __builtin_fmaxf(__builtin_fmaxf(mx, Sc[s][e >> 2][e & 3]), Sc[s][(e + 1) >> 2][(e + 1) & 3]);
       mx = max_over_groups(mx);
-      const float Mn = __builtin_fmaxf(M[s], c1 * mx);
+      // the first step always applies (M = -inf before it)
+      const float Mn = c1 * mx > M[s] + kHeadroom ? c1 * mx : M[s];
       if (__any(Mn > M[s])) {
         const float alpha = exp2f(M[s] - Mn);
         Lq[s] *= alpha;
