@@ -305,6 +305,7 @@ def cpu_baseline(w, q, k, v, target_s=12.0):
 FP4_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 matrix-core peak
 HBM_PEAK_GBPS = 8000.0
 ROUNDS = 31                # launches per leg in the interleaved sampling (median of these)
+SETTLE_S = 2.0             # seconds of whole steps before anything is timed
 
 
 class ClockSampler:
@@ -567,6 +568,15 @@ def main():
         if e:
             e[3].record()
             ev.append(e)
+
+    # ---- the clock and board power settle under load: the whole step,
+    # repeated for at least 2 s, before anything is timed
+    t_s, n_s = time.perf_counter(), 0
+    while time.perf_counter() - t_s < SETTLE_S:
+        step()
+        torch.cuda.synchronize()
+        n_s += 1
+    log(f"settle: {n_s} steps in {time.perf_counter() - t_s:.1f} s")
 
     # ---- the step contract: W untimed steps, then exactly K whole-path steps
     for i in range(args.warmup):
