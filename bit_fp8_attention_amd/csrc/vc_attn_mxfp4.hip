@@ -55,7 +55,10 @@ VC_DEV int mx_block_exp_prob(float p) {
 
 // 8 fp32 -> 8 E2M1 nibbles (one dword, element i in nibble i) at scale 2^e
 VC_DEV u32 cvt8_fp4(const float (&x)[8], float scale) {
-  u32 w = 0u;
+  // the four conversions below write every byte of w: it starts from an
+  // unset register (an empty asm defines it), not from a zero written first
+  u32 w;
+  asm volatile("" : "=v"(w));
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[0], x[1], scale, 0);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[2], x[3], scale, 1);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[4], x[5], scale, 2);
