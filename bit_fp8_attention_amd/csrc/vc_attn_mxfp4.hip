@@ -46,7 +46,8 @@ VC_DEV int mx_block_exp(float amax) {
   return e;
 }
 
-// mx_block_exp for a block's maximum p = 2^lm (finite), without the loop: with p = m 2^f, m in [0.5, 1), the answer is f - 3, plus one when
+// mx_block_exp for a block's maximum p = 2^lm (finite), without the loop:
+// with p = m 2^f, m in [0.5, 1), the answer is f - 3, plus one when
 // m > 0.75 (then 6 2^(f - 3) = 0.75 2^f < p), at least -127; 0 for p = 0
 VC_DEV int mx_block_exp_prob(float p) {
   const int e = __builtin_amdgcn_frexp_expf(p) - 3 + (__builtin_amdgcn_frexp_mantf(p) > 0.75f ? 1 : 0);
