@@ -380,6 +380,7 @@ __global__ __launch_bounds__(256, 2) void attn4_kernel(
   //   mean side: (mu, mu)   (mu is exact in bf16)
   //   sum side:  (r.hi, r.lo)
   float rb[4] = {0.f, 0.f, 0.f, 0.f};
+  const bool hi_half = hh != 0;
   if (VS) {  // rows never written must read as finite zeros
     for (int e2 = tid; e2 < MR * D; e2 += 256) (&mring[0][0])[e2] = 0;
     __syncthreads();
@@ -523,9 +524,12 @@ __global__ __launch_bounds__(256, 2) void attn4_kernel(
     L += rr;
     if (VS) {
       const int slot = i & 7;
+      // the lanes whose half carries this slot (a lane mask picked by a
+      // scalar test, so the selects below need no per-lane compare)
+      const bool mine = (slot >> 2) ? hi_half : !hi_half;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        if (slot == 4 * hh + q) rb[q] = rr;
+        if (mine && (slot & 3) == q) rb[q] = rr;
       if (slot == 7 || i == nblk - 1) {
         v8bf Br;
 #pragma unroll
