@@ -55,9 +55,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
   __shared__ __attribute__((aligned(1024))) uint8_t vring[4][TB];
   uint8_t* const kst0 = kring[0];
   uint8_t* const kst1 = kring[1];
-  uint8_t* const kst2 = kring[2];
   uint8_t* const vst0 = vring[0];
-  uint8_t* const vst1 = vring[1];
   uint8_t* const vst3 = vring[3];
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
@@ -88,18 +86,23 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
     krow[r] = p / (D * 2);
     kcol[r] = (((p % (D * 2)) / 16) ^ (D == 128 ? swb(krow[r]) : (swb(krow[r]) & 7))) * 8;
   }
-  auto issue_k = [&](uint8_t* dst, int j) {
+  // copy destinations as LDS addresses, taken once: a stage is an integer
+  // offset from its ring
+  const unsigned kring_a = lds_addr_of(kring), vring_a = lds_addr_of(vring);
+  auto kdst = [&](int i) { return kring_a + (unsigned)((i & 3) * TB); };
+  auto vdst = [&](int i) { return vring_a + (unsigned)((i & 3) * TB); };
+  auto issue_k = [&](unsigned dst, int j) {
     const int key0 = tile_at(j >> 1) * kBlk + (j & 1) * kHalf;
 #pragma unroll
     for (int r = 0; r < NI; ++r) {
       const int key = min(key0 + krow[r], S - 1);  // rows past S are masked; any valid row will do
-      lds_dma16_raw(kbp + (int64_t)key * kS + kcol[r], dst + (r * 4 + wq) * 1024);
+      lds_dma16_at(kbp + (int64_t)key * kS + kcol[r], dst + (unsigned)((r * 4 + wq) * 1024));
     }
   };
   // V half-tiles are contiguous: the wave's NI consecutive 1 KB blocks under one M0
-  auto issue_v = [&](uint8_t* dst, int j) {
+  auto issue_v = [&](unsigned dst, int j) {
     const uint8_t* vsrc = vb + ((int64_t)tile_at(j >> 1) * 2 + (j & 1)) * TB;
-    lds_dma16_kb<NI>(vsrc + wq * NI * 1024 + l * 16, dst + wq * NI * 1024);
+    lds_dma16_kb_at<NI>(vsrc + wq * NI * 1024 + l * 16, dst + (unsigned)(wq * NI * 1024));
   };
   constexpr int GRP = 2 * NI;  // copies per half-A wave per step
   // the stages of step i (i mod 4; picked at run time): a shift, as one
@@ -114,11 +117,11 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
   const bool tail_last = ragged && !tail_first;
 
   if (!hb) {  // prologue (half A): K_0, V_0, K_1, then K_2, V_1; K_0 must have landed before M(0)
-    issue_k(kst0, 0);
-    issue_v(vst0, 0);
-    if (1 < n) issue_k(kst1, 1);
-    if (2 < n) issue_k(kst2, 2);
-    if (1 < n) issue_v(vst1, 1);
+    issue_k(kdst(0), 0);
+    issue_v(vdst(0), 0);
+    if (1 < n) issue_k(kdst(1), 1);
+    if (2 < n) issue_k(kdst(2), 2);
+    if (1 < n) issue_v(vdst(1), 1);
     if (n >= 3)
       wait_vm_n<4 * NI>();
     else
@@ -259,8 +262,8 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(const uint16_t* __res
     // wait until only these and the previous step's copies are in flight,
     // so the barrier ending this slot publishes K_{j+1} and V_j
     if (!hb) {
-      if (j + 3 < n) issue_k(kst_of(j + 3), j + 3);
-      if (j + 2 < n) issue_v(vst_of(j + 2), j + 2);
+      if (j + 3 < n) issue_k(kdst(j + 3), j + 3);
+      if (j + 2 < n) issue_v(vdst(j + 2), j + 2);
       if (j + 3 < n)
         wait_vm_n<2 * GRP>();
       else

@@ -132,10 +132,7 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t kring[4][TB];
   __shared__ __attribute__((aligned(1024))) uint8_t vring[4][TB];
   uint8_t* const kst0 = kring[0];
-  uint8_t* const kst1 = kring[1];
-  uint8_t* const kst2 = kring[2];
   uint8_t* const vst0 = vring[0];
-  uint8_t* const vst1 = vring[1];
   uint8_t* const vst3 = vring[3];
   // V-Smooth: ring of the scaled block-mean rows (bf16 hi | lo << 16 per
   // channel) of the last 16 visited tiles (one 8-tile restoration window
@@ -194,14 +191,19 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
   // wq NI KB on, under one M0; with V-Smooth (half A) also bytes
   // [wq D, (wq + 1) D) of the tile's mean row (D / 16 lanes), issued first
   // in a group, so that a read of the ring waits for no tile
+  // copy destinations as LDS addresses: the rings' addresses are taken once
+  // and a stage is an integer offset from them
+  const unsigned kring_a = lds_addr_of(kring), vring_a = lds_addr_of(vring), mring_a = lds_addr_of(mring);
+  auto kdst = [&](int i) { return kring_a + (unsigned)((i & 3) * TB); };
+  auto vdst = [&](int i) { return vring_a + (unsigned)((i & 3) * TB); };
   auto issue_mu = [&](int i) {
     if (VS) {
       const uint8_t* msrc = (const uint8_t*)(mu + ((int64_t)bh * nblk + tile_at(i)) * D) + wq * D;
-      if (l < D / 16) lds_dma16_raw(msrc + loff, (uint8_t*)&mring[i & (MR - 1)][0] + wq * D);
+      if (l < D / 16) lds_dma16_at(msrc + loff, mring_a + (unsigned)((i & (MR - 1)) * D * 4 + wq * D));
     }
   };
-  auto issue_k = [&](uint8_t* dst, int i) { lds_dma16_kb<NI>(ksrc(i) + wq * NI * 1024 + loff, dst + wq * NI * 1024); };
-  auto issue_v = [&](uint8_t* dst, int i) { lds_dma16_kb<NI>(vsrc(i) + wq * NI * 1024 + loff, dst + wq * NI * 1024); };
+  auto issue_k = [&](unsigned dst, int i) { lds_dma16_kb_at<NI>(ksrc(i) + wq * NI * 1024 + loff, dst + wq * NI * 1024); };
+  auto issue_v = [&](unsigned dst, int i) { lds_dma16_kb_at<NI>(vsrc(i) + wq * NI * 1024 + loff, dst + wq * NI * 1024); };
   constexpr int GRP_A = VS ? 2 * NI + 1 : NI;  // copies per half-A wave per V phase
 
   const FragBase<D> fb(lr, g);
@@ -218,12 +220,12 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
   // K_2, V_1); K_0 must have landed before M(0)
   if (!hb) {
     issue_mu(0);
-    issue_k(kst0, 0);
-    issue_v(vst0, 0);
-    if (n > 1) issue_k(kst1, 1);
+    issue_k(kdst(0), 0);
+    issue_v(vdst(0), 0);
+    if (n > 1) issue_k(kdst(1), 1);
     if (1 < n) issue_mu(1);
-    if (2 < n) issue_k(kst2, 2);
-    if (1 < n) issue_v(vst1, 1);
+    if (2 < n) issue_k(kdst(2), 2);
+    if (1 < n) issue_v(vdst(1), 1);
     if (n >= 3)
       wait_vm_n<4 * NI + (VS ? 1 : 0)>();
     else
@@ -482,14 +484,14 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
     // phases)
     if (!hb) {
       if (j + 2 < n) issue_mu(j + 2);
-      if (j + 3 < n) issue_k(kst_of(j + 3), j + 3);
-      if (VS && j + 2 < n) issue_v(vst_of(j + 2), j + 2);
+      if (j + 3 < n) issue_k(kdst(j + 3), j + 3);
+      if (VS && j + 2 < n) issue_v(vdst(j + 2), j + 2);
       if (j + 3 < n)
         wait_vm_n<2 * GRP_A>();
       else
         wait_vm();
     } else if (!VS) {
-      if (j + 2 < n) issue_v(vst_of(j + 2), j + 2);
+      if (j + 2 < n) issue_v(vdst(j + 2), j + 2);
     }
   };
 

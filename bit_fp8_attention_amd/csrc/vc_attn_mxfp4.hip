@@ -335,23 +335,27 @@ __global__ __launch_bounds__(256, 2) void attn4_kernel(
   // copies of tile i into stage st: each wave a quarter of the K and of the V tile
   constexpr int CW = TB / 4;  // bytes per wave (2 KB at D = 128)
   const unsigned loff = (unsigned)l * 16u;
+  // (destinations as LDS addresses, taken once: a stage is an integer offset)
+  const unsigned kst_a = lds_addr_of(kst), vst_a = lds_addr_of(vst), mring_a = lds_addr_of(mring);
   auto issue = [&](int i, int st) {
     const int64_t t = (int64_t)bh * nblk + tile_at(i);
     const uint8_t* ks = k4 + t * TB + w * CW;
     const uint8_t* vs = v4 + t * TB + w * CW;
+    const unsigned kd = kst_a + (unsigned)(st * TB + w * CW), vd = vst_a + (unsigned)(st * TB + w * CW);
     if constexpr (CW == 2048) {  // two 1 KB blocks under one M0 each
-      lds_dma16_kb<2>(ks + loff, &kst[st][w * CW]);
-      lds_dma16_kb<2>(vs + loff, &vst[st][w * CW]);
+      lds_dma16_kb_at<2>(ks + loff, kd);
+      lds_dma16_kb_at<2>(vs + loff, vd);
     } else {
 #pragma unroll
       for (int r = 0; r < (CW + 1023) / 1024; ++r) {
         if (l * 16 < CW - 1024 * r) {
-          lds_dma16_raw(ks + 1024 * r + loff, &kst[st][w * CW + 1024 * r]);
-          lds_dma16_raw(vs + 1024 * r + loff, &vst[st][w * CW + 1024 * r]);
+          lds_dma16_at(ks + 1024 * r + loff, kd + 1024 * r);
+          lds_dma16_at(vs + 1024 * r + loff, vd + 1024 * r);
         }
       }
     }
-    if (VS && w == 0 && l < D / 8) lds_dma16_raw((const uint8_t*)(mu + t * D) + loff, &mring[i & (MR - 1)][0]);
+    if (VS && w == 0 && l < D / 8)
+      lds_dma16_at((const uint8_t*)(mu + t * D) + loff, mring_a + (unsigned)((i & (MR - 1)) * (VS ? D : 8) * 2));
   };
   // per-lane scale bytes of tile i: K byte 2 kb + c, V byte 2 cb + c
   auto load_scales = [&](int i, uint2& ks, uint2& vs) {

@@ -134,10 +134,18 @@ VC_DEV void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 // counts and drains every LDS read before its first use.  Hidden from it,
 // the fragment reads get exact partial waits; the kernel orders the copies
 // itself with explicit vmcnt waits and barriers.
-VC_DEV void lds_dma16_raw(const void* g, void* lds_base) {
-  const unsigned lds = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)LDS_PTR(lds_base));
+VC_DEV void lds_dma16_at(const void* g, unsigned lds_addr) {
+  const unsigned lds = __builtin_amdgcn_readfirstlane(lds_addr);
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
 }
+
+// The LDS address of a pointer into a __shared__ array.  The cast from a
+// generic pointer tests it for null (a scalar compare and select each
+// time), so a kernel that copies in a loop takes its arrays' addresses once
+// and adds offsets in integer arithmetic.
+VC_DEV unsigned lds_addr_of(const void* p) { return (unsigned)(uintptr_t)LDS_PTR(p); }
+
+VC_DEV void lds_dma16_raw(const void* g, void* lds_base) { lds_dma16_at(g, lds_addr_of(lds_base)); }
 
 // NB consecutive 1 KB copies under one M0: lane i of copy r reads
 // g + 1024 r and lands at lds_base + 1024 r + 16 i.  The instruction's
@@ -145,9 +153,9 @@ VC_DEV void lds_dma16_raw(const void* g, void* lds_base) {
 // copies need one M0 write between them (a wave's copies issue about a
 // quarter faster than with an M0 write before each, measured).
 template <int NB>
-VC_DEV void lds_dma16_kb(const void* g, void* lds_base) {
+VC_DEV void lds_dma16_kb_at(const void* g, unsigned lds_addr) {
   static_assert(NB == 2 || NB == 4, "2 or 4 KB per call");
-  const unsigned lds = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)LDS_PTR(lds_base));
+  const unsigned lds = __builtin_amdgcn_readfirstlane(lds_addr);
   if constexpr (NB == 4)
     asm volatile(
         "s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off\n\tglobal_load_lds_dwordx4 %0, off offset:1024\n\t"
@@ -159,6 +167,11 @@ VC_DEV void lds_dma16_kb(const void* g, void* lds_base) {
                      g),
                  "s"(lds)
                  : "memory", "m0");
+}
+
+template <int NB>
+VC_DEV void lds_dma16_kb(const void* g, void* lds_base) {
+  lds_dma16_kb_at<NB>(g, lds_addr_of(lds_base));
 }
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
