@@ -296,9 +296,13 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
     if constexpr (K0 < K1) fr[K0 % 3] = frag(std::integral_constant<int, K0>{});
     if constexpr (K0 + 1 < K1) fr[(K0 + 1) % 3] = frag(std::integral_constant<int, K0 + 1>{});
     float rr[2] = {0.f, 0.f};
+    v4f rsum[2];
     if constexpr (PV) {
 #pragma unroll
-      for (int s = 0; s < 2; ++s) rr[s] = mfma_fp8(ones, P[s], zero4)[0];
+      for (int s = 0; s < 2; ++s) {
+        rsum[s] = mfma_fp8(ones, P[s], zero4);
+        rr[s] = rsum[s][0];
+      }
     }
     static_for<K0, K1>([&](auto kk) {
       constexpr int k = decltype(kk)::value;
@@ -336,6 +340,11 @@ __global__ __launch_bounds__(512, 1) void attn_fp8_kernel(
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       });
     }
+    // with V-Smooth the row sums' whole results stay allocated through the
+    // chain: with three of their four registers free, the compiler wrote into
+    // one while the product was still in flight, which cost a hazard wait
+    // (measured faster with V-Smooth, slightly slower on the plain path)
+    if constexpr (PV && VS) asm volatile("" ::"v"(rsum[0]), "v"(rsum[1]));
     // keep the score products in this block, ahead of the mean-restoration
     // branch: the block-scaled products were otherwise moved below it, out
     // of the interleaving above
