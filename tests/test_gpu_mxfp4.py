@@ -167,11 +167,10 @@ def test_attn4_parity_large_rises(vc, vsmooth, seq):
     The oracle follows the kernel's rule here (DEFER4: rises within the
     headroom unapplied), which the CPU pins show gives the same output as
     applying every rise of the integer max, and counts the applied rises."""
-    from test_oracle_mxfp4 import rising_keys
     print(f"case attn4 large rises vsmooth={vsmooth} seq={seq}", flush=True)
     B, H, S, D = 1, 2, 1000, 128
     q, k, v = vcsynth.random_qkv(B, S, H, D, seed=5 + seq, v_kind="t3")
-    k = rising_keys(k, 3)
+    k = vcsynth.keys_rising_by_tile(k, 3)
     sm = float(np.float32(1 / math.sqrt(D)))
     kw, mu = {}, None
     if vsmooth:

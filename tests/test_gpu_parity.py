@@ -478,11 +478,10 @@ BF16_TOL = 1e-2  # bf16 probabilities and output rounding, 2^-9 relative each
 def test_attn_bf16_baseline_vs_exact(vc, B, S, H, D, sm, seq, rise):
     """rise: keys of tile t scaled by 1 + rise t, so the running max rises
     past the kernel's headroom of 8 after the first step."""
-    from test_oracle_mxfp4 import rising_keys
     print(f"case bf16 baseline B={B} S={S} H={H} D={D} seq={seq} rise={rise}", flush=True)
     q, k, v = vcsynth.random_qkv(B, S, H, D, seed=3 * S + D, v_kind="t3")
     if rise:
-        k = rising_keys(k, rise)
+        k = vcsynth.keys_rising_by_tile(k, rise)
     vt = vc.vc_pack_v_bf16(v.cuda())
     o = vc.vc_attn_fwd_bf16(q.cuda(), k.cuda(), vt, sm_scale=sm, sequential=seq)
     torch.cuda.synchronize()

@@ -199,15 +199,6 @@ def test_attn4_running_max_is_the_integer_ceiling(vs):
         assert res["stats"][j, 1] == int(res["stats"][j, 1])
 
 
-def rising_keys(k, step):
-    """Keys of tile t scaled by 1 + step t (bf16 [B,S,H,D]), so that in key
-    order each tile's scores reach well past the last one's: rises beyond
-    any headroom."""
-    import torch
-    t = torch.arange(k.shape[1]) // 128
-    return (k.float() * (1 + step * t).float()[None, :, None, None]).to(torch.bfloat16)
-
-
 @pytest.mark.parametrize("vs,flags,rising", [(False, 0, False), (True, 0, False), (True, oracle.SEQUENTIAL, False),
                                              (False, oracle.SEQUENTIAL, False), (False, oracle.SEQUENTIAL, True),
                                              (True, 0, True)])
@@ -220,7 +211,7 @@ def test_attn4_deferred_rises_change_no_output(vs, flags, rising):
     S, D = 1000, 64
     q, k, v = vcsynth.random_qkv(1, S, 1, D, seed=12)
     if rising:
-        k = rising_keys(k, 2)
+        k = vcsynth.keys_rising_by_tile(k, 2)
     qb, kb, vb = (vcsynth.bf16_bits(x) for x in (q, k, v))
     rows = np.arange(0, S, 3)
     kw = dict(vsmooth=vs, nclust=8, iters=2, seed=4, rows=rows, sm_scale=0.3)

@@ -207,3 +207,11 @@ def random_qkv(B, S, H, D, seed, device="cpu", v_kind="normal"):
 def bf16_bits(x: torch.Tensor):
     """bf16 tensor -> numpy uint16 bit patterns (on the host)."""
     return x.detach().contiguous().cpu().view(torch.int16).numpy().view("uint16")
+
+
+def keys_rising_by_tile(k: torch.Tensor, step: float) -> torch.Tensor:
+    """bf16 keys [B,S,H,D] with the keys of 128-token tile t scaled by
+    1 + step t, so that in key order each tile's scores reach well past the
+    previous tile's: the running maximum keeps rising."""
+    t = torch.arange(k.shape[1], device=k.device) // 128
+    return (k.float() * (1 + step * t).float()[None, :, None, None]).to(torch.bfloat16)
